@@ -1,0 +1,145 @@
+"""Float64 CPU oracle for the RWKV WKV operator -- test infrastructure only.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or executes anything here, and this
+package never imports the product.
+
+The arithmetic lives in ``wkv_oracle.c`` (plain C, float64); this module only
+compiles it with gcc and marshals numpy arrays.  See the header of that file
+for the passages of the pages each function restates and for the parity pin
+of each function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wkv_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math", "-pthread",
+             "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        D = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.wkvo_forward_brute.argtypes = [i64, i64, i64, D, D, D, D, D, D, D]
+        lib.wkvo_forward_scan.argtypes = [i64, i64, i64, D, D, D, D, D, D, D, ctypes.c_int]
+        lib.wkvo_backward_brute.argtypes = [i64, i64, i64, D, D, D, D, D, D, D, D, D]
+        lib.wkvo_backward_scan.argtypes = [i64, i64, i64, D, D, D, D, D, D, D, D, D,
+                                           ctypes.c_int]
+        for f in (lib.wkvo_forward_brute, lib.wkvo_forward_scan, lib.wkvo_backward_brute,
+                  lib.wkvo_backward_scan):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _shapes(k, w):
+    k = np.asarray(k)
+    if k.ndim != 3:
+        raise ValueError("k must be [B][T][C]")
+    B, T, C = k.shape
+    if np.asarray(w).shape != (C,):
+        raise ValueError("w and u must be [C]")
+    return B, T, C
+
+
+def forward_brute(w, u, k, v, state_in=None):
+    """O(T^2) closed form.  Returns (y [B,T,C], state_out [3,B,C]) in float64."""
+    B, T, C = _shapes(k, w)
+    w, u, k, v = _f64(w), _f64(u), _f64(k), _f64(v)
+    s_in = None if state_in is None else _f64(state_in)
+    if s_in is not None and s_in.shape != (3, B, C):
+        raise ValueError("state_in must be [3][B][C]")
+    y = np.empty((B, T, C))
+    s_out = np.empty((3, B, C))
+    rc = _load().wkvo_forward_brute(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(s_in),
+                                    _ptr(y), _ptr(s_out))
+    if rc:
+        raise RuntimeError(f"wkvo_forward_brute failed ({rc})")
+    return y, s_out
+
+
+def forward_scan(w, u, k, v, state_in=None, nthreads: int = 1):
+    """O(T) log-space recurrence.  Returns (y [B,T,C], state_out [3,B,C])."""
+    B, T, C = _shapes(k, w)
+    w, u, k, v = _f64(w), _f64(u), _f64(k), _f64(v)
+    s_in = None if state_in is None else _f64(state_in)
+    if s_in is not None and s_in.shape != (3, B, C):
+        raise ValueError("state_in must be [3][B][C]")
+    y = np.empty((B, T, C))
+    s_out = np.empty((3, B, C))
+    rc = _load().wkvo_forward_scan(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(s_in),
+                                   _ptr(y), _ptr(s_out), int(nthreads))
+    if rc:
+        raise RuntimeError(f"wkvo_forward_scan failed ({rc})")
+    return y, s_out
+
+
+def backward_brute(w, u, k, v, dy):
+    """O(T^2) analytic backward (empty initial state).  Returns (dk, dv, dw, du)."""
+    B, T, C = _shapes(k, w)
+    w, u, k, v, dy = _f64(w), _f64(u), _f64(k), _f64(v), _f64(dy)
+    dk, dv = np.empty((B, T, C)), np.empty((B, T, C))
+    dw, du = np.empty(C), np.empty(C)
+    rc = _load().wkvo_backward_brute(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                                     _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du))
+    if rc:
+        raise RuntimeError(f"wkvo_backward_brute failed ({rc})")
+    return dk, dv, dw, du
+
+
+def backward_scan(w, u, k, v, dy, nthreads: int = 1):
+    """O(T) reverse-scan backward (empty initial state).  Returns (dk, dv, dw, du)."""
+    B, T, C = _shapes(k, w)
+    w, u, k, v, dy = _f64(w), _f64(u), _f64(k), _f64(v), _f64(dy)
+    dk, dv = np.empty((B, T, C)), np.empty((B, T, C))
+    dw, du = np.empty(C), np.empty(C)
+    rc = _load().wkvo_backward_scan(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                                    _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), int(nthreads))
+    if rc:
+        raise RuntimeError(f"wkvo_backward_scan failed ({rc})")
+    return dk, dv, dw, du
+
+
+def canonical_state(state):
+    """(a, b, o) -> (m, lam): m = a/b, the weighted mean of past values, and
+    lam = o + ln b, the log of the total decayed weight.  Two (a, b, o) triples
+    that describe the same sums give the same (m, lam).  Empty lanes (b == 0)
+    give m = 0, lam = -inf."""
+    s = np.asarray(state, dtype=np.float64)
+    a, b, o = s[0], s[1], s[2]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        m = np.where(b > 0, a / np.where(b > 0, b, 1.0), 0.0)
+        lam = np.where(b > 0, o + np.log(np.where(b > 0, b, 1.0)), -np.inf)
+    return m, lam

@@ -1,0 +1,415 @@
+/*
+ * wkv_oracle.c -- plain float64 CPU oracle for the RWKV WKV time-mixing operator.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load
+ * this file: only the test suite, the package smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with the
+ * HIP library; the two meet only on the seeded input tensors.
+ *
+ * Sources (the pages this restates; no listing is translated line by line):
+ *   [Core]      RWKV architecture deep dive (youngju.dev), section
+ *               "WKV mechanism: mathematical formulation / core computation":
+ *               the closed-form weighted average that defines wkv_t.
+ *   [Recurrent] same article, section "Recurrent formulation": running
+ *               numerator/denominator updated with decay exp(-w).
+ *   [LogSpace]  same article, section "Numerical stability via log-space
+ *               computation": running max exponent kept beside the sums.
+ *   [Parallel]  same article, section "Parallel training formulation":
+ *               zero-initialised running sums, bonus only on the current token.
+ *   [QuickStart] rwkv-architecture skill page, section "Quick start" (GPT mode
+ *               vs RNN mode with the state carried between calls).
+ *
+ * Conventions (all arrays row-major, float64):
+ *   k, v, y, dy, dk, dv : [B][T][C]   (channel fastest)
+ *   w, u                : [C]         w = exp(decay) is the per-channel decay
+ *                                      rate (the pages require w > 0; the
+ *                                      oracle accepts any finite w)
+ *   state               : [3][B][C]   planes a, b, o.  The true running sums
+ *                                      are A = a*exp(o) and Bden = b*exp(o).
+ *                                      The empty state is a = b = 0, o = -inf.
+ *   Token index t runs 0..T-1 here; the pages count from 1.
+ *
+ * Parity status of each function (pins live in the test suite):
+ *   wkvo_forward_brute     pinned (library softmax limits, geometric series,
+ *                          the pages' two recurrences, invariants)
+ *   wkvo_forward_scan      pinned (brute force, chunking identity)
+ *   wkvo_backward_brute    pinned (central finite differences, invariants)
+ *   wkvo_backward_scan     pinned (brute-force backward, finite differences)
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define IDX(b, t, c) (((int64_t)(b) * T + (t)) * C + (c))
+#define SIDX(p, b, c) (((int64_t)(p) * B + (b)) * C + (c))
+
+static double dmax(double x, double y) { return x > y ? x : y; }
+
+/* ------------------------------------------------------------------------ */
+/* Forward, O(T^2): the closed form of [Core], written out per output token.  */
+/* ------------------------------------------------------------------------ */
+/*
+ * [Core] defines, for token t (1-based on the page),
+ *     wkv_t = ( sum_{i<t} e^{-(t-1-i)w + k_i} v_i + e^{u+k_t} v_t )
+ *           / ( sum_{i<t} e^{-(t-1-i)w + k_i}     + e^{u+k_t}     ).
+ * A carried state ([QuickStart]: the state returned by one call is passed to
+ * the next) adds the decayed sums of all earlier tokens, e^{-(t-1)w} A0 and
+ * e^{-(t-1)w} B0, to the numerator and denominator.  With 0-based t the decay
+ * distance of past token i is (t-1-i) and of the state it is t.
+ * Every exponent is shifted by the largest one before exponentiating, which
+ * changes nothing in the ratio.
+ */
+static void forward_brute_lane(int64_t T, double w, double u, const double *k,
+                               const double *v, int64_t stride, double a0,
+                               double b0, double o0, double *y, double *s_out) {
+    double *x = (double *)malloc(sizeof(double) * (size_t)(T + 1));
+    double *val = (double *)malloc(sizeof(double) * (size_t)(T + 1));
+    int has_state = (b0 > 0.0);
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t n = 0;
+        for (int64_t i = 0; i < t; ++i) {
+            x[n] = k[i * stride] - (double)(t - 1 - i) * w;
+            val[n] = v[i * stride];
+            ++n;
+        }
+        x[n] = u + k[t * stride];
+        val[n] = v[t * stride];
+        ++n;
+        double m = x[0];
+        for (int64_t j = 1; j < n; ++j) m = dmax(m, x[j]);
+        double xs = 0.0;
+        if (has_state) {
+            xs = o0 - (double)t * w;
+            m = dmax(m, xs);
+        }
+        double num = 0.0, den = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            double e = exp(x[j] - m);
+            num += e * val[j];
+            den += e;
+        }
+        if (has_state) {
+            double e = exp(xs - m);
+            num += e * a0;
+            den += e * b0;
+        }
+        y[t * stride] = num / den;
+    }
+    if (s_out) {
+        /* State after the last token: A_T = e^{-Tw} A0 + sum_{i<T} e^{k_i-(T-1-i)w} v_i. */
+        double m = -INFINITY;
+        for (int64_t i = 0; i < T; ++i) m = dmax(m, k[i * stride] - (double)(T - 1 - i) * w);
+        double xs = o0 - (double)T * w;
+        if (has_state) m = dmax(m, xs);
+        double a = 0.0, b = 0.0;
+        if (m == -INFINITY) {
+            s_out[0] = 0.0;
+            s_out[1] = 0.0;
+            s_out[2] = -INFINITY;
+        } else {
+            for (int64_t i = 0; i < T; ++i) {
+                double e = exp(k[i * stride] - (double)(T - 1 - i) * w - m);
+                a += e * v[i * stride];
+                b += e;
+            }
+            if (has_state) {
+                double e = exp(xs - m);
+                a += e * a0;
+                b += e * b0;
+            }
+            s_out[0] = a;
+            s_out[1] = b;
+            s_out[2] = m;
+        }
+    }
+    free(x);
+    free(val);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Forward, O(T): the recurrence of [Recurrent] in the log-space form of      */
+/* [LogSpace], with the output read as in [Core] and [Parallel].             */
+/* ------------------------------------------------------------------------ */
+/*
+ * The state (a, b, o) stands for the sums A = a e^o, B = b e^o of all tokens
+ * seen so far, each decayed by e^{-w} per later token.
+ *   output  : wkv_t = (A + e^{u+k_t} v_t) / (B + e^{u+k_t})
+ *             -- the past sums enter undecayed, which is the closed form of
+ *             [Core] and the loop of [Parallel] (the "Recurrent formulation"
+ *             section multiplies the past by one more e^{-w} here; that form
+ *             equals this one with the bonus u replaced by u + w).
+ *   update  : A <- e^{-w} A + e^{k_t} v_t,  B <- e^{-w} B + e^{k_t}
+ *             ([Recurrent]); u does not enter the state.
+ * Both steps factor out the larger exponent first ([LogSpace]).
+ */
+static void forward_scan_lane(int64_t T, double w, double u, const double *k,
+                              const double *v, int64_t stride, double *a_,
+                              double *b_, double *o_, double *y) {
+    double a = *a_, b = *b_, o = *o_;
+    for (int64_t t = 0; t < T; ++t) {
+        double kt = k[t * stride], vt = v[t * stride];
+        double p = dmax(o, u + kt);
+        double ep = exp(o - p), ec = exp(u + kt - p);
+        y[t * stride] = (ep * a + ec * vt) / (ep * b + ec);
+        double q = dmax(o - w, kt);
+        double fp = exp(o - w - q), fc = exp(kt - q);
+        a = fp * a + fc * vt;
+        b = fp * b + fc;
+        o = q;
+    }
+    *a_ = a;
+    *b_ = b;
+    *o_ = o;
+}
+
+int wkvo_forward_brute(int64_t B, int64_t T, int64_t C, const double *w,
+                       const double *u, const double *k, const double *v,
+                       const double *s_in, double *y, double *s_out) {
+    if (B < 0 || T < 0 || C < 0) return 1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c) {
+            double a0 = 0.0, b0 = 0.0, o0 = -INFINITY;
+            if (s_in) {
+                a0 = s_in[SIDX(0, b, c)];
+                b0 = s_in[SIDX(1, b, c)];
+                o0 = s_in[SIDX(2, b, c)];
+            }
+            double so[3];
+            forward_brute_lane(T, w[c], u[c], k + IDX(b, 0, c), v + IDX(b, 0, c), C, a0, b0,
+                               o0, y + IDX(b, 0, c), so);
+            if (s_out) {
+                s_out[SIDX(0, b, c)] = so[0];
+                s_out[SIDX(1, b, c)] = so[1];
+                s_out[SIDX(2, b, c)] = so[2];
+            }
+        }
+    return 0;
+}
+
+/* Lane range [l0, l1) of the B*C lanes; lanes are independent. */
+typedef struct {
+    int64_t B, T, C, l0, l1;
+    const double *w, *u, *k, *v, *s_in;
+    double *y, *s_out;
+} scan_job;
+
+static void *scan_job_run(void *arg) {
+    scan_job *j = (scan_job *)arg;
+    int64_t B = j->B, T = j->T, C = j->C;
+    for (int64_t lane = j->l0; lane < j->l1; ++lane) {
+        int64_t b = lane / C, c = lane % C;
+        double a = 0.0, bb = 0.0, o = -INFINITY;
+        if (j->s_in) {
+            a = j->s_in[SIDX(0, b, c)];
+            bb = j->s_in[SIDX(1, b, c)];
+            o = j->s_in[SIDX(2, b, c)];
+        }
+        forward_scan_lane(T, j->w[c], j->u[c], j->k + IDX(b, 0, c), j->v + IDX(b, 0, c), C, &a,
+                          &bb, &o, j->y + IDX(b, 0, c));
+        if (j->s_out) {
+            j->s_out[SIDX(0, b, c)] = a;
+            j->s_out[SIDX(1, b, c)] = bb;
+            j->s_out[SIDX(2, b, c)] = o;
+        }
+    }
+    return NULL;
+}
+
+/* nthreads <= 1 runs on the calling thread.  Threads split lanes only. */
+int wkvo_forward_scan(int64_t B, int64_t T, int64_t C, const double *w, const double *u,
+                      const double *k, const double *v, const double *s_in, double *y,
+                      double *s_out, int nthreads) {
+    if (B < 0 || T < 0 || C < 0) return 1;
+    int64_t lanes = B * C;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > lanes) nthreads = lanes > 0 ? (int)lanes : 1;
+    scan_job jobs[256];
+    pthread_t th[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = (scan_job){B, T, C, lanes * i / nthreads, lanes * (i + 1) / nthreads,
+                             w, u, k, v, s_in, y, s_out};
+    }
+    if (nthreads == 1) {
+        scan_job_run(&jobs[0]);
+        return 0;
+    }
+    for (int i = 0; i < nthreads; ++i)
+        if (pthread_create(&th[i], NULL, scan_job_run, &jobs[i]) != 0) return 2;
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward.  The pages give no backward; these are the derivatives of the    */
+/* closed form of [Core] (empty initial state), with L = sum_t dy_t * y_t.    */
+/* ------------------------------------------------------------------------ */
+/*
+ * With p_{t,i} = E_{t,i} / D_t (the weight of token i in output t; the weights
+ * of one output sum to 1) and g_t = dy_t:
+ *   dv_i = sum_{t>=i} g_t p_{t,i}
+ *   dk_i = sum_{t>=i} g_t p_{t,i} (v_i - y_t)
+ *   du   = sum_{b,t}   g_t p_{t,t} (v_t - y_t)
+ *   dw   = -sum_{b,t} sum_{i<t} (t-1-i) g_t p_{t,i} (v_i - y_t)
+ * dw and du are [C], summed over the batch and the tokens.
+ */
+int wkvo_backward_brute(int64_t B, int64_t T, int64_t C, const double *w, const double *u,
+                        const double *k, const double *v, const double *dy, double *dk,
+                        double *dv, double *dw, double *du) {
+    if (B < 0 || T < 0 || C < 0) return 1;
+    double *x = (double *)malloc(sizeof(double) * (size_t)(T + 1));
+    for (int64_t c = 0; c < C; ++c) {
+        dw[c] = 0.0;
+        du[c] = 0.0;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c) {
+            const double *kk = k + IDX(b, 0, c), *vv = v + IDX(b, 0, c), *gg = dy + IDX(b, 0, c);
+            double *dkk = dk + IDX(b, 0, c), *dvv = dv + IDX(b, 0, c);
+            for (int64_t i = 0; i < T; ++i) {
+                dkk[i * C] = 0.0;
+                dvv[i * C] = 0.0;
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                /* exponents of output t: x[i] for past tokens, x[t] with the bonus */
+                for (int64_t i = 0; i < t; ++i) x[i] = kk[i * C] - (double)(t - 1 - i) * w[c];
+                x[t] = u[c] + kk[t * C];
+                double m = x[0];
+                for (int64_t i = 1; i <= t; ++i) m = dmax(m, x[i]);
+                double den = 0.0, num = 0.0;
+                for (int64_t i = 0; i <= t; ++i) {
+                    double e = exp(x[i] - m);
+                    den += e;
+                    num += e * vv[i * C];
+                }
+                double yt = num / den, g = gg[t * C];
+                for (int64_t i = 0; i <= t; ++i) {
+                    double p = exp(x[i] - m) / den;
+                    dvv[i * C] += g * p;
+                    dkk[i * C] += g * p * (vv[i * C] - yt);
+                    if (i == t)
+                        du[c] += g * p * (vv[i * C] - yt);
+                    else
+                        dw[c] -= (double)(t - 1 - i) * g * p * (vv[i * C] - yt);
+                }
+            }
+        }
+    free(x);
+    return 0;
+}
+
+/*
+ * O(T) reverse scan of the same derivatives.  For token i define the sums over
+ * later outputs t > i (l_t = ln D_t):
+ *   R_i  = sum_{t>i} g_t e^{-(t-1-i)w - l_t}         S_i  = same with g_t y_t
+ *   R'_i = sum_{t>i} (t-1-i) g_t e^{-(t-1-i)w - l_t}  S'_i = same with g_t y_t
+ * so that, since p_{t,i} = e^{k_i} e^{-(t-1-i)w - l_t} for t > i,
+ *   dv_i = p_{i,i} g_i + e^{k_i} R_i
+ *   dk_i = p_{i,i} g_i (v_i - y_i) + e^{k_i} (v_i R_i - S_i)
+ *   dw  -= e^{k_i} (v_i R'_i - S'_i),   du += p_{i,i} g_i (v_i - y_i)
+ * and stepping from i to i-1:
+ *   R_{i-1} = g_i e^{-l_i} + e^{-w} R_i,   R'_{i-1} = e^{-w} (R'_i + R_i).
+ * The four sums are held as R = Rs * e^{rho} with rho_{i-1} = max(-l_i, rho_i - w),
+ * which keeps e^{k_i + rho_i} = max_t p_{t,i} <= 1 and every stored value bounded.
+ */
+typedef struct {
+    int64_t B, T, C, l0, l1;
+    const double *w, *u, *k, *v, *dy;
+    double *dk, *dv, *dw_lane, *du_lane;
+} bwd_job;
+
+static void backward_scan_lane(int64_t T, double w, double u, const double *k, const double *v,
+                               const double *g, int64_t stride, double *dk, double *dv,
+                               double *dw_out, double *du_out, double *ell, double *yy) {
+    /* forward recompute of y_t and l_t = ln D_t */
+    double a = 0.0, b = 0.0, o = -INFINITY;
+    for (int64_t t = 0; t < T; ++t) {
+        double kt = k[t * stride], vt = v[t * stride];
+        double p = dmax(o, u + kt);
+        double ep = exp(o - p), ec = exp(u + kt - p);
+        double den = ep * b + ec;
+        yy[t] = (ep * a + ec * vt) / den;
+        ell[t] = p + log(den);
+        double q = dmax(o - w, kt);
+        double fp = exp(o - w - q), fc = exp(kt - q);
+        a = fp * a + fc * vt;
+        b = fp * b + fc;
+        o = q;
+    }
+    double Rs = 0.0, Ss = 0.0, R1 = 0.0, S1 = 0.0, rho = -INFINITY;
+    double dw = 0.0, du = 0.0;
+    for (int64_t i = T - 1; i >= 0; --i) {
+        double ki = k[i * stride], vi = v[i * stride], gi = g[i * stride];
+        double pii = exp(u + ki - ell[i]);
+        double ek = exp(ki + rho);
+        double own = pii * gi;
+        dv[i * stride] = own + ek * Rs;
+        dk[i * stride] = own * (vi - yy[i]) + ek * (vi * Rs - Ss);
+        dw -= ek * (vi * R1 - S1);
+        du += own * (vi - yy[i]);
+        /* step the sums from "after i" to "after i-1" */
+        double nrho = dmax(-ell[i], rho - w);
+        double fo = exp(rho - w - nrho), fn = exp(-ell[i] - nrho);
+        double nR1 = fo * (R1 + Rs), nS1 = fo * (S1 + Ss);
+        Rs = fo * Rs + fn * gi;
+        Ss = fo * Ss + fn * gi * yy[i];
+        R1 = nR1;
+        S1 = nS1;
+        rho = nrho;
+    }
+    *dw_out = dw;
+    *du_out = du;
+}
+
+static void *bwd_job_run(void *arg) {
+    bwd_job *j = (bwd_job *)arg;
+    int64_t T = j->T, C = j->C;
+    double *ell = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double *yy = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int64_t lane = j->l0; lane < j->l1; ++lane) {
+        int64_t b = lane / C, c = lane % C;
+        backward_scan_lane(T, j->w[c], j->u[c], j->k + IDX(b, 0, c), j->v + IDX(b, 0, c),
+                           j->dy + IDX(b, 0, c), C, j->dk + IDX(b, 0, c), j->dv + IDX(b, 0, c),
+                           &j->dw_lane[lane], &j->du_lane[lane], ell, yy);
+    }
+    free(ell);
+    free(yy);
+    return NULL;
+}
+
+int wkvo_backward_scan(int64_t B, int64_t T, int64_t C, const double *w, const double *u,
+                       const double *k, const double *v, const double *dy, double *dk,
+                       double *dv, double *dw, double *du, int nthreads) {
+    if (B < 0 || T < 0 || C < 0) return 1;
+    int64_t lanes = B * C;
+    double *dw_lane = (double *)calloc((size_t)(lanes > 0 ? lanes : 1), sizeof(double));
+    double *du_lane = (double *)calloc((size_t)(lanes > 0 ? lanes : 1), sizeof(double));
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > lanes) nthreads = lanes > 0 ? (int)lanes : 1;
+    bwd_job jobs[256];
+    pthread_t th[256];
+    for (int i = 0; i < nthreads; ++i)
+        jobs[i] = (bwd_job){B, T, C, lanes * i / nthreads, lanes * (i + 1) / nthreads,
+                            w, u, k, v, dy, dk, dv, dw_lane, du_lane};
+    if (nthreads == 1) {
+        bwd_job_run(&jobs[0]);
+    } else {
+        for (int i = 0; i < nthreads; ++i)
+            if (pthread_create(&th[i], NULL, bwd_job_run, &jobs[i]) != 0) return 2;
+        for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    }
+    /* sum the per-lane parts over the batch in a fixed order */
+    for (int64_t c = 0; c < C; ++c) {
+        dw[c] = 0.0;
+        du[c] = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            dw[c] += dw_lane[b * C + c];
+            du[c] += du_lane[b * C + c];
+        }
+    }
+    free(dw_lane);
+    free(du_lane);
+    return 0;
+}

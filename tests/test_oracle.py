@@ -1,0 +1,378 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Nothing here touches a GPU.  Each test pins the oracle to something other than
+itself: a library routine in a limiting case, a closed-form series, the pages'
+other two statements of the same operator, invariants, brute force, and
+central finite differences for the backward.
+
+Pages cited:
+  RWKV architecture deep dive (youngju.dev): sections "WKV mechanism: core
+  computation" (closed form), "Recurrent formulation", "Numerical stability via
+  log-space computation", "Parallel training formulation", "Duality".
+  rwkv-architecture skill page: "Quick start" (GPT mode = RNN mode over chunks),
+  "Workflow 2: Long context processing".
+"""
+import os
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+from linear_recurrent_attention_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_case(seed, B=2, T=23, C=5, recipe=synth.RECIPES[synth.TINY]):
+    d = synth.make(synth.TINY, index=seed, B=B, T=T, C=C, recipe=recipe)
+    return {n: t.double().numpy() for n, t in d.items()}
+
+
+def rand_state(oracle, seed, B, C, T0=7):
+    """A reachable non-empty state: the oracle's state after T0 random tokens."""
+    d = rand_case(1000 + seed, B=B, T=T0, C=C)
+    _, s = oracle.forward_brute(d["w"], d["u"], d["k"], d["v"])
+    return s
+
+
+# ---------------------------------------------------------------- forward ---
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("with_state", [False, True])
+def test_brute_equals_scan(oracle, seed, with_state):
+    d = rand_case(seed, B=2, T=41, C=6)
+    s_in = rand_state(oracle, seed, 2, 6) if with_state else None
+    yb, sb = oracle.forward_brute(d["w"], d["u"], d["k"], d["v"], s_in)
+    ys, ss = oracle.forward_scan(d["w"], d["u"], d["k"], d["v"], s_in)
+    np.testing.assert_allclose(ys, yb, rtol=1e-12, atol=1e-13)
+    mb, lb = oracle.canonical_state(sb)
+    ms, ls = oracle.canonical_state(ss)
+    np.testing.assert_allclose(ms, mb, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ls, lb, rtol=1e-12, atol=1e-12)
+
+
+def test_single_token_from_empty_state_is_v(oracle):
+    # Core computation: with no past terms the weight of the only token cancels.
+    d = rand_case(7, B=3, T=1, C=9)
+    for fn in (oracle.forward_brute, oracle.forward_scan):
+        y, s = fn(d["w"], d["u"], d["k"], d["v"])
+        np.testing.assert_allclose(y, d["v"], rtol=1e-15, atol=0)
+
+
+def test_constant_v_gives_v(oracle):
+    d = rand_case(8, B=2, T=30, C=4)
+    v = np.broadcast_to(np.linspace(-2, 3, 4), d["v"].shape).copy()
+    for fn in (oracle.forward_brute, oracle.forward_scan):
+        y, _ = fn(d["w"], d["u"], d["k"], v)
+        np.testing.assert_allclose(y, v, rtol=1e-14, atol=1e-14)
+
+
+def test_fast_decay_limit_is_two_token_softmax(oracle):
+    """w -> inf: only the newest past token (distance 0 in the closed form) and the
+    current token survive, so wkv_t is a softmax over (k_{t-1}, u+k_t).  This is
+    what tells the closed-form placement of exp(-w) from the recurrence section's
+    (which would give v_t in this limit)."""
+    d = rand_case(9, B=1, T=12, C=3)
+    w = np.full(3, 60.0)
+    y, _ = oracle.forward_brute(w, d["u"], d["k"], d["v"])
+    k, v, u = d["k"][0], d["v"][0], d["u"]
+    for t in range(1, 12):
+        scores = np.stack([k[t - 1], u + k[t]])
+        ref = (softmax(scores, axis=0) * np.stack([v[t - 1], v[t]])).sum(0)
+        np.testing.assert_allclose(y[0, t], ref, rtol=1e-12, atol=1e-14)
+    ys, _ = oracle.forward_scan(w, d["u"], d["k"], d["v"])
+    np.testing.assert_allclose(ys, y, rtol=1e-12, atol=1e-14)
+
+
+def test_no_decay_limit_is_causal_softmax_attention(oracle):
+    """w -> 0+: wkv_t is softmax attention over tokens 1..t with scores k_i, the
+    current token's score raised by the bonus u."""
+    d = rand_case(10, B=1, T=20, C=4)
+    w = np.full(4, 1e-14)
+    y, _ = oracle.forward_brute(w, d["u"], d["k"], d["v"])
+    ys, _ = oracle.forward_scan(w, d["u"], d["k"], d["v"])
+    k, v, u = d["k"][0], d["v"][0], d["u"]
+    for t in range(20):
+        scores = k[: t + 1].copy()
+        scores[t] += u
+        ref = (softmax(scores, axis=0) * v[: t + 1]).sum(0)
+        np.testing.assert_allclose(y[0, t], ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(ys[0, t], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_constant_k_geometric_series(oracle):
+    """Constant k: the past weights form a geometric series in e^{-w}.  With v the
+    indicator of token j, y_t is the share of token j in output t."""
+    T, C, kappa, j = 25, 3, 0.7, 6
+    w = np.array([0.05, 0.4, 2.0])
+    u = np.array([0.3, -1.1, 0.8])
+    k = np.full((1, T, C), kappa)
+    v = np.zeros((1, T, C))
+    v[0, j] = 1.0
+    r = np.exp(-w)
+    for fn in (oracle.forward_brute, oracle.forward_scan):
+        y, s = fn(w, u, k, v)
+        for t in range(T):
+            geom = (1 - r ** t) / (1 - r)            # sum_{m<t} r^m: t past tokens
+            den = geom + np.exp(u)
+            if t < j:
+                ref = np.zeros(C)
+            elif t == j:
+                ref = np.exp(u) / den
+            else:
+                ref = r ** (t - 1 - j) / den
+            np.testing.assert_allclose(y[0, t], ref, rtol=1e-12, atol=1e-15)
+        # state after T tokens: total weight e^kappa (1 - r^T)/(1 - r)
+        m, lam = oracle.canonical_state(s)
+        np.testing.assert_allclose(lam[0], kappa + np.log((1 - r ** T) / (1 - r)), rtol=1e-12)
+        np.testing.assert_allclose(m[0], r ** (T - 1 - j) / ((1 - r ** T) / (1 - r)), rtol=1e-12)
+
+
+def test_recurrent_section_form_is_closed_form_with_shifted_bonus(oracle):
+    """The recurrence section multiplies the whole past by e^{-w} in the output
+    while the closed form does not; the two agree once the bonus is shifted by w
+    (the common factor cancels in the ratio).  Here the recurrence section's
+    formulas are run directly (plain float64, no stabilisation, small inputs)."""
+    d = rand_case(11, B=1, T=16, C=5)
+    w, u, k, v = d["w"], d["u"], d["k"][0], d["v"][0]
+
+    def recurrent_section(bonus):
+        alpha = np.zeros(5)
+        beta = np.zeros(5)
+        out = []
+        for t in range(16):
+            ek = np.exp(k[t])
+            euk = np.exp(bonus + k[t])
+            out.append((np.exp(-w) * alpha + euk * v[t]) / (np.exp(-w) * beta + euk))
+            alpha = np.exp(-w) * alpha + ek * v[t]
+            beta = np.exp(-w) * beta + ek
+        return np.array(out)
+
+    y, _ = oracle.forward_brute(w, u, d["k"], d["v"])
+    np.testing.assert_allclose(recurrent_section(u - w), y[0], rtol=1e-12, atol=1e-14)
+    assert np.max(np.abs(recurrent_section(u) - y[0])) > 1e-3
+
+
+def test_parallel_section_loop_equals_closed_form(oracle):
+    """The parallel-training section's loop: zero running sums, the bonus on the
+    current token only, sums decayed after each output."""
+    d = rand_case(12, B=1, T=19, C=4)
+    w, u, k, v = d["w"], d["u"], d["k"][0], d["v"][0]
+    alpha = np.zeros(4)
+    beta = np.zeros(4)
+    ref = []
+    for t in range(19):
+        euk = np.exp(u + k[t])
+        ref.append((alpha + euk * v[t]) / (beta + euk))
+        alpha = np.exp(-w) * alpha + np.exp(k[t]) * v[t]
+        beta = np.exp(-w) * beta + np.exp(k[t])
+    y, _ = oracle.forward_brute(w, u, d["k"], d["v"])
+    np.testing.assert_allclose(y[0], np.array(ref), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_outputs_are_convex_combinations(oracle, seed):
+    d = rand_case(20 + seed, B=2, T=50, C=7, recipe=synth.RECIPES[synth.STABILITY])
+    s_in = rand_state(oracle, seed, 2, 7)
+    m0, _ = oracle.canonical_state(s_in)
+    y, _ = oracle.forward_scan(d["w"], d["u"], d["k"], d["v"], s_in)
+    v = d["v"]
+    lo = np.minimum(np.minimum.accumulate(v, axis=1), m0[:, None, :])
+    hi = np.maximum(np.maximum.accumulate(v, axis=1), m0[:, None, :])
+    tol = 1e-12 * (1 + np.abs(v).max())
+    assert np.all(y >= lo - tol) and np.all(y <= hi + tol)
+
+
+def test_state_invariant(oracle):
+    """Max-normalised state: the largest decayed weight is exactly 1, so
+    1 <= b <= number of tokens absorbed, and |a| <= b * max|v|."""
+    d = rand_case(30, B=3, T=64, C=8, recipe=synth.RECIPES[synth.STABILITY])
+    for T in (1, 5, 64):
+        _, s = oracle.forward_scan(d["w"], d["u"], d["k"][:, :T], d["v"][:, :T])
+        a, b = s[0], s[1]
+        assert np.all(b >= 1 - 1e-12) and np.all(b <= T + 1e-9)
+        vmax = np.abs(d["v"][:, :T]).max(axis=1)
+        assert np.all(np.abs(a) <= b * vmax + 1e-12)
+
+
+def test_empty_state_forms_agree(oracle):
+    d = rand_case(31, B=2, T=9, C=3)
+    empty = np.zeros((3, 2, 3))
+    empty[2] = -np.inf
+    for fn in (oracle.forward_brute, oracle.forward_scan):
+        y0, s0 = fn(d["w"], d["u"], d["k"], d["v"])
+        y1, s1 = fn(d["w"], d["u"], d["k"], d["v"], empty)
+        np.testing.assert_array_equal(y0, y1)
+        np.testing.assert_array_equal(s0, s1)
+
+
+def test_state_is_defined_up_to_common_scale(oracle):
+    """(a, b, o) and (a e^d, b e^d, o - d) are the same state."""
+    d = rand_case(32, B=2, T=13, C=4)
+    s = rand_state(oracle, 5, 2, 4)
+    s2 = s.copy()
+    s2[0] *= np.exp(3.5)
+    s2[1] *= np.exp(3.5)
+    s2[2] -= 3.5
+    for fn in (oracle.forward_brute, oracle.forward_scan):
+        y1, o1 = fn(d["w"], d["u"], d["k"], d["v"], s)
+        y2, o2 = fn(d["w"], d["u"], d["k"], d["v"], s2)
+        np.testing.assert_allclose(y2, y1, rtol=1e-13, atol=1e-14)
+        for x1, x2 in zip(oracle.canonical_state(o1), oracle.canonical_state(o2)):
+            np.testing.assert_allclose(x2, x1, rtol=1e-13, atol=1e-13)
+
+
+def _chunked(oracle, fn, d, cuts, s_in=None):
+    ys, s = [], s_in
+    t0 = 0
+    for n in cuts:
+        sl = slice(t0, t0 + n)
+        y, s = fn(d["w"], d["u"], d["k"][:, sl], d["v"][:, sl], s)
+        ys.append(y)
+        t0 += n
+    return np.concatenate(ys, axis=1), s
+
+
+def _golden_cuts():
+    total, cuts = None, None
+    with open(os.path.join(GOLDEN, "quickstart_chunking.txt")) as f:
+        for line in f:
+            if line.startswith("total"):
+                total = int(line.split()[1])
+            elif line.startswith("chunks"):
+                cuts = [int(x) for x in line.split()[1:]]
+    assert sum(cuts) == total
+    return total, cuts
+
+
+@pytest.mark.parametrize("pattern", ["quickstart", "all_ones", "random"])
+def test_gpt_mode_equals_rnn_mode_over_chunks(oracle, pattern):
+    """Same weights, same results: one call over the sequence equals calls over
+    any chunking of it with the state carried (Quick start; Duality)."""
+    if pattern == "quickstart":
+        T, cuts = _golden_cuts()
+    elif pattern == "all_ones":
+        T, cuts = 17, [1] * 17
+    else:
+        T = 97
+        rng = np.random.default_rng(5)
+        pts = np.sort(rng.choice(np.arange(1, T), size=9, replace=False))
+        cuts = list(np.diff(np.concatenate([[0], pts, [T]])))
+    d = rand_case(40, B=2, T=T, C=6)
+    s_in = rand_state(oracle, 9, 2, 6)
+    yb, sb = oracle.forward_brute(d["w"], d["u"], d["k"], d["v"], s_in)
+    for fn in (oracle.forward_brute, oracle.forward_scan):
+        yc, sc = _chunked(oracle, fn, d, cuts, s_in)
+        np.testing.assert_allclose(yc, yb, rtol=1e-12, atol=1e-13)
+        for x1, x2 in zip(oracle.canonical_state(sb), oracle.canonical_state(sc)):
+            np.testing.assert_allclose(x2, x1, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_length_call_keeps_state(oracle):
+    d = rand_case(41, B=1, T=0, C=3)
+    s = rand_state(oracle, 3, 1, 3)
+    for fn in (oracle.forward_brute, oracle.forward_scan):
+        y, s2 = fn(d["w"], d["u"], d["k"], d["v"], s)
+        assert y.shape == (1, 0, 3)
+        np.testing.assert_allclose(s2, s, rtol=1e-15)
+
+
+def test_wide_exponents_stay_finite(oracle):
+    """Stability recipe (k ~ N(0,8) with +-60 outliers, decay up to e^3): no
+    overflow, and brute force and scan agree."""
+    d = rand_case(42, B=2, T=200, C=8, recipe=synth.RECIPES[synth.STABILITY])
+    assert np.abs(d["k"]).max() == 60.0
+    yb, sb = oracle.forward_brute(d["w"], d["u"], d["k"], d["v"])
+    ys, ss = oracle.forward_scan(d["w"], d["u"], d["k"], d["v"])
+    assert np.all(np.isfinite(yb)) and np.all(np.isfinite(sb))
+    np.testing.assert_allclose(ys, yb, rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------- backward ---
+
+def _loss(oracle, w, u, k, v, dy):
+    y, _ = oracle.forward_brute(w, u, k, v)
+    return float((y * dy).sum())
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_backward_brute_equals_scan(oracle, seed):
+    d = synth.make(synth.STABILITY, index=seed, B=2, T=45, C=6, with_dy=True)
+    d = {n: t.double().numpy() for n, t in d.items()}
+    gb = oracle.backward_brute(d["w"], d["u"], d["k"], d["v"], d["dy"])
+    gs = oracle.backward_scan(d["w"], d["u"], d["k"], d["v"], d["dy"])
+    for a, b in zip(gs, gb):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12 * (1 + np.abs(b).max()))
+
+
+@pytest.mark.parametrize("outlier", [False, True])
+def test_backward_matches_finite_differences(oracle, outlier):
+    """Central differences of L = sum dy*y on a B=1, T=32, C=8 slice of the
+    stability workload; the second copy forces a +60 entry into k."""
+    d = synth.make(synth.STABILITY, index=3, B=1, T=32, C=8, with_dy=True)
+    d = {n: t.double().numpy() for n, t in d.items()}
+    if outlier:
+        d["k"][0, 11, 2] = 60.0
+        d["k"][0, 20, 5] = -60.0
+    w, u, k, v, dy = d["w"], d["u"], d["k"], d["v"], d["dy"]
+    dk, dv, dw, du = oracle.backward_scan(w, u, k, v, dy)
+    dkb, dvb, dwb, dub = oracle.backward_brute(w, u, k, v, dy)
+
+    def fd(arr, idx):
+        x0 = arr[idx]
+        h = 1e-6 * max(1.0, abs(x0))
+        arr[idx] = x0 + h
+        lp = _loss(oracle, w, u, k, v, dy)
+        arr[idx] = x0 - h
+        lm = _loss(oracle, w, u, k, v, dy)
+        arr[idx] = x0
+        return (lp - lm) / (2 * h)
+
+    rng = np.random.default_rng(0)
+    picks = [(0, int(t), int(c)) for t, c in zip(rng.integers(0, 32, 24), rng.integers(0, 8, 24))]
+    if outlier:
+        picks += [(0, 11, 2), (0, 20, 5), (0, 12, 2)]
+    for grad, gbrute, arr in ((dk, dkb, k), (dv, dvb, v)):
+        for idx in picks:
+            ref = fd(arr, idx)
+            scale = max(1e-3, np.abs(grad).max())
+            assert abs(grad[idx] - ref) <= 1e-6 * scale, (idx, grad[idx], ref)
+            assert abs(gbrute[idx] - ref) <= 1e-6 * scale
+    for grad, gbrute, arr in ((dw, dwb, w), (du, dub, u)):
+        for c in range(8):
+            ref = fd(arr, (c,))
+            scale = max(1e-3, np.abs(grad).max())
+            assert abs(grad[c] - ref) <= 1e-6 * scale, (c, grad[c], ref)
+            assert abs(gbrute[c] - ref) <= 1e-6 * scale
+
+
+def test_backward_invariants(oracle):
+    """Shifting every k of a lane leaves y unchanged, so sum_i dk_i = 0 per lane;
+    the weights of each output sum to one, so sum_i dv_i = sum_t dy_t per lane;
+    adding a constant to every v shifts every y by it, so dk, dw, du are unchanged."""
+    d = synth.make(synth.STABILITY, index=5, B=3, T=60, C=5, with_dy=True)
+    d = {n: t.double().numpy() for n, t in d.items()}
+    dk, dv, dw, du = oracle.backward_scan(d["w"], d["u"], d["k"], d["v"], d["dy"])
+    scale = np.abs(dk).max()
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-11 * scale * 60)
+    np.testing.assert_allclose(dv.sum(axis=1), d["dy"].sum(axis=1), rtol=1e-11, atol=1e-11)
+    dk2, dv2, dw2, du2 = oracle.backward_scan(d["w"], d["u"], d["k"], d["v"] + 2.5, d["dy"])
+    np.testing.assert_allclose(dk2, dk, rtol=1e-9, atol=1e-10 * scale)
+    np.testing.assert_allclose(dv2, dv, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dw2, dw, rtol=1e-9, atol=1e-9 * np.abs(dw).max())
+    np.testing.assert_allclose(du2, du, rtol=1e-9, atol=1e-9 * np.abs(du).max())
+
+
+def test_threads_do_not_change_results(oracle):
+    d = synth.make(synth.GPT, index=0, B=2, T=33, C=16, with_dy=True)
+    d = {n: t.double().numpy() for n, t in d.items()}
+    y1, s1 = oracle.forward_scan(d["w"], d["u"], d["k"], d["v"], nthreads=1)
+    y4, s4 = oracle.forward_scan(d["w"], d["u"], d["k"], d["v"], nthreads=4)
+    np.testing.assert_array_equal(y1, y4)
+    np.testing.assert_array_equal(s1, s4)
+    g1 = oracle.backward_scan(d["w"], d["u"], d["k"], d["v"], d["dy"], nthreads=1)
+    g4 = oracle.backward_scan(d["w"], d["u"], d["k"], d["v"], d["dy"], nthreads=4)
+    for a, b in zip(g1, g4):
+        np.testing.assert_array_equal(a, b)
