@@ -1,0 +1,412 @@
+#!/usr/bin/env python3
+"""Benchmark of the WKV forward on one MI355X.
+
+Default workload (the headline metric): GPT-mode WKV forward at B=8, T=1024,
+C=2048, fp32, shaped like one layer of a 24-layer, 2048-wide model at context
+1024; 24 independently seeded layers, all resident in HBM (4.8 GB of inputs
+and outputs, far above the 256 MB last-level cache), called back to back.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the forward over all 24 layers (24 calls of
+wkv_forward).  Prints one JSON line with the lane-token throughput
+(tokens x channels / s), the roofline of the forward kernel (algorithmic HBM
+bytes per launch over its average launch time, measured with HIP events on the
+stream it runs on), and the float64 CPU oracle timed on this host as a baseline.
+
+Other workloads (--workload stream|decode|stability_fwd|stability_bwd) print
+their own line in the same format; they are parity workloads with extra
+measurements, not the headline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "WKV fwd tokens·channels/sec + HBM GB/s (% peak), B=8 T=1024 C=2048 fp32"
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["linear_recurrent_attention_amd/csrc/wkv_forward.hip",
+                  "linear_recurrent_attention_amd/csrc/wkv_lookback.hip",
+                  "linear_recurrent_attention_amd/csrc/wkv_step.hip",
+                  "linear_recurrent_attention_amd/csrc/wkv_backward.hip",
+                  "linear_recurrent_attention_amd/csrc/wkv_device.hpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get(workload)
+    if not e or e.get("source_hash") != source_hash() or e.get("kernel") != kernel:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def host_cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record(self.stream)
+
+    def stop_ms(self):
+        self.b.record(self.stream)
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def cpu_baseline_gpt(torch, synth, inputs_fn, budget_s: float):
+    """The oracle's O(T) recurrence on whole layers of the same workload."""
+    import oracle
+    cores = host_cores()
+    done = 0
+    elapsed = 0.0
+    layer = 0
+    while elapsed < budget_s and layer < 24:
+        d = inputs_fn(layer)
+        a = [d[n].double().cpu().numpy() for n in ("w", "u", "k", "v")]
+        t0 = time.perf_counter()
+        oracle.forward_scan(*a, nthreads=cores)
+        elapsed += time.perf_counter() - t0
+        done += d["k"].numel()
+        layer += 1
+    return {"value": done / elapsed, "unit": "tok·ch/s", "cores": cores, "kind": "oracle",
+            "sample": f"{layer} of the 24 seeded B=8 T=1024 C=2048 layers, whole, "
+                      f"float64 O(T) recurrence on {cores} threads ({elapsed:.1f} s)"}
+
+
+def bench_gpt(args, torch, wkv, synth):
+    sh = synth.SHAPES[synth.GPT]
+    B, T, C, NL = sh["B"], sh["T"], sh["C"], sh["layers"]
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    log(f"gpt: generating {NL} layers of B={B} T={T} C={C} on the device")
+    layers = []
+    for l in range(NL):
+        d = synth.make(synth.GPT, index=l, device=dev)
+        d["y"] = torch.empty_like(d["k"])
+        d["s"] = torch.empty((3, B, C), device=dev)
+        layers.append(d)
+    plan = tuple(args.plan) if args.plan else None
+    chosen = plan or wkv.wkv_forward_plan_auto(B, T, C)
+
+    def call(d):
+        wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=d["y"], state_out=d["s"],
+                        stream=stream, plan=plan)
+
+    for _ in range(args.warmup):
+        for d in layers:
+            call(d)
+    torch.cuda.synchronize()
+    # per-layer timing (median of repeats), reported as the mean over layers
+    per_layer = []
+    tm = Timer(torch, stream)
+    for d in layers:
+        reps = []
+        for _ in range(5):
+            tm.start()
+            call(d)
+            reps.append(tm.stop_ms())
+        reps.sort()
+        per_layer.append(reps[len(reps) // 2])
+    torch.cuda.synchronize()
+    log(f"gpt: timing {args.steps} steps x {NL} layers")
+    t_wall = time.perf_counter()
+    tm.start()
+    for _ in range(args.steps):
+        for d in layers:
+            call(d)
+    ms = tm.stop_ms()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    launches = args.steps * NL
+    ms_launch = ms / launches
+    lane_tok = B * T * C
+    algo_bytes = 12 * lane_tok + 8 * C + 12 * B * C      # k, v in, y out; w, u; state out
+    achieved = algo_bytes / (ms_launch * 1e-3) / 1e9
+    kname = kernel_name(chosen, wkv)
+    traffic = measured_traffic(kname, "gpt")
+    out = {
+        "metric": METRIC,
+        "value": lane_tok * launches / (ms * 1e-3),
+        "unit": "tok·ch/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; k, v ~ N(0,1) with k x2, decay ~ U(-5,1), u ~ N(0,0.5))",
+        "config": {"workload": "gpt_forward", "B": B, "T": T, "C": C, "layers": NL,
+                   "kernel": kname, "plan": list(chosen),
+                   "mean_over_layers_of_median_ms": sum(per_layer) / len(per_layer),
+                   "hbm_gbs": achieved, "pct_peak_hbm": 100 * achieved / PEAK_HBM_GBS,
+                   "wall_ms_timed_region": wall_ms},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": algo_bytes,
+                     "avg_launch_us": ms_launch * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        log("gpt: timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline_gpt(
+            torch, synth, lambda l: {n: layers[l][n] for n in ("w", "u", "k", "v")},
+            args.cpu_seconds)
+    return out
+
+
+def kernel_name(plan, wkv) -> str:
+    kernel, nw, ls = plan
+    if kernel == wkv.WKV_KERNEL_LANE:
+        return "fwd_lane_kernel"
+    if kernel == wkv.WKV_KERNEL_SEGMENTED:
+        return f"fwd_seg_kernel<{nw},{ls}>"
+    if kernel == wkv.WKV_KERNEL_LOOKBACK:
+        return f"fwd_lookback_kernel<{nw},{ls}>"
+    return f"kernel{kernel}<{nw},{ls}>"
+
+
+def bench_stream(args, torch, wkv, synth):
+    """B=1 C=5120, 1024 chunks of 1024 tokens with the state carried; all
+    64.6 GB of inputs resident before timing; per-call mean."""
+    sh = synth.SHAPES[synth.STREAM]
+    C, TC, NCH = sh["C"], sh["T"], sh["chunks"]
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    w, u = synth.channel_params(synth.STREAM, 0, C, device=dev)
+    log(f"stream: generating {NCH} chunks")
+    k = torch.empty((NCH, 1, TC, C), device=dev)
+    v = torch.empty((NCH, 1, TC, C), device=dev)
+    for j in range(NCH):
+        k[j], v[j] = synth.sequence(synth.STREAM, j, (1, TC, C), device=dev)
+    y = torch.empty((NCH, 1, TC, C), device=dev)
+    st = torch.empty((3, 1, C), device=dev)
+    plan = tuple(args.plan) if args.plan else None
+
+    def run_all():
+        wkv.wkv_forward(w, u, k[0], v[0], y=y[0], state_in=None, state_out=st, stream=stream,
+                        plan=plan)
+        for j in range(1, NCH):
+            wkv.wkv_forward(w, u, k[j], v[j], y=y[j], state_in=st, state_out=st, stream=stream,
+                            plan=plan)
+
+    for _ in range(args.warmup):
+        run_all()
+    torch.cuda.synchronize()
+    tm = Timer(torch, stream)
+    tm.start()
+    for _ in range(args.steps):
+        run_all()
+    ms = tm.stop_ms()
+    per_call = ms / (args.steps * NCH)
+    lane_tok = TC * C
+    algo = 12 * lane_tok + 8 * C + 24 * C
+    chosen = plan or wkv.wkv_forward_plan_auto(1, TC, C)
+    return {"metric": "WKV streaming fwd tokens·channels/sec, B=1 C=5120, 1024 chunks x 1024",
+            "value": lane_tok * NCH * args.steps / (ms * 1e-3), "unit": "tok·ch/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms / args.steps, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "stream_forward", "C": C, "chunk": TC, "chunks": NCH,
+                       "kernel": kernel_name(chosen, wkv), "per_call_us": per_call * 1e3},
+            "roofline": {"bound": "hbm", "achieved": algo / (per_call * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": algo / (per_call * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "traffic": measured_traffic(kernel_name(chosen, wkv), "stream"),
+                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per_call * 1e3}}
+
+
+def bench_decode(args, torch, wkv, synth):
+    """L=24 B=1024 C=4096 batched T=1 steps; state from 256 warm-up tokens;
+    inputs from a ring of 32 distinct [24][1024][4096] k, v sets."""
+    sh = synth.SHAPES[synth.DECODE]
+    L, B, C, WU, RING = sh["L"], sh["B"], sh["C"], sh["warmup"], sh["ring"]
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    state = torch.empty((L, 3, B, C), device=dev)
+    w_all = torch.empty((L, C), device=dev)
+    u_all = torch.empty((L, C), device=dev)
+    for l in range(L):
+        w_all[l], u_all[l] = synth.channel_params(synth.DECODE, l, C, device=dev)
+        kk, vv = synth.sequence(synth.DECODE, l, (B, WU, C), device=dev)
+        wkv.wkv_forward(w_all[l], u_all[l], kk, vv, state_out=state[l], stream=stream)
+        del kk, vv
+    log("decode: generating the input ring")
+    ring = [synth.sequence(synth.DECODE, 1000 + r, (L, B, C), device=dev) for r in range(RING)]
+    y = torch.empty((L, B, C), device=dev)
+    nsteps = args.steps * 64
+    for r in range(args.warmup * 8):
+        wkv.wkv_step(w_all, u_all, ring[r % RING][0], ring[r % RING][1], state, y=y, stream=stream)
+    torch.cuda.synchronize()
+    tm = Timer(torch, stream)
+    tm.start()
+    for r in range(nsteps):
+        wkv.wkv_step(w_all, u_all, ring[r % RING][0], ring[r % RING][1], state, y=y, stream=stream)
+    ms = tm.stop_ms()
+    per = ms / nsteps
+    lanes = L * B * C
+    algo = 36 * lanes + 8 * L * C
+    return {"metric": "WKV decode steps/sec, L=24 B=1024 C=4096 fp32", "value": 1e3 / per,
+            "unit": "steps/s", "n_gpus": 1, "steps": nsteps, "warmup": args.warmup * 8,
+            "ms_per_step": per, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "decode_step", "L": L, "B": B, "C": C,
+                       "kernel": "step_kernel<4>",
+                       "state_gbs": 24 * lanes / (per * 1e-3) / 1e9},
+            "roofline": {"bound": "hbm", "achieved": algo / (per * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": algo / (per * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("step_kernel<4>", "decode"),
+                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3}}
+
+
+def bench_stability(args, torch, wkv, synth, backward: bool):
+    sh = synth.SHAPES[synth.STABILITY]
+    B, T, C = sh["B"], sh["T"], sh["C"]
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    sets = [synth.make(synth.STABILITY, index=i, device=dev, with_dy=backward) for i in range(4)]
+    lane_tok = B * T * C
+    if backward:
+        ws = torch.empty(wkv.wkv_backward_workspace_size(B, T, C), device=dev, dtype=torch.uint8)
+        outs = [tuple(torch.empty_like(s["k"]) for _ in range(2)) for s in sets]
+        dwu = torch.empty((2, C), device=dev)
+
+        def call(i):
+            s = sets[i]
+            wkv.wkv_backward(s["w"], s["u"], s["k"], s["v"], s["dy"], dk=outs[i][0],
+                             dv=outs[i][1], dw=dwu[0], du=dwu[1], workspace=ws, stream=stream)
+        algo = 20 * lane_tok + 16 * C
+        name, kname = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32", \
+            "bwd_seg_kernel<16,8>"
+    else:
+        ys = [torch.empty_like(s["k"]) for s in sets]
+
+        def call(i):
+            s = sets[i]
+            wkv.wkv_forward(s["w"], s["u"], s["k"], s["v"], y=ys[i], stream=stream)
+        algo = 12 * lane_tok + 8 * C
+        name = "WKV fwd tokens·channels/sec, B=8 T=4096 C=2048 fp32 (wide exponents)"
+        kname = kernel_name(wkv.wkv_forward_plan_auto(B, T, C), wkv)
+    for i in range(args.warmup):
+        call(i % 4)
+    torch.cuda.synchronize()
+    n = args.steps * 4
+    tm = Timer(torch, stream)
+    tm.start()
+    for i in range(n):
+        call(i % 4)
+    ms = tm.stop_ms()
+    per = ms / n
+    wl = "stability_bwd" if backward else "stability_fwd"
+    return {"metric": name, "value": lane_tok / (per * 1e-3), "unit": "tok·ch/s",
+            "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": per,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": {"workload": wl, "B": B, "T": T, "C": C,
+                                            "kernel": kname},
+            "roofline": {"bound": "hbm", "achieved": algo / (per * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": algo / (per * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "traffic": measured_traffic(kname, wl),
+                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3}}
+
+
+def bench_copy(args, torch, wkv, synth):
+    """A plain device-to-device copy of 1 GiB (torch's copy kernel): the
+    reference for scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE) read
+    by rocprofv3, since its algorithmic traffic is known exactly."""
+    n = (1 << 30) // 4
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    x = torch.empty(n, device=dev).uniform_()
+    y = torch.empty_like(x)
+    for _ in range(args.warmup):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    tm = Timer(torch, stream)
+    tm.start()
+    for _ in range(args.steps):
+        y.copy_(x)
+    ms = tm.stop_ms() / args.steps
+    algo = 2 * 4 * n
+    return {"metric": "device copy GB/s (1 GiB read + 1 GiB written)",
+            "value": algo / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": {"workload": "copy", "bytes_read": 4 * n,
+                                            "bytes_written": 4 * n}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt",
+                    choices=["gpt", "stream", "decode", "stability_fwd", "stability_bwd", "copy"])
+    ap.add_argument("--plan", type=int, nargs=3, default=None,
+                    metavar=("KERNEL", "SEGMENTS", "SEG_LEN"),
+                    help="force a forward kernel (wkv_forward_ex plan)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the WKV lanes are independent, so the operator "
+              "shards across GPUs without communication and this build runs on one GPU only "
+              "(--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    from linear_recurrent_attention_amd import synth, wkv
+    wkv.load_library()
+    fn = {"gpt": bench_gpt, "stream": bench_stream, "decode": bench_decode, "copy": bench_copy,
+          "stability_fwd": lambda a, t, w, s: bench_stability(a, t, w, s, False),
+          "stability_bwd": lambda a, t, w, s: bench_stability(a, t, w, s, True)}[args.workload]
+    torch.cuda.synchronize()
+    out = fn(args, torch, wkv, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * wkv.h -- C ABI of libwkv, the RWKV WKV time-mixing operator on AMD MI355X (gfx950).
+ *
+ * The operator (RWKV architecture deep dive, youngju.dev, section "WKV
+ * mechanism: core computation"): for each lane (b, c) and token t,
+ *
+ *   wkv_t = ( sum_{i<t} e^{-(t-1-i) w + k_i} v_i + e^{u + k_t} v_t )
+ *         / ( sum_{i<t} e^{-(t-1-i) w + k_i}     + e^{u + k_t}     )
+ *
+ * with a per-channel decay rate w = exp(decay) > 0 and a bonus u that only the
+ * current token receives.  The same operator runs in GPT mode over a whole
+ * sequence and in RNN mode over chunks or single tokens with a state carried
+ * between calls (section "Duality"; rwkv-architecture skill page, "Quick
+ * start" and "Workflow 2: Long context processing"); any chunking gives the
+ * same outputs as one call over the whole sequence.
+ *
+ * The state (section "Numerical stability via log-space computation") is three
+ * planes per lane: a (scaled numerator), b (scaled denominator) and o (the
+ * running maximum exponent, natural-log units).  It stands for the running
+ * sums A = a e^o and B = b e^o of every token seen so far, each decayed by
+ * e^{-w} per later token; u is not part of it.  The empty state is a = b = 0
+ * with o = -1e38 (or -inf, or any o <= -1e30).  A state is defined only up to
+ * a common scale: (a e^d, b e^d, o - d) is the same state.
+ *
+ * Memory and ownership
+ *   - Every tensor argument is a device pointer to float32 (IEEE binary32),
+ *     allocated and owned by the caller; the library never frees them and
+ *     never keeps them after the call returns.
+ *   - Layouts are dense row-major with the channel index fastest:
+ *       k, v, y, dy, dk, dv : [B][T][C]
+ *       w, u, dw, du        : [C]             (wkv_step: w, u are [L][C])
+ *       state               : [3][B][C]       planes a, b, o
+ *                                             (wkv_step: [L][3][B][C])
+ *   - The library owns nothing of the caller's; it may keep one small internal
+ *     scratch buffer per (device, stream) for cross-workgroup scan state,
+ *     allocated on the first call that needs it and kept until the process
+ *     ends.  The backward takes its scratch from the caller (workspace).
+ *
+ * Execution
+ *   - Every call is asynchronous on `stream` (0 = the default stream) and
+ *     runs on the device that is current on the calling thread.  Calls on one
+ *     stream run in order.
+ *   - Indexing is 64-bit: a single call may exceed 2^31 elements.
+ *
+ * Errors
+ *   - Arguments are checked on the host, synchronously, before anything is
+ *     launched: a negative dimension (WKV_ERR_DIM), a byte size that overflows
+ *     int64 (WKV_ERR_OVERFLOW), a required pointer that is NULL while the
+ *     tensor is non-empty (WKV_ERR_NULL), an output that overlaps an input or
+ *     another output (WKV_ERR_ALIAS; state_out may equal state_in exactly
+ *     but may not overlap it partially), a workspace that is too small
+ *     (WKV_ERR_WORKSPACE), or a plan that names no compiled kernel
+ *     (WKV_ERR_UNSUPPORTED).  Nothing is launched when a check fails.
+ *   - A failed launch or HIP runtime call returns WKV_ERR_HIP; a fault inside a
+ *     kernel surfaces at the caller's next synchronisation of the stream.
+ *   - Values are not checked on the device.  Preconditions: w > 0 and finite
+ *     inputs; NaN and Inf propagate.
+ *   - No C++ exception crosses this interface.
+ *   - The library keeps no mutable global state other than its per-device
+ *     caches, which are guarded by a mutex; calls may come from several
+ *     threads.
+ */
+#ifndef LIBWKV_WKV_H
+#define LIBWKV_WKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV_API __attribute__((visibility("default")))
+
+typedef enum wkv_status {
+    WKV_OK = 0,
+    WKV_ERR_NULL = 1,
+    WKV_ERR_DIM = 2,
+    WKV_ERR_OVERFLOW = 3,
+    WKV_ERR_ALIAS = 4,
+    WKV_ERR_WORKSPACE = 5,
+    WKV_ERR_UNSUPPORTED = 6,
+    WKV_ERR_HIP = 7
+} wkv_status;
+
+/*
+ * GPT / RNN-chunk forward over T tokens of B sequences with C channels.
+ * Cites: section "WKV mechanism: core computation" (the output), "Recurrent
+ * formulation" and "Numerical stability via log-space computation" (the state
+ * it carries), "Parallel training formulation" (zero initial state when no
+ * state is passed); skill page "Quick start" (RNN mode carries the state).
+ *
+ *   w, u       [C]        decay rate (w > 0) and bonus; required when B*C > 0
+ *   k, v       [B][T][C]  keys and values; required when B*T*C > 0
+ *   y          [B][T][C]  output, fully overwritten; required when B*T*C > 0
+ *   state_in   [3][B][C]  state before the first token, or NULL for the empty
+ *                         state
+ *   state_out  [3][B][C]  state after the last token, or NULL to discard it;
+ *                         may equal state_in (updated in place)
+ * T == 0 copies state_in (or the empty state) to state_out and writes no y.
+ * y must not overlap any input or state buffer.
+ */
+WKV_API wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                               const float *k, const float *v, float *y, const float *state_in,
+                               float *state_out, hipStream_t stream);
+
+/*
+ * Batched single-token RNN step for L layers at once: exactly wkv_forward with
+ * T = 1 applied to each layer l with its own w[l], u[l] and state[l].
+ * Cites: section "Numerical stability via log-space computation" (one token
+ * read against, then folded into, the carried state); skill page "Workflow 1:
+ * Text generation" (token-by-token use of the state).
+ *
+ *   w, u       [L][C]
+ *   k, v, y    [L][B][C]
+ *   state_in   [L][3][B][C]   required when L*B*C > 0 (a step always reads the
+ *                             state; pass a buffer holding the empty state to
+ *                             start a sequence)
+ *   state_out  [L][3][B][C]   required when L*B*C > 0; may equal state_in
+ */
+WKV_API wkv_status wkv_step(int64_t L, int64_t B, int64_t C, const float *w, const float *u,
+                            const float *k, const float *v, float *y, const float *state_in,
+                            float *state_out, hipStream_t stream);
+
+/* Bytes of device workspace wkv_backward needs for this shape (0 when empty).
+ * Returns 0 as well for invalid (negative or overflowing) shapes. */
+WKV_API size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C);
+
+/*
+ * Gradients of L = sum dy * y through the GPT-mode forward with the empty
+ * initial state.  The pages state no backward; these are the derivatives of
+ * the closed form (section "WKV mechanism: core computation"), with p_{t,i}
+ * the weight of token i in output t:
+ *   dv_i = sum_{t>=i} dy_t p_{t,i},  dk_i = sum_{t>=i} dy_t p_{t,i} (v_i - y_t)
+ *   du   = sum_{b,t} dy_t p_{t,t} (v_t - y_t)
+ *   dw   = -sum_{b,t} sum_{i<t} (t-1-i) dy_t p_{t,i} (v_i - y_t)
+ * dw is d/dw of the ABI input w (d/d decay = w * dw).
+ *
+ *   w, u, k, v   as for wkv_forward
+ *   dy           [B][T][C] upstream gradient
+ *   dk, dv       [B][T][C] outputs, fully overwritten
+ *   dw, du       [C] outputs, overwritten with the sums over B and T; the
+ *                summation order is fixed, so results are bitwise
+ *                reproducible run to run
+ *   workspace    device scratch of at least wkv_backward_workspace_size(B,T,C)
+ *                bytes, 256-byte aligned, owned by the caller, not read before
+ *                it is written; may be NULL when that size is 0
+ * Outputs must not overlap inputs, each other, or the workspace.
+ */
+WKV_API wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                                const float *k, const float *v, const float *dy, float *dk,
+                                float *dv, float *dw, float *du, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+WKV_API const char *wkv_status_string(wkv_status s);
+
+/*
+ * Forward with an explicit kernel choice, for testing every kernel on every
+ * shape and for tuning.  Same arguments, semantics and errors as wkv_forward;
+ * `plan` NULL or plan->kernel == WKV_KERNEL_AUTO behaves exactly like
+ * wkv_forward.  A plan whose (kernel, segments, seg_len) is not among the
+ * compiled variants returns WKV_ERR_UNSUPPORTED.
+ *   WKV_KERNEL_LANE        one thread per lane, sequential over T
+ *   WKV_KERNEL_SEGMENTED   one workgroup per (sequence, 64 channels) owns the
+ *                          whole sequence; `segments` waves each sweep seg_len
+ *                          tokens of every tile of segments*seg_len tokens,
+ *                          composing segment states with decay e^{-w len}
+ *   WKV_KERNEL_LOOKBACK    workgroups own (64 channels, block of
+ *                          segments*seg_len tokens) and chain block states by a
+ *                          decoupled look-back over earlier blocks
+ */
+typedef enum wkv_kernel {
+    WKV_KERNEL_AUTO = 0,
+    WKV_KERNEL_LANE = 1,
+    WKV_KERNEL_SEGMENTED = 2,
+    WKV_KERNEL_LOOKBACK = 3
+} wkv_kernel;
+
+typedef struct wkv_forward_plan {
+    int32_t kernel;    /* wkv_kernel */
+    int32_t segments;  /* waves per workgroup (SEGMENTED, LOOKBACK); 0 = default */
+    int32_t seg_len;   /* tokens per wave per tile (SEGMENTED, LOOKBACK); 0 = default */
+    int32_t reserved;  /* must be 0 */
+} wkv_forward_plan;
+
+WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                                  const float *k, const float *v, float *y,
+                                  const float *state_in, float *state_out,
+                                  const wkv_forward_plan *plan, hipStream_t stream);
+
+/* The plan wkv_forward would use for this shape on the current device. */
+WKV_API wkv_status wkv_forward_plan_auto(int64_t B, int64_t T, int64_t C, wkv_forward_plan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBWKV_WKV_H */

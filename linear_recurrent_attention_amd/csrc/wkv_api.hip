@@ -1,0 +1,281 @@
+// wkv_api.hip -- C ABI of libwkv: argument checks, kernel choice, launches.
+//
+// Every check runs on the host before anything touches the HIP runtime, so an
+// invalid call returns its status without a launch (and without needing a
+// device).  The kernels live in wkv_forward.hip, wkv_step.hip and
+// wkv_backward.hip.
+#include <map>
+#include <mutex>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "../../include/wkv.h"
+#include "wkv_internal.hpp"
+
+namespace {
+
+using wkv::BwdArgs;
+using wkv::FwdArgs;
+using wkv::StepArgs;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+
+// n elements of 4 bytes (or `elem` bytes), as a byte count, or -1 on overflow.
+int64_t bytes_of(int64_t a, int64_t b, int64_t c, int64_t elem = 4) {
+    int64_t x, y, z;
+    if (!mul_ok(a, b, &x) || !mul_ok(x, c, &y) || !mul_ok(y, elem, &z)) return -1;
+    return z;
+}
+
+struct Range {
+    uintptr_t lo;
+    uintptr_t hi;  // exclusive
+};
+
+Range rng(const void *p, int64_t bytes) {
+    if (!p || bytes <= 0) return Range{0, 0};
+    return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Cached per-device facts (compute-unit count), guarded by a mutex.
+struct DeviceInfo {
+    int cus = 0;
+};
+std::mutex g_mu;
+std::vector<DeviceInfo> g_dev;
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+    if (g_dev[dev].cus == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        g_dev[dev].cus = n;
+    }
+    return g_dev[dev].cus;
+}
+
+// Scratch of the look-back forward, one buffer per (device, stream) so that
+// calls on different streams never share it.  Allocated and zeroed on first
+// use, grown (after draining the stream) when a larger shape needs more, and
+// kept until the process ends.
+struct Scratch {
+    void *p = nullptr;
+    size_t bytes = 0;
+};
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+hipError_t stream_scratch(hipStream_t st, size_t need, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_mu);
+    Scratch &s = g_scratch[std::make_pair(dev, st)];
+    if (s.bytes < need) {
+        if (s.p) {
+            // a launch still queued on this stream may use the old buffer
+            if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+            if ((e = hipFree(s.p)) != hipSuccess) return e;
+            s.p = nullptr;
+            s.bytes = 0;
+        }
+        const size_t bytes = need < ((size_t)4 << 20) ? ((size_t)4 << 20) : need;
+        if ((e = hipMalloc(&s.p, bytes)) != hipSuccess) return e;
+        if ((e = hipMemsetAsync(s.p, 0, bytes, st)) != hipSuccess) return e;
+        s.bytes = bytes;
+    }
+    *out = s.p;
+    return hipSuccess;
+}
+
+// Largest look-back scratch a call may ask for; longer sequences use the
+// segmented kernel, which needs none.
+constexpr size_t kLookbackScratchMax = (size_t)256 << 20;
+
+// The plan for a shape.  Pure host arithmetic, given the compute-unit count.
+wkv_forward_plan auto_plan(int64_t B, int64_t T, int64_t C, int cus) {
+    wkv_forward_plan p{WKV_KERNEL_LANE, 0, 0, 0};
+    const int64_t lanes = B * C;
+    // one wave of 64 lanes per SIMD on every CU, four deep, keeps the lane
+    // kernel fed on its own; below that the sequence is split into segments
+    const int64_t lane_kernel_min = (int64_t)cus * 4 * 4 * 64;
+    if (lanes >= lane_kernel_min || T <= 16) return p;
+    p.kernel = WKV_KERNEL_SEGMENTED;
+    p.segments = 16;
+    p.seg_len = 16;
+    return p;
+}
+
+wkv_status check_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                         const float *k, const float *v, const float *y, const float *s_in,
+                         const float *s_out) {
+    if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(B, T, C);
+    const int64_t st = bytes_of(3, B, C);
+    const int64_t ch = bytes_of(1, 1, C);
+    if (seq < 0 || st < 0 || ch < 0) return WKV_ERR_OVERFLOW;
+    if (B * C > 0 && (!w || !u)) return WKV_ERR_NULL;
+    if (seq > 0 && (!k || !v || !y)) return WKV_ERR_NULL;
+    const Range rw = rng(w, B * C > 0 ? ch : 0), ru = rng(u, B * C > 0 ? ch : 0);
+    const Range rk = rng(k, seq), rv = rng(v, seq), ry = rng(y, seq);
+    const Range ri = rng(s_in, st), ro = rng(s_out, st);
+    for (Range r : {rw, ru, rk, rv, ri, ro})
+        if (overlap(ry, r)) return WKV_ERR_ALIAS;
+    for (Range r : {rw, ru, rk, rv})
+        if (overlap(ro, r)) return WKV_ERR_ALIAS;
+    if (overlap(ro, ri) && s_out != (float *)s_in) return WKV_ERR_ALIAS;
+    return WKV_OK;
+}
+
+wkv_status from_hip(hipError_t e) { return e == hipSuccess ? WKV_OK : WKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+WKV_API const char *wkv_status_string(wkv_status s) {
+    switch (s) {
+        case WKV_OK: return "ok";
+        case WKV_ERR_NULL: return "a required pointer is NULL";
+        case WKV_ERR_DIM: return "a dimension is negative";
+        case WKV_ERR_OVERFLOW: return "a tensor's byte size overflows int64";
+        case WKV_ERR_ALIAS: return "an output overlaps an input or another output";
+        case WKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case WKV_ERR_UNSUPPORTED: return "no compiled kernel for this plan or shape";
+        case WKV_ERR_HIP: return "HIP runtime or launch error";
+        default: return "unknown status";
+    }
+}
+
+WKV_API wkv_status wkv_forward_plan_auto(int64_t B, int64_t T, int64_t C, wkv_forward_plan *plan) {
+    if (!plan) return WKV_ERR_NULL;
+    if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
+    if (bytes_of(B, T, C) < 0) return WKV_ERR_OVERFLOW;
+    *plan = auto_plan(B, T, C, device_cus());
+    return WKV_OK;
+}
+
+WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                                  const float *k, const float *v, float *y,
+                                  const float *state_in, float *state_out,
+                                  const wkv_forward_plan *plan, hipStream_t stream) {
+    wkv_status st = check_forward(B, T, C, w, u, k, v, y, state_in, state_out);
+    if (st != WKV_OK) return st;
+    wkv_forward_plan p{WKV_KERNEL_AUTO, 0, 0, 0};
+    if (plan) p = *plan;
+    if (p.reserved != 0) return WKV_ERR_UNSUPPORTED;
+    switch (p.kernel) {
+        case WKV_KERNEL_AUTO:
+        case WKV_KERNEL_LANE:
+            break;
+        case WKV_KERNEL_SEGMENTED:
+            if (p.segments == 0) p.segments = 16;
+            if (p.seg_len == 0) p.seg_len = 16;
+            if (!wkv::forward_seg_supported(p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
+            break;
+        case WKV_KERNEL_LOOKBACK:
+            if (p.segments == 0) p.segments = 4;
+            if (p.seg_len == 0) p.seg_len = 16;
+            if (!wkv::forward_lookback_supported(p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
+            break;
+        default:
+            return WKV_ERR_UNSUPPORTED;
+    }
+    const int64_t lanes = B * C;
+    if (lanes == 0) return WKV_OK;
+    if (T == 0) {
+        if (!state_out || state_out == state_in) return WKV_OK;
+        return from_hip(wkv::launch_state_copy(lanes, state_in, state_out, stream));
+    }
+    if (p.kernel == WKV_KERNEL_AUTO) p = auto_plan(B, T, C, device_cus());
+    const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out};
+    if (p.kernel == WKV_KERNEL_LANE) {
+        if ((lanes + 255) / 256 > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
+        return from_hip(wkv::launch_forward_lane(a, stream));
+    }
+    if (p.kernel == WKV_KERNEL_LOOKBACK) {
+        const int64_t ntiles = wkv::lookback_tiles(B, T, C, p.segments, p.seg_len);
+        if (ntiles > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
+        const size_t need = wkv::lookback_scratch_bytes(ntiles);
+        if (need > kLookbackScratchMax) return WKV_ERR_UNSUPPORTED;
+        void *scratch = nullptr;
+        const hipError_t e = stream_scratch(stream, need, &scratch);
+        if (e != hipSuccess) return WKV_ERR_HIP;
+        return from_hip(wkv::launch_forward_lookback(a, p.segments, p.seg_len, scratch, stream));
+    }
+    if (B * ((C + 63) / 64) > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
+    return from_hip(wkv::launch_forward_seg(a, p.segments, p.seg_len, stream));
+}
+
+WKV_API wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                               const float *k, const float *v, float *y, const float *state_in,
+                               float *state_out, hipStream_t stream) {
+    return wkv_forward_ex(B, T, C, w, u, k, v, y, state_in, state_out, nullptr, stream);
+}
+
+WKV_API wkv_status wkv_step(int64_t L, int64_t B, int64_t C, const float *w, const float *u,
+                            const float *k, const float *v, float *y, const float *state_in,
+                            float *state_out, hipStream_t stream) {
+    if (L < 0 || B < 0 || C < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(L, B, C);
+    const int64_t st = bytes_of(3 * L, B, C);
+    const int64_t ch = bytes_of(L, 1, C);
+    if (seq < 0 || st < 0 || ch < 0 || L > INT64_MAX / 3) return WKV_ERR_OVERFLOW;
+    if (seq == 0) return WKV_OK;
+    if (!w || !u || !k || !v || !y || !state_in || !state_out) return WKV_ERR_NULL;
+    const Range rw = rng(w, ch), ru = rng(u, ch), rk = rng(k, seq), rv = rng(v, seq),
+                ry = rng(y, seq), ri = rng(state_in, st), ro = rng(state_out, st);
+    for (Range r : {rw, ru, rk, rv, ri, ro})
+        if (overlap(ry, r)) return WKV_ERR_ALIAS;
+    for (Range r : {rw, ru, rk, rv})
+        if (overlap(ro, r)) return WKV_ERR_ALIAS;
+    if (overlap(ro, ri) && state_out != (float *)state_in) return WKV_ERR_ALIAS;
+    if (L * B > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
+    const StepArgs a{L, B, C, w, u, k, v, y, state_in, state_out};
+    return from_hip(wkv::launch_step(a, stream));
+}
+
+WKV_API size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0 || bytes_of(B, T, C) < 0) return 0;
+    return wkv::backward_workspace_bytes(B, T, C);
+}
+
+WKV_API wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                                const float *k, const float *v, const float *dy, float *dk,
+                                float *dv, float *dw, float *du, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(B, T, C);
+    const int64_t ch = bytes_of(1, 1, C);
+    if (seq < 0 || ch < 0) return WKV_ERR_OVERFLOW;
+    if (C == 0) return WKV_OK;
+    if (!dw || !du) return WKV_ERR_NULL;
+    if (seq > 0 && (!w || !u || !k || !v || !dy || !dk || !dv)) return WKV_ERR_NULL;
+    const size_t need = wkv::backward_workspace_bytes(B, T, C);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return WKV_ERR_WORKSPACE;
+    const Range rw = rng(w, seq > 0 ? ch : 0), ru = rng(u, seq > 0 ? ch : 0);
+    const Range rk = rng(k, seq), rv = rng(v, seq), rg = rng(dy, seq);
+    const Range rdk = rng(dk, seq), rdv = rng(dv, seq), rdw = rng(dw, ch), rdu = rng(du, ch);
+    const Range rws = rng(workspace, (int64_t)need);
+    const Range outs[] = {rdk, rdv, rdw, rdu, rws};
+    for (int i = 0; i < 5; ++i) {
+        for (Range r : {rw, ru, rk, rv, rg})
+            if (overlap(outs[i], r)) return WKV_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(outs[i], outs[j])) return WKV_ERR_ALIAS;
+    }
+    const BwdArgs a{B, T, C, w, u, k, v, dy, dk, dv, dw, du, workspace};
+    return from_hip(wkv::launch_backward(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,450 @@
+// wkv_backward.hip -- gradients dk, dv, dw, du of the GPT-mode WKV forward (gfx950).
+//
+// The pages give no backward; this differentiates the closed form (RWKV
+// architecture deep dive, youngju.dev, "WKV mechanism: core computation") with
+// the empty initial state.  With g_t = dy_t, D_t the denominator of output t,
+// lambda_t = log2 D_t, and for token i the sums over later outputs
+//   R_i  = sum_{t>i} g_t 2^{-(t-1-i)W - lambda_t}          S_i  = same with g_t y_t
+//   R'_i = sum_{t>i} (t-1-i) g_t 2^{-(t-1-i)W - lambda_t}  S'_i = same with g_t y_t
+// the gradients are
+//   dv_i = p_ii g_i + e^{k_i} R_i
+//   dk_i = p_ii g_i (v_i - y_i) + e^{k_i} (v_i R_i - S_i)
+//   dw  -= e^{k_i} (v_i R'_i - S'_i),      du += p_ii g_i (v_i - y_i)
+// where p_ii is the weight of token i in its own output.  Stepping from i to
+// i-1:  R_{i-1} = g_i 2^{-lambda_i} + 2^{-W} R_i,  R'_{i-1} = 2^{-W} (R'_i + R_i).
+// The four sums are kept scaled by 2^rho, where rho tracks max(-lambda_i,
+// rho_i - W) within a fixed margin, so that e^{k_i} 2^{rho_i} stays within a
+// bounded factor of the largest weight of token i in any later output (at most
+// 1) and nothing overflows.
+//
+// One workgroup owns (sequence b, 64 channels) and the whole sequence, NW waves
+// each owning a segment of LS tokens in every tile of NW*LS tokens:
+//   phase 1 (tiles forward)  fold k, v into segment summaries, scan them across
+//            waves, and store each segment's starting state (a, b, anchor, steps)
+//            in the workspace;
+//   phase 2 (tiles backward) reload k, v, dy; recompute y, lambda and p_ii from
+//            the stored starting state; fold each segment's tokens backward into
+//            a local (R, S, R', S', rho) summary; scan the summaries backward
+//            across waves (composing over a stretch of len tokens:
+//            R = R_early + 2^{-W len} R_late, R' = R'_early + 2^{-W len}(R'_late +
+//            len R_late)); re-sweep backward from each segment's suffix state,
+//            emitting dk, dv and accumulating dw, du.
+// dw and du: per-thread float sums, combined across waves and then across the
+// batch in double precision in a fixed order (deterministic; no atomics).
+#include "wkv_device.hpp"
+#include "wkv_internal.hpp"
+
+namespace wkv {
+
+namespace {
+
+constexpr int kBwdNW = 16;
+constexpr int kBwdLS = 8;
+
+// Reverse-scan state: the four sums in the frame 2^rho, rho = r0 - m W kept as
+// an anchor and a step count (as for the forward Lane: one rounding per use,
+// no drift along the sequence).
+struct Rev {
+    float R, S, R1, S1;
+    float r0;  // anchor exponent (log2 units)
+    float m;   // decay steps since the anchor
+};
+
+__device__ __forceinline__ Rev rev_empty() { return Rev{0.0f, 0.0f, 0.0f, 0.0f, kEmpty2, 0.0f}; }
+__device__ __forceinline__ float rev_rho(const Rev &z, float W) { return fmaf(-z.m, W, z.r0); }
+
+// Hysteresis of the reverse frame (log2 units): the frame moves only when a new
+// term exceeds it by more than 2^kRevHyst.  After a dominant token (k = +60,
+// say) every later denominator decays by exactly W per token, in step with the
+// frame itself, so "is the new term above the frame" is a tie decided by
+// rounding at every token; re-anchoring on each of those ties chains thousands
+// of rounded scale factors into the sums (percent-level errors).  With the
+// margin the frame holds, the stored sums grow by at most 2^kRevHyst per part
+// (2^(2 kRevHyst) after compositions), far inside float range.
+constexpr float kRevHyst = 8.0f;
+
+// Fold output token i (gradient g, output y, lambda = log2 D_i) into the sums.
+__device__ __forceinline__ void rev_absorb(Rev &z, float g, float y, float lam, float W) {
+    const float m1 = z.m + 1.0f;
+    const float old = fmaf(m1, -W, z.r0);  // frame of the sums, decayed one step
+    const float d = old + lam;             // old frame minus the new term's exponent -lam
+    const bool keep_old = d > -kRevHyst;
+    const float E = ex2(keep_old ? -d : d);
+    const float fo = keep_old ? 1.0f : E;
+    const float fn = keep_old ? E : 1.0f;
+    const float gn = fn * g;
+    z.R1 = fo * (z.R1 + z.R);
+    z.S1 = fo * (z.S1 + z.S);
+    z.R = fmaf(fo, z.R, gn);
+    z.S = fmaf(fo, z.S, gn * y);
+    z.r0 = keep_old ? z.r0 : -lam;
+    z.m = keep_old ? m1 : 0.0f;
+}
+
+// e <- e (+) l: the sums of a stretch of `len` tokens (e, earlier in time)
+// followed by the sums of everything after it (l), seen from before the
+// stretch.  l's frame moves by len decay steps, which only extends its anchor's
+// step count.
+__device__ __forceinline__ void rev_compose(Rev &e, const Rev &l, float W, float len) {
+    const float lm = l.m + len;
+    const float ld = fmaf(-lm, W, l.r0);
+    const float d = ld - rev_rho(e, W);
+    const bool late_big = d > kRevHyst;  // same hysteresis as rev_absorb
+    const float E = ex2(late_big ? -d : d);
+    const float fe = late_big ? E : 1.0f;
+    const float fl = late_big ? 1.0f : E;
+    e.R1 = fmaf(fe, e.R1, fl * fmaf(len, l.R, l.R1));
+    e.S1 = fmaf(fe, e.S1, fl * fmaf(len, l.S, l.S1));
+    e.R = fmaf(fe, e.R, fl * l.R);
+    e.S = fmaf(fe, e.S, fl * l.S);
+    e.r0 = late_big ? l.r0 : e.r0;
+    e.m = late_big ? lm : e.m;
+}
+
+template <int NW>
+struct BwdShared {
+    float f[2][4][NW][64];
+    float r[2][6][NW][64];
+    double red[2][NW][64];
+};
+
+template <int NW>
+__device__ __forceinline__ void fwd_put(BwdShared<NW> &sh, int buf, int s, int lane, const Lane &L) {
+    sh.f[buf][0][s][lane] = L.a;
+    sh.f[buf][1][s][lane] = L.b;
+    sh.f[buf][2][s][lane] = L.e0;
+    sh.f[buf][3][s][lane] = L.n;
+}
+
+template <int NW>
+__device__ __forceinline__ Lane fwd_get(const BwdShared<NW> &sh, int buf, int s, int lane) {
+    return Lane{sh.f[buf][0][s][lane], sh.f[buf][1][s][lane], sh.f[buf][2][s][lane],
+                sh.f[buf][3][s][lane]};
+}
+
+template <int NW>
+__device__ __forceinline__ void rev_put(BwdShared<NW> &sh, int buf, int s, int lane, const Rev &z) {
+    sh.r[buf][0][s][lane] = z.R;
+    sh.r[buf][1][s][lane] = z.S;
+    sh.r[buf][2][s][lane] = z.R1;
+    sh.r[buf][3][s][lane] = z.S1;
+    sh.r[buf][4][s][lane] = z.r0;
+    sh.r[buf][5][s][lane] = z.m;
+}
+
+template <int NW>
+__device__ __forceinline__ Rev rev_get(const BwdShared<NW> &sh, int buf, int s, int lane) {
+    return Rev{sh.r[buf][0][s][lane], sh.r[buf][1][s][lane], sh.r[buf][2][s][lane],
+               sh.r[buf][3][s][lane], sh.r[buf][4][s][lane], sh.r[buf][5][s][lane]};
+}
+
+// LS rows t0.. of one tensor through a wave-uniform descriptor (rows past the
+// end of the sequence are not read and hold 0).
+template <int LS>
+__device__ __forceinline__ void load_seg(float (&X)[LS], const TileRows &r, int64_t t0, int64_t T) {
+    if (t0 + LS <= T) {
+#pragma unroll
+        for (int j = 0; j < LS; ++j) X[j] = r.ld(j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < LS; ++j) X[j] = (t0 + j < T) ? r.ld(j) : 0.0f;
+    }
+}
+
+// Forward token for the recompute: y, lambda = log2 D and the own weight p_ii.
+template <bool SAFE>
+__device__ __forceinline__ void fwd_token(Lane &L, float K, float v, const Chan &ch, float &y,
+                                          float &lam, float &pii) {
+    const float o = lane_o(L, ch.W);  // frame of the past sums before this token
+    const float n1 = L.n + 1.0f;
+    const float h = fmaf(n1, -ch.W, L.e0);
+    const float s = K - h;
+    const float E = ex2(-fabsf(s));
+    const bool pos = s > 0.0f;
+    const float P = pos ? E : 1.0f;
+    const float Q = pos ? 1.0f : E;
+    if constexpr (!SAFE) {
+        const float aP = L.a * P, bP = L.b * P, Qc = Q * ch.c1;
+        const float den = bP + Qc;
+        const float r = rcp(den);
+        y = fmaf(Qc, v, aP) * r;
+        pii = Qc * r;
+        // D = 2^{o} (b + c1 2^s) = 2^{max(h, K) + W} den
+        lam = (pos ? K + ch.W : o) + lg2(den);
+    } else {
+        const float x = (ch.U + K) - o;
+        const float F = ex2(-fabsf(x));
+        const bool px = x > 0.0f;
+        const float Pp = px ? F : 1.0f, Qq = px ? 1.0f : F;
+        const float den = fmaf(L.b, Pp, Qq);
+        const float r = rcp(den);
+        y = fmaf(Qq, v, L.a * Pp) * r;
+        pii = Qq * r;
+        // D = 2^{max(o, U + K)} den
+        lam = fmaxf(o, ch.U + K) + lg2(den);
+    }
+    L.a = fmaf(L.a, P, Q * v);
+    L.b = fmaf(L.b, P, Q);
+    L.e0 = pos ? K : L.e0;
+    L.n = pos ? 0.0f : n1;
+}
+
+template <int NW, int LS, bool SAFE>
+__device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_t bb, int64_t c,
+                                         bool active, const Chan &ch, const float *kseq,
+                                         const float *vseq, const float *gseq, float *dkseq,
+                                         float *dvseq, uint32_t voff, float *__restrict__ ck,
+                                         double *__restrict__ part, BwdShared<NW> &sh) {
+    constexpr int TT = NW * LS;
+    const int lane = threadIdx.x & 63;
+    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t rowb = (uint32_t)(C * 4);
+    auto rows = [&](const float *seq, int64_t t0) { return TileRows(seq + t0 * C, voff, rowb); };
+    const int64_t ntiles = (T + TT - 1) / TT;
+
+    // ---------------- phase 1: starting state of every segment ----------------
+    {
+        Lane carry = lane_empty();
+        float Kc[LS], Vc[LS];
+        load_seg<LS>(Kc, rows(kseq, (int64_t)s * LS), (int64_t)s * LS, T);
+        load_seg<LS>(Vc, rows(vseq, (int64_t)s * LS), (int64_t)s * LS, T);
+        for (int64_t tile = 0; tile < ntiles; ++tile) {
+            const int64_t t0 = tile * TT + (int64_t)s * LS;
+            float Kn[LS], Vn[LS];
+            if (tile + 1 < ntiles) {
+                load_seg<LS>(Kn, rows(kseq, t0 + TT), t0 + TT, T);
+                load_seg<LS>(Vn, rows(vseq, t0 + TT), t0 + TT, T);
+            }
+            Lane S = lane_empty();
+#pragma unroll
+            for (int j = 0; j < LS; ++j)
+                if (t0 + j < T) absorb(S, Kc[j] * kLog2e, Vc[j], ch);
+            int buf = 0;
+#pragma unroll
+            for (int d = 1; d < NW; d <<= 1) {
+                fwd_put(sh, buf, s, lane, S);
+                __syncthreads();
+                if (s >= d) {
+                    Lane X = fwd_get(sh, buf, s - d, lane);
+                    compose(X, S, ch.W, (float)(d * LS));
+                    S = X;
+                }
+                buf ^= 1;
+            }
+            fwd_put(sh, buf, s, lane, S);
+            __syncthreads();
+            Lane R = carry;
+            if (s > 0) compose(R, fwd_get(sh, buf, s - 1, lane), ch.W, (float)(s * LS));
+            compose(carry, fwd_get(sh, buf, NW - 1, lane), ch.W, (float)TT);
+            float *q = ck + ((tile * NW + s) * 4) * 64 + lane;
+            q[0] = R.a;
+            q[64] = R.b;
+            q[128] = R.e0;
+            q[192] = R.n;
+#pragma unroll
+            for (int j = 0; j < LS; ++j) {
+                Kc[j] = Kn[j];
+                Vc[j] = Vn[j];
+            }
+        }
+    }
+
+    // ---------------- phase 2: tiles in reverse ----------------
+    float dw_acc = 0.0f, du_acc = 0.0f;
+    Rev carry = rev_empty();
+    float Kc[LS], Vc[LS], Gc[LS];
+    {
+        const int64_t t0 = (ntiles - 1) * TT + (int64_t)s * LS;
+        load_seg<LS>(Kc, rows(kseq, t0), t0, T);
+        load_seg<LS>(Vc, rows(vseq, t0), t0, T);
+        load_seg<LS>(Gc, rows(gseq, t0), t0, T);
+    }
+    for (int64_t tile = ntiles - 1; tile >= 0; --tile) {
+        const int64_t t0 = tile * TT + (int64_t)s * LS;
+        float Kn[LS], Vn[LS], Gn[LS];
+        if (tile > 0) {
+            load_seg<LS>(Kn, rows(kseq, t0 - TT), t0 - TT, T);
+            load_seg<LS>(Vn, rows(vseq, t0 - TT), t0 - TT, T);
+            load_seg<LS>(Gn, rows(gseq, t0 - TT), t0 - TT, T);
+        }
+        // forward recompute of y, lambda, p_ii from the stored starting state
+        float Y[LS], LAM[LS], PII[LS];
+        {
+            const float *q = ck + ((tile * NW + s) * 4) * 64 + lane;
+            Lane L{q[0], q[64], q[128], q[192]};
+#pragma unroll
+            for (int j = 0; j < LS; ++j) {
+                Y[j] = 0.0f;
+                LAM[j] = 0.0f;
+                PII[j] = 0.0f;
+                if (t0 + j < T) fwd_token<SAFE>(L, Kc[j] * kLog2e, Vc[j], ch, Y[j], LAM[j], PII[j]);
+            }
+        }
+        // local backward summary of this segment
+        Rev z = rev_empty();
+#pragma unroll
+        for (int j = LS - 1; j >= 0; --j)
+            if (t0 + j < T) rev_absorb(z, Gc[j], Y[j], LAM[j], ch.W);
+        // inclusive scan from the last segment backward (Hillis-Steele)
+        int buf = 0;
+#pragma unroll
+        for (int d = 1; d < NW; d <<= 1) {
+            rev_put(sh, buf, s, lane, z);
+            __syncthreads();
+            if (s + d < NW) rev_compose(z, rev_get(sh, buf, s + d, lane), ch.W, (float)(d * LS));
+            buf ^= 1;
+        }
+        rev_put(sh, buf, s, lane, z);
+        __syncthreads();
+        Rev suf = rev_empty();
+        if (s + 1 < NW) suf = rev_get(sh, buf, s + 1, lane);
+        const Rev agg = rev_get(sh, buf, 0, lane);
+        rev_compose(suf, carry, ch.W, (float)((NW - 1 - s) * LS));
+        {
+            Rev nc = agg;
+            rev_compose(nc, carry, ch.W, (float)TT);
+            carry = nc;
+        }
+        // re-sweep backward from the suffix state, emitting gradients
+        const TileRows dkr = rows(dkseq, t0), dvr = rows(dvseq, t0);
+#pragma unroll
+        for (int j = LS - 1; j >= 0; --j) {
+            if (t0 + j < T) {
+                const float K = Kc[j] * kLog2e;
+                const float v = Vc[j], g = Gc[j], y = Y[j];
+                const float ek = ex2(K + rev_rho(suf, ch.W));
+                const float own = PII[j] * g;
+                const float vy = v - y;
+                if (active) {
+                    dvr.st(j, fmaf(ek, suf.R, own));
+                    dkr.st(j, fmaf(own, vy, ek * fmaf(v, suf.R, -suf.S)));
+                }
+                dw_acc = fmaf(-ek, fmaf(v, suf.R1, -suf.S1), dw_acc);
+                du_acc = fmaf(own, vy, du_acc);
+                rev_absorb(suf, g, y, LAM[j], ch.W);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < LS; ++j) {
+            Kc[j] = Kn[j];
+            Vc[j] = Vn[j];
+            Gc[j] = Gn[j];
+        }
+    }
+
+    // dw, du of this lane: sum over the waves in a fixed order
+    sh.red[0][s][lane] = (double)dw_acc;
+    sh.red[1][s][lane] = (double)du_acc;
+    __syncthreads();
+    if (s == 0 && active) {
+        double sw = 0.0, su = 0.0;
+        for (int i = 0; i < NW; ++i) {
+            sw += sh.red[0][i][lane];
+            su += sh.red[1][i][lane];
+        }
+        part[bb * C + c] = sw;
+        part[B * C + bb * C + c] = su;
+    }
+}
+
+template <int NW, int LS>
+__global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, int64_t C,
+                                                          const float *__restrict__ w,
+                                                          const float *__restrict__ u,
+                                                          const float *__restrict__ k,
+                                                          const float *__restrict__ v,
+                                                          const float *__restrict__ dy,
+                                                          float *__restrict__ dk,
+                                                          float *__restrict__ dv,
+                                                          float *__restrict__ ckpt,
+                                                          double *__restrict__ part) {
+    __shared__ BwdShared<NW> sh;
+    constexpr int TT = NW * LS;
+    const int64_t ngroups = (C + 63) / 64;
+    const int64_t g = blockIdx.x % ngroups;
+    const int64_t bb = blockIdx.x / ngroups;
+    const int64_t c = g * 64 + (threadIdx.x & 63);
+    const bool active = c < C;
+    const Chan ch = make_chan(active ? w[c] : 0.0f, active ? u[c] : 0.0f);
+    const bool fast = __syncthreads_and(chan_fast_ok(ch));
+    const int64_t ntiles = (T + TT - 1) / TT;
+    // wave-uniform base of this (sequence, channel group); inactive lanes read
+    // the group's first channel and never store
+    const int64_t base = bb * T * C + g * 64;
+    const uint32_t voff = active ? (uint32_t)(threadIdx.x & 63) * 4u : 0u;
+    float *ck = ckpt + (int64_t)blockIdx.x * ntiles * NW * 4 * 64;
+    if (fast)
+        bwd_body<NW, LS, false>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
+                                dk + base, dv + base, voff, ck, part, sh);
+    else
+        bwd_body<NW, LS, true>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
+                               dk + base, dv + base, voff, ck, part, sh);
+}
+
+// dw[c], du[c] = sums over the batch of the per-lane parts, in order b = 0..B-1.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(int64_t B, int64_t C,
+                                                         const double *__restrict__ part,
+                                                         float *__restrict__ dw,
+                                                         float *__restrict__ du) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= C) return;
+    double sw = 0.0, su = 0.0;
+    for (int64_t b = 0; b < B; ++b) {
+        sw += part[b * C + c];
+        su += part[B * C + b * C + c];
+    }
+    dw[c] = (float)sw;
+    du[c] = (float)su;
+}
+
+// dw = du = 0 when there are no tokens.
+__global__ __launch_bounds__(256) void bwd_zero_kernel(int64_t C, float *__restrict__ dw,
+                                                       float *__restrict__ du) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= C) return;
+    dw[c] = 0.0f;
+    du[c] = 0.0f;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C) {
+    if (B <= 0 || T <= 0 || C <= 0) return 0;
+    constexpr int64_t TT = kBwdNW * kBwdLS;
+    const int64_t ngroups = (C + 63) / 64;
+    const int64_t ntiles = (T + TT - 1) / TT;
+    const size_t ck = (size_t)B * ngroups * ntiles * kBwdNW * 4 * 64 * sizeof(float);
+    const size_t part = (size_t)2 * B * C * sizeof(double);
+    return align_up(ck) + align_up(part);
+}
+
+hipError_t launch_backward(const BwdArgs &a, hipStream_t st) {
+    const int64_t C = a.C;
+    if (a.B == 0 || a.T == 0) {
+        if (C == 0) return hipSuccess;
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,
+                           C, a.dw, a.du);
+        return hipGetLastError();
+    }
+    constexpr int64_t TT = kBwdNW * kBwdLS;
+    const int64_t ngroups = (C + 63) / 64;
+    const int64_t ntiles = (a.T + TT - 1) / TT;
+    float *ck = (float *)a.ws;
+    double *part = (double *)((char *)a.ws +
+                              align_up((size_t)a.B * ngroups * ntiles * kBwdNW * 4 * 64 *
+                                       sizeof(float)));
+    const int64_t grid = a.B * ngroups;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS>), dim3((unsigned)grid), dim3(kBwdNW * 64),
+                       0, st, a.B, a.T, C, a.w, a.u, a.k, a.v, a.dy, a.dk, a.dv, ck, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,
+                       a.B, C, part, a.dw, a.du);
+    return hipGetLastError();
+}
+
+}  // namespace wkv

@@ -1,0 +1,206 @@
+// wkv_device.hpp -- device-side arithmetic of the WKV operator for gfx950.
+//
+// The operator (RWKV architecture deep dive, youngju.dev, "WKV mechanism: core
+// computation"): per lane, wkv_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t})
+// where A, B are the running sums of e^{k_i} v_i and e^{k_i}, decayed by e^{-w}
+// per later token ("Recurrent formulation"), kept as a scaled pair and a running
+// maximum exponent ("Numerical stability via log-space computation").
+//
+// Inside kernels every exponent is held in log2 units (K = k log2 e, W = w log2 e,
+// U = u log2 e, o2 = o log2 e) so that each exponential is one v_exp_f32.  The
+// register state of a lane is a Lane: the scaled sums and their frame exponent,
+// kept as an anchor plus a count of decay steps.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Exponent of the empty state inside kernels (log2 units).  Finite, so that
+// differences against it stay ordered; exp2 of minus it is exactly 0.
+constexpr float kEmpty2 = -1.0e38f;
+// |U - W| (log2 units) up to which the one-exponential step is used; beyond it
+// e^{u-w} could leave the float range and the two-exponential step runs.
+constexpr float kFastLimit2 = 86.0f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Per-channel constants of one lane.
+struct Chan {
+    float W;   // w log2 e
+    float U;   // u log2 e
+    float c1;  // e^{u-w} = 2^{U-W}: the bonus relative to one step of decay
+};
+
+__device__ __forceinline__ Chan make_chan(float w, float u) {
+    Chan ch;
+    ch.W = w * kLog2e;
+    ch.U = u * kLog2e;
+    ch.c1 = ex2(ch.U - ch.W);
+    return ch;
+}
+
+__device__ __forceinline__ bool chan_fast_ok(const Chan &ch) {
+    return fabsf(ch.U - ch.W) <= kFastLimit2;
+}
+
+// Register state of one lane: the sums (a, b) of all tokens so far, in the
+// frame 2^f with f = e0 - n W.  e0 is the exponent at which the frame was last
+// re-anchored (the token that became the largest decayed term, or the start of
+// a segment) and n the number of decay steps since then.  Deriving f from the
+// anchor with one fma keeps its error at one rounding: stepping f <- f - W
+// token after token (as a direct transcription of the log-space recurrence
+// would) accumulates a systematic rounding bias of up to half an ulp of f per
+// token, which at |f| ~ 90 and small W reaches percent-level errors in the
+// weights after a few thousand tokens.
+struct Lane {
+    float a, b;  // scaled numerator and denominator
+    float e0;    // anchor exponent (log2 units)
+    float n;     // decay steps since the anchor (exact in float up to 2^24)
+};
+
+__device__ __forceinline__ Lane lane_at(float a, float b, float o) { return Lane{a, b, o, 0.0f}; }
+__device__ __forceinline__ Lane lane_empty() { return Lane{0.0f, 0.0f, kEmpty2, 0.0f}; }
+// Frame exponent of the sums after the last token.
+__device__ __forceinline__ float lane_o(const Lane &L, float W) { return fmaf(-L.n, W, L.e0); }
+
+// One token against the state, then folded into it.  Returns wkv_t.
+//
+// The past sums, decayed for this token, sit at h = e0 - (n+1) W.  With
+// s = K - h the update keeps the larger of h and K as the new frame:
+//   s <= 0:  a' = a + 2^s v,        b' = b + 2^s,        frame h (n+1 steps)
+//   s >  0:  a' = a 2^{-s} + v,     b' = b 2^{-s} + 1,   frame K (re-anchored)
+// The output needs the bonus term e^{u+k_t} relative to the undecayed past
+// frame h + W, i.e. 2^{U + K - h - W} = c1 2^s; scaling numerator and
+// denominator by the update's factor (1 or 2^{-s}) gives
+//   y = (a P + c1 Q v) / (b P + c1 Q),   (P, Q) = s > 0 ? (2^{-s}, 1) : (1, 2^s)
+// so one exponential E = 2^{-|s|} serves both.  Valid while c1 is a normal
+// float with margin, i.e. |U - W| <= kFastLimit2.
+__device__ __forceinline__ float step_fast(Lane &L, float K, float v, const Chan &ch) {
+    const float n1 = L.n + 1.0f;
+    const float h = fmaf(n1, -ch.W, L.e0);
+    const float s = K - h;
+    const float E = ex2(-fabsf(s));
+    const bool pos = s > 0.0f;
+    const float P = pos ? E : 1.0f;
+    const float Q = pos ? 1.0f : E;
+    const float aP = L.a * P;
+    const float bP = L.b * P;
+    const float Qc = Q * ch.c1;
+    const float y = fmaf(Qc, v, aP) * rcp(bP + Qc);
+    L.a = fmaf(Q, v, aP);
+    L.b = bP + Q;
+    L.e0 = pos ? K : L.e0;
+    L.n = pos ? 0.0f : n1;
+    return y;
+}
+
+// The same token with the output normalised on its own maximum (two
+// exponentials); valid for any finite u, w.
+__device__ __forceinline__ float step_safe(Lane &L, float K, float v, const Chan &ch) {
+    const float o = lane_o(L, ch.W);
+    const float x = (ch.U + K) - o;
+    const float F = ex2(-fabsf(x));
+    const bool px = x > 0.0f;
+    const float Pp = px ? F : 1.0f;
+    const float Qq = px ? 1.0f : F;
+    const float y = fmaf(Qq, v, L.a * Pp) * rcp(fmaf(L.b, Pp, Qq));
+    const float n1 = L.n + 1.0f;
+    const float h = fmaf(n1, -ch.W, L.e0);
+    const float s = K - h;
+    const float E = ex2(-fabsf(s));
+    const bool pos = s > 0.0f;
+    const float P = pos ? E : 1.0f;
+    const float Q = pos ? 1.0f : E;
+    L.a = fmaf(L.a, P, Q * v);
+    L.b = fmaf(L.b, P, Q);
+    L.e0 = pos ? K : L.e0;
+    L.n = pos ? 0.0f : n1;
+    return y;
+}
+
+template <bool SAFE>
+__device__ __forceinline__ float step(Lane &L, float K, float v, const Chan &ch) {
+    if constexpr (SAFE)
+        return step_safe(L, K, v, ch);
+    else
+        return step_fast(L, K, v, ch);
+}
+
+// Fold a token into the state without producing an output (segment summaries).
+__device__ __forceinline__ void absorb(Lane &L, float K, float v, const Chan &ch) {
+    const float n1 = L.n + 1.0f;
+    const float h = fmaf(n1, -ch.W, L.e0);
+    const float s = K - h;
+    const float E = ex2(-fabsf(s));
+    const bool pos = s > 0.0f;
+    const float P = pos ? E : 1.0f;
+    const float Q = pos ? 1.0f : E;
+    L.a = fmaf(L.a, P, Q * v);
+    L.b = fmaf(L.b, P, Q);
+    L.e0 = pos ? K : L.e0;
+    L.n = pos ? 0.0f : n1;
+}
+
+// X <- X (+) Y: the state X followed by a stretch of `len` tokens whose
+// contribution from an empty start is Y (both anchored Lanes).  X decays by
+// 2^{-W len} across the stretch, which only adds len to its step count (exact
+// in float), then the two sums add in the larger frame.  No exponent is ever
+// rounded and stored, so long chains of compositions (one per tile of a long
+// sequence) do not drift.  Empty operands are identities.
+__device__ __forceinline__ void compose(Lane &X, const Lane &Y, float W, float len) {
+    const float nxl = X.n + len;
+    const float fx = fmaf(-nxl, W, X.e0);
+    const float fy = fmaf(-Y.n, W, Y.e0);
+    const float d = fx - fy;
+    const float E = ex2(-fabsf(d));
+    const bool xbig = d > 0.0f;
+    const float P = xbig ? 1.0f : E;
+    const float Q = xbig ? E : 1.0f;
+    X.a = fmaf(X.a, P, Y.a * Q);
+    X.b = fmaf(X.b, P, Y.b * Q);
+    X.e0 = xbig ? X.e0 : Y.e0;
+    X.n = xbig ? nxl : Y.n;
+}
+
+// Consecutive rows of a row-major [rows][C] float tensor, seen by one wave.
+// `base` must be wave-uniform (it becomes a buffer descriptor in scalar
+// registers); `voff` is the lane's byte offset inside a row and `rowb` = 4*C
+// the row pitch.  Row j is addressed by the scalar offset j*rowb, so an access
+// is a single buffer instruction with one 32-bit vector offset.  Offsets stay
+// below 2^32 bytes from `base`.
+struct TileRows {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t voff;
+    uint32_t rowb;
+    __device__ __forceinline__ TileRows(const float *base, uint32_t voff_, uint32_t rowb_)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0,
+                                              (int)0xffffffffu, kBufferWord3)),
+          voff(voff_), rowb(rowb_) {}
+    // The b32 buffer builtins move raw 32-bit words (unsigned int): bit-cast,
+    // never convert.
+    __device__ __forceinline__ float ld(int j) const {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, (uint32_t)j * rowb, 0));
+    }
+    __device__ __forceinline__ void st(int j, float x) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff,
+                                              (uint32_t)j * rowb, 0);
+    }
+
+    // Buffer descriptor word 3 for gfx9-family raw 32-bit accesses
+    // (DATA_FORMAT = 32 bits).
+    static constexpr int kBufferWord3 = 0x00020000;
+};
+
+// ABI state (natural-log exponent) -> kernel exponent (log2), mapping -inf and
+// anything below the empty sentinel onto it.
+__device__ __forceinline__ float o_in(float o_nat) { return fmaxf(o_nat * kLog2e, kEmpty2); }
+__device__ __forceinline__ float o_out(float o2) { return o2 * kLn2; }
+
+}  // namespace wkv

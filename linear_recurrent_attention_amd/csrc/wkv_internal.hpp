@@ -1,0 +1,54 @@
+// wkv_internal.hpp -- launcher interface between the host dispatcher
+// (wkv_api.hip) and the kernel translation units.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wkv {
+
+struct FwdArgs {
+    int64_t B, T, C;
+    const float *w, *u, *k, *v;
+    float *y;
+    const float *s_in;
+    float *s_out;
+};
+
+struct StepArgs {
+    int64_t L, B, C;
+    const float *w, *u, *k, *v;
+    float *y;
+    const float *s_in;
+    float *s_out;
+};
+
+struct BwdArgs {
+    int64_t B, T, C;
+    const float *w, *u, *k, *v, *dy;
+    float *dk, *dv, *dw, *du;
+    void *ws;
+};
+
+// forward (wkv_forward.hip)
+hipError_t launch_forward_lane(const FwdArgs &a, hipStream_t st);
+bool forward_seg_supported(int nw, int ls);
+hipError_t launch_forward_seg(const FwdArgs &a, int nw, int ls, hipStream_t st);
+hipError_t launch_state_copy(int64_t lanes, const float *s_in, float *s_out, hipStream_t st);
+
+// forward with decoupled look-back (wkv_lookback.hip)
+bool forward_lookback_supported(int nw, int ls);
+int64_t lookback_tiles(int64_t B, int64_t T, int64_t C, int nw, int ls);
+size_t lookback_scratch_bytes(int64_t ntiles);
+hipError_t launch_forward_lookback(const FwdArgs &a, int nw, int ls, void *scratch,
+                                   hipStream_t st);
+
+// step (wkv_step.hip)
+hipError_t launch_step(const StepArgs &a, hipStream_t st);
+
+// backward (wkv_backward.hip)
+size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
+hipError_t launch_backward(const BwdArgs &a, hipStream_t st);
+
+}  // namespace wkv

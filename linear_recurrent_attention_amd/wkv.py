@@ -1,0 +1,191 @@
+"""Thin Python binding of libwkv (include/wkv.h): argument marshalling only.
+
+Every function here forwards to the C entry point of the same name, passing
+device pointers taken from torch tensors and the stream handle of the given
+(or current) torch stream.  No arithmetic of the operator happens in Python,
+and there is no fallback: if ``libwkv.so`` is not built, or a tensor is not a
+float32 tensor on a HIP device, the call raises.
+
+Layouts (C-contiguous, channel fastest):
+    w, u            [C]          (wkv_step: [L][C])
+    k, v, y, dy     [B][T][C]    (wkv_step: [L][B][C])
+    state           [3][B][C]    planes a, b, o   (wkv_step: [L][3][B][C])
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwkv.so")
+
+# wkv_status values
+WKV_OK = 0
+WKV_ERR_NULL = 1
+WKV_ERR_DIM = 2
+WKV_ERR_OVERFLOW = 3
+WKV_ERR_ALIAS = 4
+WKV_ERR_WORKSPACE = 5
+WKV_ERR_UNSUPPORTED = 6
+WKV_ERR_HIP = 7
+
+# wkv_kernel values
+WKV_KERNEL_AUTO = 0
+WKV_KERNEL_LANE = 1
+WKV_KERNEL_SEGMENTED = 2
+WKV_KERNEL_LOOKBACK = 3
+
+EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backward",
+            "wkv_status_string", "wkv_forward_ex", "wkv_forward_plan_auto")
+
+
+class WkvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({wkv_status_string(status)})")
+
+
+class ForwardPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("segments", ctypes.c_int32),
+                ("seg_len", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libwkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m linear_recurrent_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.wkv_forward.argtypes = [i64, i64, i64] + [vp] * 7 + [vp]
+    lib.wkv_forward.restype = ctypes.c_int
+    lib.wkv_forward_ex.argtypes = [i64, i64, i64] + [vp] * 7 + [ctypes.POINTER(ForwardPlan), vp]
+    lib.wkv_forward_ex.restype = ctypes.c_int
+    lib.wkv_forward_plan_auto.argtypes = [i64, i64, i64, ctypes.POINTER(ForwardPlan)]
+    lib.wkv_forward_plan_auto.restype = ctypes.c_int
+    lib.wkv_step.argtypes = [i64, i64, i64] + [vp] * 7 + [vp]
+    lib.wkv_step.restype = ctypes.c_int
+    lib.wkv_backward_workspace_size.argtypes = [i64, i64, i64]
+    lib.wkv_backward_workspace_size.restype = sz
+    lib.wkv_backward.argtypes = [i64, i64, i64] + [vp] * 9 + [vp, sz, vp]
+    lib.wkv_backward.restype = ctypes.c_int
+    lib.wkv_status_string.argtypes = [ctypes.c_int]
+    lib.wkv_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def wkv_status_string(status: int) -> str:
+    return load_library().wkv_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"expected float32, got {t.dtype}")
+    if t.numel() > 0 and not t.is_cuda:
+        raise TypeError("expected a tensor on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != WKV_OK:
+        raise WkvError(fn, status)
+
+
+def _bundle_shape(k, state, L=None):
+    if k.dim() != 3:
+        raise ValueError("k must be 3-D")
+    return tuple(int(x) for x in k.shape)
+
+
+def wkv_forward(w, u, k, v, y=None, state_in=None, state_out=None, stream=None, plan=None):
+    """GPT / RNN-chunk forward.  Returns (y, state_out).
+
+    ``state_out`` is written when given (it may be ``state_in`` itself for an
+    in-place update); pass ``state_out=True`` to have one allocated.  ``plan``
+    is an optional (kernel, segments, seg_len) triple for ``wkv_forward_ex``.
+    """
+    B, T, C = _bundle_shape(k, state_in)
+    if y is None:
+        y = torch.empty_like(k)
+    if state_out is True:
+        state_out = torch.empty((3, B, C), device=k.device, dtype=torch.float32)
+    lib = load_library()
+    args = [B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(state_in),
+            _ptr(state_out)]
+    if plan is None:
+        _check("wkv_forward", lib.wkv_forward(*args, _stream(stream)))
+    else:
+        p = ForwardPlan(*plan, 0) if len(plan) == 3 else ForwardPlan(*plan)
+        _check("wkv_forward_ex", lib.wkv_forward_ex(*args, ctypes.byref(p), _stream(stream)))
+    return y, state_out
+
+
+def wkv_forward_plan_auto(B: int, T: int, C: int):
+    p = ForwardPlan()
+    _check("wkv_forward_plan_auto", load_library().wkv_forward_plan_auto(B, T, C, ctypes.byref(p)))
+    return (p.kernel, p.segments, p.seg_len)
+
+
+def wkv_step(w, u, k, v, state_in, state_out=None, y=None, stream=None):
+    """Batched T=1 step over L layers.  k, v: [L][B][C]; state: [L][3][B][C].
+    ``state_out`` defaults to ``state_in`` (in-place).  Returns (y, state_out)."""
+    if k.dim() != 3:
+        raise ValueError("k must be [L][B][C]")
+    L, B, C = (int(x) for x in k.shape)
+    if y is None:
+        y = torch.empty_like(k)
+    if state_out is None:
+        state_out = state_in
+    st = load_library().wkv_step(L, B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                 _ptr(state_in), _ptr(state_out), _stream(stream))
+    _check("wkv_step", st)
+    return y, state_out
+
+
+def wkv_backward_workspace_size(B: int, T: int, C: int) -> int:
+    return int(load_library().wkv_backward_workspace_size(B, T, C))
+
+
+def wkv_backward(w, u, k, v, dy, dk=None, dv=None, dw=None, du=None, workspace=None,
+                 stream=None):
+    """Gradients (dk, dv, dw, du) of sum(dy * y) for the GPT-mode forward with the
+    empty initial state.  ``workspace`` is a uint8 device tensor of at least
+    ``wkv_backward_workspace_size(B, T, C)`` bytes (allocated when omitted)."""
+    B, T, C = _bundle_shape(k, None)
+    dev = k.device
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    dw = torch.empty(C, device=dev, dtype=torch.float32) if dw is None else dw
+    du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
+    need = wkv_backward_workspace_size(B, T, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
+    st = load_library().wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                                     _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), ws_ptr,
+                                     workspace.numel(), _stream(stream))
+    _check("wkv_backward", st)
+    return dk, dv, dw, du

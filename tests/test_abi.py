@@ -1,0 +1,147 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects invalid arguments with the documented status
+before touching the HIP runtime.  No call here reaches a kernel launch: every
+argument set is invalid, so the host checks return first."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wkv.h")
+LIB = os.path.join(ROOT, "linear_recurrent_attention_amd", "libwkv.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from linear_recurrent_attention_amd import build
+        build.build()
+    from linear_recurrent_attention_amd import wkv
+    return wkv.load_library(LIB)
+
+
+def declared_entry_points():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"WKV_API\s+[\w\s\*]*?\b(wkv_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_entry_points()
+    for n in ("wkv_forward", "wkv_step", "wkv_backward", "wkv_backward_workspace_size",
+              "wkv_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)$", out, flags=re.M))
+    for n in declared_entry_points():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+    from linear_recurrent_attention_amd import wkv
+    assert set(wkv.EXPORTED) == set(declared_entry_points())
+
+
+def test_status_strings(lib):
+    from linear_recurrent_attention_amd import wkv
+    seen = set()
+    for s in range(8):
+        txt = wkv.wkv_status_string(s)
+        assert txt and txt not in seen
+        seen.add(txt)
+    assert wkv.wkv_status_string(99) == "unknown status"
+
+
+# Fake, never dereferenced device addresses for the validation paths.
+P = 1 << 40
+
+
+def fwd(lib, B, T, C, w=P, u=P + 0x1000, k=P + 0x100000, v=P + 0x10000000, y=P + 0x20000000,
+        si=None, so=None):
+    vp = ctypes.c_void_p
+    return lib.wkv_forward(B, T, C, vp(w) if w else None, vp(u) if u else None,
+                           vp(k) if k else None, vp(v) if v else None, vp(y) if y else None,
+                           vp(si) if si else None, vp(so) if so else None, None)
+
+
+def test_forward_rejects_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    assert fwd(lib, -1, 4, 4) == W.WKV_ERR_DIM
+    assert fwd(lib, 4, -1, 4) == W.WKV_ERR_DIM
+    assert fwd(lib, 4, 4, -2) == W.WKV_ERR_DIM
+    assert fwd(lib, 1 << 30, 1 << 20, 1 << 20) == W.WKV_ERR_OVERFLOW
+    assert fwd(lib, 2, 8, 16, k=None) == W.WKV_ERR_NULL
+    assert fwd(lib, 2, 8, 16, y=None) == W.WKV_ERR_NULL
+    assert fwd(lib, 2, 8, 16, w=None) == W.WKV_ERR_NULL
+    # y overlapping k, v, w, a state buffer
+    assert fwd(lib, 2, 8, 16, y=P + 0x100000 + 64) == W.WKV_ERR_ALIAS
+    assert fwd(lib, 2, 8, 16, y=P + 0x10000000) == W.WKV_ERR_ALIAS
+    assert fwd(lib, 2, 8, 16, y=P - 16) == W.WKV_ERR_ALIAS
+    assert fwd(lib, 2, 8, 16, si=P + 0x20000000 + 8) == W.WKV_ERR_ALIAS
+    # state_out partially overlapping state_in, or overlapping an input
+    si = P + 0x30000000
+    assert fwd(lib, 2, 8, 16, si=si, so=si + 4) == W.WKV_ERR_ALIAS
+    assert fwd(lib, 2, 8, 16, so=P + 0x100000) == W.WKV_ERR_ALIAS
+
+
+def test_step_rejects_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    base = [vp(P), vp(P + 0x1000), vp(P + 0x100000), vp(P + 0x200000), vp(P + 0x300000)]
+    si, so = vp(P + 0x400000), vp(P + 0x400000)
+    assert lib.wkv_step(-1, 2, 4, *base, si, so, None) == W.WKV_ERR_DIM
+    assert lib.wkv_step(2, 2, 4, *base, None, so, None) == W.WKV_ERR_NULL
+    assert lib.wkv_step(2, 2, 4, *base, si, vp(P + 0x400000 + 4), None) == W.WKV_ERR_ALIAS
+    assert lib.wkv_step(2, 2, 4, *base[:4], vp(P + 0x100000), si, so, None) == W.WKV_ERR_ALIAS
+    assert lib.wkv_step(1 << 40, 1 << 20, 1 << 10, *base, si, so, None) == W.WKV_ERR_OVERFLOW
+
+
+def test_backward_workspace_and_checks(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    assert lib.wkv_backward_workspace_size(0, 10, 10) == 0
+    assert lib.wkv_backward_workspace_size(-1, 10, 10) == 0
+    need = lib.wkv_backward_workspace_size(8, 4096, 2048)
+    assert need > 2 * 8 * 2048 * 8
+    assert lib.wkv_backward_workspace_size(8, 4097, 2048) > need   # one more tile
+    vp = ctypes.c_void_p
+    ins = [vp(P + i * 0x10000000) for i in range(5)]           # w u k v dy
+    outs = [vp(P + (8 + i) * 0x10000000) for i in range(4)]    # dk dv dw du
+    ws = vp(P + 16 * 0x10000000)
+    n = lib.wkv_backward_workspace_size(2, 64, 32)
+    assert lib.wkv_backward(2, 64, 32, *ins, *outs, ws, n - 1, None) == W.WKV_ERR_WORKSPACE
+    assert lib.wkv_backward(2, 64, 32, *ins, *outs, None, n, None) == W.WKV_ERR_WORKSPACE
+    bad = list(outs)
+    bad[0] = ins[2]                                            # dk == k
+    assert lib.wkv_backward(2, 64, 32, *ins, *bad, ws, n, None) == W.WKV_ERR_ALIAS
+    bad = list(outs)
+    bad[3] = vp(P + 9 * 0x10000000 + 4)                        # du inside dv
+    assert lib.wkv_backward(2, 64, 32, *ins, *bad, ws, n, None) == W.WKV_ERR_ALIAS
+    assert lib.wkv_backward(2, 64, 32, *ins, *outs, outs[1], n, None) == W.WKV_ERR_ALIAS
+    assert lib.wkv_backward(-2, 64, 32, *ins, *outs, ws, n, None) == W.WKV_ERR_DIM
+    assert lib.wkv_backward(2, 64, 32, *ins[:4], None, *outs, ws, n, None) == W.WKV_ERR_NULL
+
+
+def test_forward_ex_rejects_unknown_plans(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    args = [2, 8, 16, vp(P), vp(P + 0x1000), vp(P + 0x100000), vp(P + 0x10000000),
+            vp(P + 0x20000000), None, None]
+    for plan in ((9, 0, 0, 0), (W.WKV_KERNEL_SEGMENTED, 3, 16, 0),
+                 (W.WKV_KERNEL_SEGMENTED, 16, 7, 0), (W.WKV_KERNEL_LANE, 0, 0, 1)):
+        p = W.ForwardPlan(*plan)
+        assert lib.wkv_forward_ex(*args, ctypes.byref(p), None) == W.WKV_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from linear_recurrent_attention_amd import wkv
+    with pytest.raises(RuntimeError, match="missing"):
+        wkv._lib_saved = wkv._lib
+        wkv._lib = None
+        try:
+            wkv.load_library(str(tmp_path / "libwkv.so"))
+        finally:
+            wkv._lib = wkv._lib_saved
