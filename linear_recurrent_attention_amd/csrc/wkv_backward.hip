@@ -51,7 +51,6 @@ struct Rev {
 };
 
 __device__ __forceinline__ Rev rev_empty() { return Rev{0.0f, 0.0f, 0.0f, 0.0f, kEmpty2, 0.0f}; }
-__device__ __forceinline__ float rev_rho(const Rev &z, float W) { return fmaf(-z.m, W, z.r0); }
 
 // Hysteresis of the reverse frame (log2 units): the frame moves only when a new
 // term exceeds it by more than 2^kRevHyst.  After a dominant token (k = +60,
@@ -66,8 +65,9 @@ constexpr float kRevHyst = 8.0f;
 // Fold output token i (gradient g, output y, lambda = log2 D_i) into the sums.
 __device__ __forceinline__ void rev_absorb(Rev &z, float g, float y, float lam, float W) {
     const float m1 = z.m + 1.0f;
-    const float old = fmaf(m1, -W, z.r0);  // frame of the sums, decayed one step
-    const float d = old + lam;             // old frame minus the new term's exponent -lam
+    // old frame (r0 - m1 W, the sums decayed one step) minus the new term's
+    // exponent -lam, anchors first
+    const float d = fmaf(-m1, W, z.r0 + lam);
     const bool keep_old = d > -kRevHyst;
     const float E = ex2(keep_old ? -d : d);
     const float fo = keep_old ? 1.0f : E;
@@ -87,9 +87,11 @@ __device__ __forceinline__ void rev_absorb(Rev &z, float g, float y, float lam, 
 // step count.
 __device__ __forceinline__ void rev_compose(Rev &e, const Rev &l, float W, float len) {
     const float lm = l.m + len;
-    const float ld = fmaf(-lm, W, l.r0);
-    const float d = ld - rev_rho(e, W);
-    const bool late_big = d > kRevHyst;  // same hysteresis as rev_absorb
+    // frame of l moved across the stretch minus the frame of e, anchors first
+    const float d = fmaf(-(lm - e.m), W, l.r0 - e.r0);
+    // keep the later part's frame unless it is smaller by more than the margin:
+    // the later part is the long carried sum, which is then never rescaled
+    const bool late_big = d > -kRevHyst;
     const float E = ex2(late_big ? -d : d);
     const float fe = late_big ? E : 1.0f;
     const float fl = late_big ? 1.0f : E;
@@ -157,8 +159,7 @@ __device__ __forceinline__ void fwd_token(Lane &L, float K, float v, const Chan 
                                           float &lam, float &pii) {
     const float o = lane_o(L, ch.W);  // frame of the past sums before this token
     const float n1 = L.n + 1.0f;
-    const float h = fmaf(n1, -ch.W, L.e0);
-    const float s = K - h;
+    const float s = fmaf(n1, ch.W, K - L.e0);
     const float E = ex2(-fabsf(s));
     const bool pos = s > 0.0f;
     const float P = pos ? E : 1.0f;
@@ -172,7 +173,7 @@ __device__ __forceinline__ void fwd_token(Lane &L, float K, float v, const Chan 
         // D = 2^{o} (b + c1 2^s) = 2^{max(h, K) + W} den
         lam = (pos ? K + ch.W : o) + lg2(den);
     } else {
-        const float x = (ch.U + K) - o;
+        const float x = fmaf(L.n, ch.W, (ch.U + K) - L.e0);
         const float F = ex2(-fabsf(x));
         const bool px = x > 0.0f;
         const float Pp = px ? F : 1.0f, Qq = px ? 1.0f : F;
@@ -312,7 +313,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             if (t0 + j < T) {
                 const float K = Kc[j] * kLog2e;
                 const float v = Vc[j], g = Gc[j], y = Y[j];
-                const float ek = ex2(K + rev_rho(suf, ch.W));
+                const float ek = ex2(fmaf(-suf.m, ch.W, K + suf.r0));
                 const float own = PII[j] * g;
                 const float vy = v - y;
                 if (active) {

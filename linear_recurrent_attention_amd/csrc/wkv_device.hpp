@@ -57,7 +57,10 @@ __device__ __forceinline__ bool chan_fast_ok(const Chan &ch) {
 // token after token (as a direct transcription of the log-space recurrence
 // would) accumulates a systematic rounding bias of up to half an ulp of f per
 // token, which at |f| ~ 90 and small W reaches percent-level errors in the
-// weights after a few thousand tokens.
+// weights after a few thousand tokens.  Differences of two frames are formed
+// as (anchor - anchor) - (steps - steps) W: close anchors subtract exactly, so a
+// rescale factor 2^d is as accurate as d itself rather than off by an ulp of
+// |f| (~8e-6 at |f| ~ 90).
 struct Lane {
     float a, b;  // scaled numerator and denominator
     float e0;    // anchor exponent (log2 units)
@@ -83,8 +86,7 @@ __device__ __forceinline__ float lane_o(const Lane &L, float W) { return fmaf(-L
 // float with margin, i.e. |U - W| <= kFastLimit2.
 __device__ __forceinline__ float step_fast(Lane &L, float K, float v, const Chan &ch) {
     const float n1 = L.n + 1.0f;
-    const float h = fmaf(n1, -ch.W, L.e0);
-    const float s = K - h;
+    const float s = fmaf(n1, ch.W, K - L.e0);  // K - h, anchor difference first
     const float E = ex2(-fabsf(s));
     const bool pos = s > 0.0f;
     const float P = pos ? E : 1.0f;
@@ -103,16 +105,14 @@ __device__ __forceinline__ float step_fast(Lane &L, float K, float v, const Chan
 // The same token with the output normalised on its own maximum (two
 // exponentials); valid for any finite u, w.
 __device__ __forceinline__ float step_safe(Lane &L, float K, float v, const Chan &ch) {
-    const float o = lane_o(L, ch.W);
-    const float x = (ch.U + K) - o;
+    const float x = fmaf(L.n, ch.W, (ch.U + K) - L.e0);  // (U + K) - frame
     const float F = ex2(-fabsf(x));
     const bool px = x > 0.0f;
     const float Pp = px ? F : 1.0f;
     const float Qq = px ? 1.0f : F;
     const float y = fmaf(Qq, v, L.a * Pp) * rcp(fmaf(L.b, Pp, Qq));
     const float n1 = L.n + 1.0f;
-    const float h = fmaf(n1, -ch.W, L.e0);
-    const float s = K - h;
+    const float s = fmaf(n1, ch.W, K - L.e0);
     const float E = ex2(-fabsf(s));
     const bool pos = s > 0.0f;
     const float P = pos ? E : 1.0f;
@@ -135,8 +135,7 @@ __device__ __forceinline__ float step(Lane &L, float K, float v, const Chan &ch)
 // Fold a token into the state without producing an output (segment summaries).
 __device__ __forceinline__ void absorb(Lane &L, float K, float v, const Chan &ch) {
     const float n1 = L.n + 1.0f;
-    const float h = fmaf(n1, -ch.W, L.e0);
-    const float s = K - h;
+    const float s = fmaf(n1, ch.W, K - L.e0);
     const float E = ex2(-fabsf(s));
     const bool pos = s > 0.0f;
     const float P = pos ? E : 1.0f;
@@ -155,9 +154,8 @@ __device__ __forceinline__ void absorb(Lane &L, float K, float v, const Chan &ch
 // sequence) do not drift.  Empty operands are identities.
 __device__ __forceinline__ void compose(Lane &X, const Lane &Y, float W, float len) {
     const float nxl = X.n + len;
-    const float fx = fmaf(-nxl, W, X.e0);
-    const float fy = fmaf(-Y.n, W, Y.e0);
-    const float d = fx - fy;
+    // (X.e0 - nxl W) - (Y.e0 - Y.n W), anchors first: exact when they are close
+    const float d = fmaf(-(nxl - Y.n), W, X.e0 - Y.e0);
     const float E = ex2(-fabsf(d));
     const bool xbig = d > 0.0f;
     const float P = xbig ? 1.0f : E;
