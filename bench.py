@@ -195,14 +195,16 @@ def bench_gpt(args, torch, wkv, synth):
 
 
 def kernel_name(plan, wkv) -> str:
-    kernel, nw, ls = plan
+    """Kernel symbol (template arguments as in the profiler's kernel names)."""
+    kernel, nw, ls = plan[:3]
+    cw = plan[3] if len(plan) > 3 and plan[3] else 64
     if kernel == wkv.WKV_KERNEL_LANE:
         return "fwd_lane_kernel"
     if kernel == wkv.WKV_KERNEL_SEGMENTED:
-        return f"fwd_seg_kernel<{nw},{ls}>"
+        return f"fwd_seg_kernel<{nw * cw // 64}, {ls}, {cw}>"
     if kernel == wkv.WKV_KERNEL_LOOKBACK:
-        return f"fwd_lookback_kernel<{nw},{ls}>"
-    return f"kernel{kernel}<{nw},{ls}>"
+        return f"fwd_lookback_kernel<{cw // 64}, {nw}, {ls}>"
+    return f"kernel{kernel}<{nw}, {ls}>"
 
 
 def bench_stream(args, torch, wkv, synth):
@@ -383,9 +385,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt",
                     choices=["gpt", "stream", "decode", "stability_fwd", "stability_bwd", "copy"])
-    ap.add_argument("--plan", type=int, nargs=3, default=None,
-                    metavar=("KERNEL", "SEGMENTS", "SEG_LEN"),
-                    help="force a forward kernel (wkv_forward_ex plan)")
+    ap.add_argument("--plan", type=int, nargs="+", default=None,
+                    metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
+                    "(wkv_forward_ex plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()

@@ -161,15 +161,16 @@ WKV_API const char *wkv_status_string(wkv_status s);
  * Forward with an explicit kernel choice, for testing every kernel on every
  * shape and for tuning.  Same arguments, semantics and errors as wkv_forward;
  * `plan` NULL or plan->kernel == WKV_KERNEL_AUTO behaves exactly like
- * wkv_forward.  A plan whose (kernel, segments, seg_len) is not among the
- * compiled variants returns WKV_ERR_UNSUPPORTED.
+ * wkv_forward.  A plan that names no compiled variant returns
+ * WKV_ERR_UNSUPPORTED.
  *   WKV_KERNEL_LANE        one thread per lane, sequential over T
- *   WKV_KERNEL_SEGMENTED   one workgroup per (sequence, 64 channels) owns the
- *                          whole sequence; `segments` waves each sweep seg_len
- *                          tokens of every tile of segments*seg_len tokens,
- *                          composing segment states with decay e^{-w len}
- *   WKV_KERNEL_LOOKBACK    workgroups own (64 channels, block of
- *                          segments*seg_len tokens) and chain block states by a
+ *   WKV_KERNEL_SEGMENTED   one workgroup per (sequence, `channels` channels)
+ *                          owns the whole sequence, in tiles of
+ *                          segments * seg_len tokens: each segment of seg_len
+ *                          tokens is swept by one row of lanes, and segment
+ *                          states are composed with the decay e^{-w len}
+ *   WKV_KERNEL_LOOKBACK    workgroups own (`channels` channels, block of
+ *                          segments * seg_len tokens) and chain block states by a
  *                          decoupled look-back over earlier blocks
  */
 typedef enum wkv_kernel {
@@ -181,9 +182,10 @@ typedef enum wkv_kernel {
 
 typedef struct wkv_forward_plan {
     int32_t kernel;    /* wkv_kernel */
-    int32_t segments;  /* waves per workgroup (SEGMENTED, LOOKBACK); 0 = default */
-    int32_t seg_len;   /* tokens per wave per tile (SEGMENTED, LOOKBACK); 0 = default */
-    int32_t reserved;  /* must be 0 */
+    int32_t segments;  /* segments per tile (SEGMENTED) or block (LOOKBACK); 0 = default */
+    int32_t seg_len;   /* tokens per segment (SEGMENTED, LOOKBACK); 0 = default */
+    int32_t channels;  /* channels per workgroup: SEGMENTED 64, 32 or 16; LOOKBACK 64,
+                          128 or 256; 0 = 64 */
 } wkv_forward_plan;
 
 WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *w, const float *u,

@@ -68,14 +68,19 @@ int device_cus() {
 // Scratch of the look-back forward, one buffer per (device, stream) so that
 // calls on different streams never share it.  Allocated and zeroed on first
 // use, grown (after draining the stream) when a larger shape needs more, and
-// kept until the process ends.
+// kept until the process ends.  Every launch gets a fresh epoch, which tags
+// the states it publishes; the epoch advances only when a launch was
+// accepted, under the same lock as the launch itself, so launches from several
+// host threads onto one stream stay consistent.
 struct Scratch {
     void *p = nullptr;
     size_t bytes = 0;
+    uint32_t epoch = 1;
 };
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
-hipError_t stream_scratch(hipStream_t st, size_t need, void **out) {
+hipError_t launch_with_scratch(const FwdArgs &a, int cg, int ns, int ls, size_t need,
+                               hipStream_t st) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -94,26 +99,40 @@ hipError_t stream_scratch(hipStream_t st, size_t need, void **out) {
         if ((e = hipMemsetAsync(s.p, 0, bytes, st)) != hipSuccess) return e;
         s.bytes = bytes;
     }
-    *out = s.p;
-    return hipSuccess;
+    const wkv::LookbackScratch sc{s.p, s.epoch};
+    e = wkv::launch_forward_lookback(a, cg, ns, ls, sc, st);
+    if (e == hipSuccess) {
+        s.epoch = (s.epoch + 1) & 0x3fffffffu;
+        if (s.epoch == 0) s.epoch = 1;
+    }
+    return e;
 }
 
 // Largest look-back scratch a call may ask for; longer sequences use the
 // segmented kernel, which needs none.
 constexpr size_t kLookbackScratchMax = (size_t)256 << 20;
 
-// The plan for a shape.  Pure host arithmetic, given the compute-unit count.
+// The plan for a shape.  Pure host arithmetic, given the compute-unit count;
+// thresholds from timings on MI355X (256 CUs):
+//   - very short sequences, or short ones with many lanes: the lane kernel
+//     (one thread per lane, no scan);
+//   - very many lanes: the segmented kernel (one workgroup per 64 lanes walks
+//     the whole sequence; enough workgroups to fill the chip);
+//   - otherwise the look-back kernel, whose workgroups split the sequence as
+//     well: blocks of 4 x 32 tokens when that still gives about eight
+//     workgroups per CU, else 4 x 16 for more parallelism.
 wkv_forward_plan auto_plan(int64_t B, int64_t T, int64_t C, int cus) {
-    wkv_forward_plan p{WKV_KERNEL_LANE, 0, 0, 0};
     const int64_t lanes = B * C;
-    // one wave of 64 lanes per SIMD on every CU, four deep, keeps the lane
-    // kernel fed on its own; below that the sequence is split into segments
-    const int64_t lane_kernel_min = (int64_t)cus * 4 * 4 * 64;
-    if (lanes >= lane_kernel_min || T <= 16) return p;
-    p.kernel = WKV_KERNEL_SEGMENTED;
-    p.segments = 16;
-    p.seg_len = 16;
-    return p;
+    const int64_t groups = B * ((C + 63) / 64);
+    if (T <= 16 || (lanes >= (int64_t)cus * 512 && T <= 128))
+        return wkv_forward_plan{WKV_KERNEL_LANE, 0, 0, 0};
+    const wkv_forward_plan seg{WKV_KERNEL_SEGMENTED, 16, 16, 64};
+    if (lanes >= (int64_t)cus * 1024) return seg;
+    const int ls = groups * ((T + 127) / 128) >= (int64_t)cus * 8 ? 32 : 16;
+    if (!wkv::lookback_grid_ok(B, T, C, 1, 4, ls) ||
+        wkv::lookback_scratch_bytes(B, T, C, 4, ls) > kLookbackScratchMax)
+        return seg;
+    return wkv_forward_plan{WKV_KERNEL_LOOKBACK, 4, ls, 64};
 }
 
 wkv_status check_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -173,20 +192,25 @@ WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *
     if (st != WKV_OK) return st;
     wkv_forward_plan p{WKV_KERNEL_AUTO, 0, 0, 0};
     if (plan) p = *plan;
-    if (p.reserved != 0) return WKV_ERR_UNSUPPORTED;
     switch (p.kernel) {
         case WKV_KERNEL_AUTO:
         case WKV_KERNEL_LANE:
+            if (p.channels != 0) return WKV_ERR_UNSUPPORTED;
             break;
         case WKV_KERNEL_SEGMENTED:
             if (p.segments == 0) p.segments = 16;
             if (p.seg_len == 0) p.seg_len = 16;
-            if (!wkv::forward_seg_supported(p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
+            if (p.channels == 0) p.channels = 64;
+            if (!wkv::forward_seg_supported(p.segments, p.seg_len, p.channels))
+                return WKV_ERR_UNSUPPORTED;
             break;
         case WKV_KERNEL_LOOKBACK:
             if (p.segments == 0) p.segments = 4;
             if (p.seg_len == 0) p.seg_len = 16;
-            if (!wkv::forward_lookback_supported(p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
+            if (p.channels == 0) p.channels = 64;
+            if (p.channels % 64 != 0 ||
+                !wkv::forward_lookback_supported(p.channels / 64, p.segments, p.seg_len))
+                return WKV_ERR_UNSUPPORTED;
             break;
         default:
             return WKV_ERR_UNSUPPORTED;
@@ -204,17 +228,14 @@ WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *
         return from_hip(wkv::launch_forward_lane(a, stream));
     }
     if (p.kernel == WKV_KERNEL_LOOKBACK) {
-        const int64_t ntiles = wkv::lookback_tiles(B, T, C, p.segments, p.seg_len);
-        if (ntiles > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
-        const size_t need = wkv::lookback_scratch_bytes(ntiles);
+        const int cg = p.channels / 64;
+        if (!wkv::lookback_grid_ok(B, T, C, cg, p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
+        const size_t need = wkv::lookback_scratch_bytes(B, T, C, p.segments, p.seg_len);
         if (need > kLookbackScratchMax) return WKV_ERR_UNSUPPORTED;
-        void *scratch = nullptr;
-        const hipError_t e = stream_scratch(stream, need, &scratch);
-        if (e != hipSuccess) return WKV_ERR_HIP;
-        return from_hip(wkv::launch_forward_lookback(a, p.segments, p.seg_len, scratch, stream));
+        return from_hip(launch_with_scratch(a, cg, p.segments, p.seg_len, need, stream));
     }
-    if (B * ((C + 63) / 64) > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
-    return from_hip(wkv::launch_forward_seg(a, p.segments, p.seg_len, stream));
+    if (B * ((C + p.channels - 1) / p.channels) > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
+    return from_hip(wkv::launch_forward_seg(a, p.segments, p.seg_len, p.channels, stream));
 }
 
 WKV_API wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,

@@ -166,12 +166,61 @@ __device__ __forceinline__ void compose(Lane &X, const Lane &Y, float W, float l
     X.n = xbig ? nxl : Y.n;
 }
 
+// Sweep of one whole segment in a single frame.  R is the state before the
+// segment and S the segment's own summary (its tokens absorbed from the empty
+// state), so S's anchor is the token whose decayed exponent is the largest of
+// the segment at its last token.  Measured at the segment's last token, every
+// term's weight is fixed: token t's is x_t = K_t - (L-1-t) W, the bonus term of
+// token t is c1 2^{x_t}, and R's is its frame G = R.e0 - (R.n + L) W.  (For
+// the output at token t, everything present is scaled by the same 2^{-(L-t) W}
+// relative to its own time, which cancels in the ratio.)  With F the larger of
+// G and max x_t as the frame, y_t = (A + c1 E_t v_t) / (B + c1 E_t), E_t =
+// 2^{x_t - F} <= 1, and A, B accumulate E_t v_t, E_t: one exponential and one
+// reciprocal per token, no rescaling.  Exponent differences are formed anchor
+// first as in step_fast.
+//
+// Valid when no term that is the largest present at its own time sits more
+// than 100 below F (else it could underflow): the present maximum only grows,
+// so it suffices that max(G, x_0) >= F - 100.  seg_frame() returns whether
+// that holds for this lane.
+struct SegFrame {
+    float Ae, An;       // anchor of F: F = Ae - An W
+    float alpha, beta;  // R's sums in frame F
+};
+
+__device__ __forceinline__ bool seg_frame(const Lane &R, const Lane &S, float W, float len,
+                                          float K0, SegFrame &f) {
+    const float nR = R.n + len;
+    const float D = fmaf(-(nR - S.n), W, R.e0 - S.e0);  // G - max x_t
+    const bool g = D >= 0.0f;
+    f.Ae = g ? R.e0 : S.e0;
+    f.An = g ? nR : S.n;
+    const float sc = g ? 1.0f : ex2(D);
+    f.alpha = R.a * sc;
+    f.beta = R.b * sc;
+    const float d0 = fmaf(f.An - (len - 1.0f), W, K0 - f.Ae);  // x_0 - F
+    return fmaxf(D, d0) >= -100.0f;
+}
+
+// Token t (0-based within the segment of `len` tokens) in the frame of f.
+__device__ __forceinline__ float frame_token(float &A, float &Bs, const SegFrame &f, float K,
+                                             float v, float t_from_end, const Chan &ch) {
+    const float E = ex2(fmaf(f.An - t_from_end, ch.W, K - f.Ae));
+    const float Ec = E * ch.c1;
+    const float y = fmaf(Ec, v, A) * rcp(Bs + Ec);
+    A = fmaf(E, v, A);
+    Bs += E;
+    return y;
+}
+
 // Consecutive rows of a row-major [rows][C] float tensor, seen by one wave.
 // `base` must be wave-uniform (it becomes a buffer descriptor in scalar
-// registers); `voff` is the lane's byte offset inside a row and `rowb` = 4*C
-// the row pitch.  Row j is addressed by the scalar offset j*rowb, so an access
-// is a single buffer instruction with one 32-bit vector offset.  Offsets stay
-// below 2^32 bytes from `base`.
+// registers); `voff` is the lane's byte offset from `base` (its channel, plus a
+// whole number of rows when the lanes of a wave cover several row ranges) and
+// `rowb` = 4*C the row pitch.  Row j is addressed by the scalar offset j*rowb,
+// so an access is a single buffer instruction with one 32-bit vector offset.
+// Offsets stay below 2^32 bytes from `base`.  Accesses carry the non-temporal
+// hint: every k, v and y element is touched once.
 struct TileRows {
     __amdgpu_buffer_rsrc_t r;
     uint32_t voff;
@@ -184,16 +233,18 @@ struct TileRows {
     // never convert.
     __device__ __forceinline__ float ld(int j) const {
         return __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, (uint32_t)j * rowb, 0));
+            float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, (uint32_t)j * rowb, kNT));
     }
     __device__ __forceinline__ void st(int j, float x) const {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff,
-                                              (uint32_t)j * rowb, 0);
+                                              (uint32_t)j * rowb, kNT);
     }
 
     // Buffer descriptor word 3 for gfx9-family raw 32-bit accesses
     // (DATA_FORMAT = 32 bits).
     static constexpr int kBufferWord3 = 0x00020000;
+    // Cache-policy operand: non-temporal.
+    static constexpr int kNT = 2;
 };
 
 // ABI state (natural-log exponent) -> kernel exponent (log2), mapping -inf and

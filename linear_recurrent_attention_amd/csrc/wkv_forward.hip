@@ -80,27 +80,34 @@ __global__ __launch_bounds__(256) void fwd_lane_kernel(int64_t B, int64_t T, int
 }
 
 // ---------------------------------------------------------------------------
-// Segmented two-pass scan, one workgroup per (b, 64 channels).
+// Segmented two-pass scan, one workgroup per (b, CW channels).
+//
+// A wave's 64 lanes are SPW = 64/CW segments of CW channels (lane = subsegment
+// * CW + channel), and the NW waves hold NSEG = NW*SPW consecutive segments of
+// LS tokens: a tile of NSEG*LS tokens.  With lane index l in wave w, the LDS
+// slot of (segment, channel) is simply w*64 + l, and segment s - d sits d*CW
+// slots below.  CW = 64 reads one 256-byte row per wave instruction; CW = 32
+// reads two 128-byte row pieces and gives twice as many workgroups, which lets
+// several workgroups share a CU and overlap each other's phases when B*C is
+// small.
 // ---------------------------------------------------------------------------
-template <int NW, int LS>
+template <int NW>
 struct SegShared {
-    float v[2][4][NW][64];  // ping-pong buffers of segment summaries (a, b, e0, n)
+    float v[2][4][NW * 64];  // ping-pong buffers of segment summaries (a, b, e0, n)
 
-    __device__ __forceinline__ void put(int buf, int s, int lane, const Lane &L) {
-        v[buf][0][s][lane] = L.a;
-        v[buf][1][s][lane] = L.b;
-        v[buf][2][s][lane] = L.e0;
-        v[buf][3][s][lane] = L.n;
+    __device__ __forceinline__ void put(int buf, int slot, const Lane &L) {
+        v[buf][0][slot] = L.a;
+        v[buf][1][slot] = L.b;
+        v[buf][2][slot] = L.e0;
+        v[buf][3][slot] = L.n;
     }
-    __device__ __forceinline__ Lane get(int buf, int s, int lane) const {
-        return Lane{v[buf][0][s][lane], v[buf][1][s][lane], v[buf][2][s][lane], v[buf][3][s][lane]};
+    __device__ __forceinline__ Lane get(int buf, int slot) const {
+        return Lane{v[buf][0][slot], v[buf][1][slot], v[buf][2][slot], v[buf][3][slot]};
     }
 };
 
-// This wave's LS tokens of one tile: rows t0..t0+LS-1 of a [T][C] sequence,
-// seen through a wave-uniform buffer descriptor based at row t0.  Row j is at
-// the scalar offset j*C*4 and the lane's channel at the vector offset, so a
-// load is one buffer_load_dword with no per-lane 64-bit address.
+// This lane's LS tokens of one tile, rows t0.. of its segment (rows past the end
+// of the sequence are not read and hold 0).
 template <int LS, bool FULL>
 __device__ __forceinline__ void seg_load(float (&K)[LS], float (&V)[LS], const TileRows &kr,
                                          const TileRows &vr, int64_t t0, int64_t T) {
@@ -113,27 +120,114 @@ __device__ __forceinline__ void seg_load(float (&K)[LS], float (&V)[LS], const T
     } else {
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
-            // wave-uniform condition: rows past the end are never read
             K[j] = (t0 + j < T) ? kr.ld(j) : 0.0f;
             V[j] = (t0 + j < T) ? vr.ld(j) : 0.0f;
         }
     }
 }
 
-// FULL: T is a whole number of tiles, so no token test is needed anywhere (the
-// loop body is straight-line code and the next tile's loads stay ahead of the
-// current tile's arithmetic); otherwise the last tile is ragged.
-template <int NW, int LS, bool SAFE, bool FULL>
+// Per-lane geometry of the segmented kernel.
+template <int NW, int LS, int CW>
+struct SegGeom {
+    static constexpr int SPW = 64 / CW;      // segments per wave
+    static constexpr int NSEG = NW * SPW;    // segments per tile
+    static constexpr int TT = NSEG * LS;     // tokens per tile
+    int lane;     // 0..63
+    int wave;     // wave-uniform
+    int seg;      // this lane's segment within the tile
+    int slot;     // LDS slot: wave * 64 + lane
+};
+
+// One tile: this lane's LS tokens of k, v are in registers (K, V); `carry` is
+// the state before the tile and leaves as the state after it.  FULL: T is a
+// whole number of tiles, so no token test is needed (straight-line code).
+template <int NW, int LS, int CW, bool SAFE, bool FULL>
+__device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], const float (&V)[LS],
+                                         Lane &carry, const SegGeom<NW, LS, CW> &G, int64_t B,
+                                         int64_t T, int64_t C, int64_t bb, int64_t c, bool active,
+                                         const Chan &ch, float *yseq, uint32_t voff,
+                                         float *__restrict__ s_out, SegShared<NW> &sh) {
+    using Geo = SegGeom<NW, LS, CW>;
+    const int64_t t0 = tile * Geo::TT + (int64_t)G.seg * LS;
+
+    // (1) summary of this segment from the empty state
+    Lane S = lane_empty();
+    if (FULL || t0 + LS <= T) {
+#pragma unroll
+        for (int j = 0; j < LS; ++j) absorb(S, K[j] * kLog2e, V[j], ch);
+    } else {
+#pragma unroll
+        for (int j = 0; j < LS; ++j)
+            if (t0 + j < T) absorb(S, K[j] * kLog2e, V[j], ch);
+    }
+
+    // (2) inclusive scan over the NSEG segments of the tile (Hillis-Steele,
+    // ping-pong LDS buffers: one barrier per round)
+    int buf = 0;
+#pragma unroll
+    for (int d = 1; d < Geo::NSEG; d <<= 1) {
+        sh.put(buf, G.slot, S);
+        __syncthreads();
+        if (G.seg >= d) {
+            Lane X = sh.get(buf, G.slot - d * CW);
+            compose(X, S, ch.W, (float)(d * LS));
+            S = X;
+        }
+        buf ^= 1;
+    }
+    sh.put(buf, G.slot, S);
+    __syncthreads();
+    // state at the start of this segment: carry, then segments 0..seg-1
+    Lane R = carry;
+    if (G.seg > 0) compose(R, sh.get(buf, G.slot - CW), ch.W, (float)(G.seg * LS));
+    // carry for the next tile: carry, then the whole tile
+    compose(carry, sh.get(buf, (Geo::NSEG - 1) * CW + (G.lane % CW)), ch.W, (float)Geo::TT);
+
+    // (3) re-sweep from the prefix state, emitting y
+    const int64_t tw = tile * Geo::TT + (int64_t)G.wave * Geo::SPW * LS;  // wave's first row
+    const TileRows yr(yseq + tw * C, voff, (uint32_t)(C * 4));
+    if (FULL || t0 + LS <= T) {
+#pragma unroll
+        for (int j = 0; j < LS; ++j) {
+            const float yv = step<SAFE>(R, K[j] * kLog2e, V[j], ch);
+            if (active) yr.st(j, yv);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < LS; ++j)
+            if (t0 + j < T) {
+                const float yv = step<SAFE>(R, K[j] * kLog2e, V[j], ch);
+                if (active) yr.st(j, yv);
+            }
+    }
+    // the lane holding token T-1 writes the final state
+    if (s_out && active && t0 <= T - 1 && T - 1 < t0 + LS) {
+        s_out[(0 * B + bb) * C + c] = R.a;
+        s_out[(1 * B + bb) * C + c] = R.b;
+        s_out[(2 * B + bb) * C + c] = o_out(lane_o(R, ch.W));
+    }
+}
+
+// The whole sequence of one (b, CW-channel group): tiles in order, with the
+// next tile's k, v loaded while the current one is processed.  Two register
+// sets take turns (A holds even tiles, B odd ones) so that no register copy
+// ties a prefetch to the current tile's arithmetic.
+template <int NW, int LS, int CW, bool SAFE, bool FULL>
 __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_t bb, int64_t c,
-                                         bool active, const Chan &ch, const float *kseq,
+                                         bool active, const Chan &ch,
+                                         const SegGeom<NW, LS, CW> &G, const float *kseq,
                                          const float *vseq, float *yseq, uint32_t voff,
                                          const float *__restrict__ s_in, float *__restrict__ s_out,
-                                         SegShared<NW, LS> &sh) {
-    constexpr int TT = NW * LS;
-    const int lane = threadIdx.x & 63;
-    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // segment = wave
-    const int64_t ntiles = (T + TT - 1) / TT;
+                                         SegShared<NW> &sh) {
+    using Geo = SegGeom<NW, LS, CW>;
+    const int64_t ntiles = (T + Geo::TT - 1) / Geo::TT;
     const uint32_t rowb = (uint32_t)(C * 4);
+    auto load = [&](float (&K)[LS], float (&V)[LS], int64_t tile) {
+        const int64_t tw = tile * Geo::TT + (int64_t)G.wave * Geo::SPW * LS;
+        seg_load<LS, FULL>(K, V, TileRows(kseq + tw * C, voff, rowb),
+                           TileRows(vseq + tw * C, voff, rowb),
+                           tile * Geo::TT + (int64_t)G.seg * LS, T);
+    };
 
     // carry: the state before the current tile
     Lane carry = lane_empty();
@@ -141,84 +235,23 @@ __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_
         carry = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
                         o_in(s_in[(2 * B + bb) * C + c]));
 
-    float Kc[LS], Vc[LS];
-    {
-        const int64_t t0 = (int64_t)s * LS;
-        seg_load<LS, FULL>(Kc, Vc, TileRows(kseq + t0 * C, voff, rowb),
-                           TileRows(vseq + t0 * C, voff, rowb), t0, T);
+    float KA[LS], VA[LS], KB[LS], VB[LS];
+    load(KA, VA, 0);
+    int64_t tile = 0;
+    for (; tile + 1 < ntiles; tile += 2) {
+        load(KB, VB, tile + 1);
+        seg_tile<NW, LS, CW, SAFE, FULL>(tile, KA, VA, carry, G, B, T, C, bb, c, active, ch, yseq,
+                                         voff, s_out, sh);
+        if (tile + 2 < ntiles) load(KA, VA, tile + 2);
+        seg_tile<NW, LS, CW, SAFE, FULL>(tile + 1, KB, VB, carry, G, B, T, C, bb, c, active, ch,
+                                         yseq, voff, s_out, sh);
     }
-
-    for (int64_t tile = 0; tile < ntiles; ++tile) {
-        const int64_t t0 = tile * TT + (int64_t)s * LS;
-        float Kn[LS], Vn[LS];
-        if (tile + 1 < ntiles)
-            seg_load<LS, FULL>(Kn, Vn, TileRows(kseq + (t0 + TT) * C, voff, rowb),
-                               TileRows(vseq + (t0 + TT) * C, voff, rowb), t0 + TT, T);
-
-        // (1) summary of this segment from the empty state
-        Lane S = lane_empty();
-        if (FULL || t0 + LS <= T) {
-#pragma unroll
-            for (int j = 0; j < LS; ++j) absorb(S, Kc[j] * kLog2e, Vc[j], ch);
-        } else {
-#pragma unroll
-            for (int j = 0; j < LS; ++j)
-                if (t0 + j < T) absorb(S, Kc[j] * kLog2e, Vc[j], ch);
-        }
-
-        // (2) inclusive scan over the NW segments of the tile (Hillis-Steele,
-        // ping-pong LDS buffers: one barrier per round)
-        int buf = 0;
-#pragma unroll
-        for (int d = 1; d < NW; d <<= 1) {
-            sh.put(buf, s, lane, S);
-            __syncthreads();
-            if (s >= d) {
-                Lane X = sh.get(buf, s - d, lane);
-                compose(X, S, ch.W, (float)(d * LS));
-                S = X;
-            }
-            buf ^= 1;
-        }
-        sh.put(buf, s, lane, S);
-        __syncthreads();
-        // state at the start of this segment: carry, then segments 0..s-1
-        Lane R = carry;
-        if (s > 0) compose(R, sh.get(buf, s - 1, lane), ch.W, (float)(s * LS));
-        // carry for the next tile: carry, then the whole tile
-        compose(carry, sh.get(buf, NW - 1, lane), ch.W, (float)TT);
-
-        // (3) re-sweep from the prefix state, emitting y
-        const TileRows yr(yseq + t0 * C, voff, rowb);
-        if (FULL || t0 + LS <= T) {
-#pragma unroll
-            for (int j = 0; j < LS; ++j) {
-                const float yv = step<SAFE>(R, Kc[j] * kLog2e, Vc[j], ch);
-                if (active) yr.st(j, yv);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < LS; ++j)
-                if (t0 + j < T) {
-                    const float yv = step<SAFE>(R, Kc[j] * kLog2e, Vc[j], ch);
-                    if (active) yr.st(j, yv);
-                }
-        }
-        // the wave holding token T-1 writes the final state
-        if (s_out && active && t0 <= T - 1 && T - 1 < t0 + LS) {
-            s_out[(0 * B + bb) * C + c] = R.a;
-            s_out[(1 * B + bb) * C + c] = R.b;
-            s_out[(2 * B + bb) * C + c] = o_out(lane_o(R, ch.W));
-        }
-#pragma unroll
-        for (int j = 0; j < LS; ++j) {
-            Kc[j] = Kn[j];
-            Vc[j] = Vn[j];
-        }
-    }
+    if (tile < ntiles)
+        seg_tile<NW, LS, CW, SAFE, FULL>(tile, KA, VA, carry, G, B, T, C, bb, c, active, ch, yseq,
+                                         voff, s_out, sh);
 }
 
-template <int NW, int LS>
+template <int NW, int LS, int CW>
 __global__ __launch_bounds__(NW * 64) void fwd_seg_kernel(int64_t B, int64_t T, int64_t C,
                                                           const float *__restrict__ w,
                                                           const float *__restrict__ u,
@@ -227,33 +260,41 @@ __global__ __launch_bounds__(NW * 64) void fwd_seg_kernel(int64_t B, int64_t T, 
                                                           float *__restrict__ y,
                                                           const float *__restrict__ s_in,
                                                           float *__restrict__ s_out) {
-    __shared__ SegShared<NW, LS> sh;
-    const int64_t ngroups = (C + 63) / 64;
+    using Geo = SegGeom<NW, LS, CW>;
+    __shared__ SegShared<NW> sh;
+    const int64_t ngroups = (C + CW - 1) / CW;
     const int64_t g = blockIdx.x % ngroups;
     const int64_t bb = blockIdx.x / ngroups;
-    const int lane = threadIdx.x & 63;
-    const int64_t c = g * 64 + lane;
+    Geo G;
+    G.lane = threadIdx.x & 63;
+    G.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    G.seg = G.wave * Geo::SPW + G.lane / CW;
+    G.slot = G.wave * 64 + G.lane;
+    const int ch_local = G.lane % CW;
+    const int64_t c = g * CW + ch_local;
     const bool active = c < C;
     const Chan ch = make_chan(active ? w[c] : 0.0f, active ? u[c] : 0.0f);
     // the choice is uniform over the workgroup (all waves share the channels)
     const bool fast = __syncthreads_and(chan_fast_ok(ch));
-    // wave-uniform base of this (sequence, channel group); inactive lanes read
-    // the group's first channel and never store
-    const int64_t base = bb * T * C + g * 64;
-    const uint32_t voff = active ? (uint32_t)lane * 4u : 0u;
-    const bool full = T % (NW * LS) == 0;
+    // wave-uniform base of this (sequence, channel group); each lane adds its
+    // channel and, when a wave holds several segments, its segment's rows.
+    // Inactive lanes read the group's first channel and never store.
+    const int64_t base = bb * T * C + g * CW;
+    const uint32_t voff = (active ? (uint32_t)ch_local * 4u : 0u) +
+                          (uint32_t)(G.lane / CW) * (uint32_t)LS * (uint32_t)(C * 4);
+    const bool full = T % Geo::TT == 0;
     if (fast && full)
-        seg_body<NW, LS, false, true>(B, T, C, bb, c, active, ch, k + base, v + base, y + base,
-                                      voff, s_in, s_out, sh);
+        seg_body<NW, LS, CW, false, true>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+                                          y + base, voff, s_in, s_out, sh);
     else if (fast)
-        seg_body<NW, LS, false, false>(B, T, C, bb, c, active, ch, k + base, v + base, y + base,
-                                       voff, s_in, s_out, sh);
+        seg_body<NW, LS, CW, false, false>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+                                           y + base, voff, s_in, s_out, sh);
     else if (full)
-        seg_body<NW, LS, true, true>(B, T, C, bb, c, active, ch, k + base, v + base, y + base,
-                                     voff, s_in, s_out, sh);
+        seg_body<NW, LS, CW, true, true>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+                                         y + base, voff, s_in, s_out, sh);
     else
-        seg_body<NW, LS, true, false>(B, T, C, bb, c, active, ch, k + base, v + base, y + base,
-                                      voff, s_in, s_out, sh);
+        seg_body<NW, LS, CW, true, false>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+                                          y + base, voff, s_in, s_out, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -282,33 +323,33 @@ hipError_t launch_forward_lane(const FwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int NW, int LS>
+template <int NW, int LS, int CW>
 static hipError_t launch_seg(const FwdArgs &a, hipStream_t st) {
-    const int64_t grid = a.B * ((a.C + 63) / 64);
-    hipLaunchKernelGGL((fwd_seg_kernel<NW, LS>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a.B,
-                       a.T, a.C, a.w, a.u, a.k, a.v, a.y, a.s_in, a.s_out);
+    const int64_t grid = a.B * ((a.C + CW - 1) / CW);
+    hipLaunchKernelGGL((fwd_seg_kernel<NW, LS, CW>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
+                       a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.y, a.s_in, a.s_out);
     return hipGetLastError();
 }
 
-// Compiled (segments, seg_len) variants of the segmented kernel.
-bool forward_seg_supported(int nw, int ls) {
-    switch (nw * 1000 + ls) {
-        case 16008: case 16016: case 8016: case 8032: case 4032:
-            return true;
-        default:
-            return false;
-    }
+// Compiled variants of the segmented kernel, keyed by (segments per tile,
+// tokens per segment, channels per workgroup).
+#define WKV_SEG_VARIANTS(X)                                                            \
+    X(16, 16, 64) X(16, 8, 64) X(8, 16, 64) X(8, 32, 64) X(4, 32, 64) X(16, 16, 32)   \
+    X(32, 8, 32) X(16, 8, 32) X(16, 16, 16) X(32, 8, 16)
+
+bool forward_seg_supported(int nseg, int ls, int cw) {
+#define X(NSEG, LS, CW) if (nseg == NSEG && ls == LS && cw == CW) return true;
+    WKV_SEG_VARIANTS(X)
+#undef X
+    return false;
 }
 
-hipError_t launch_forward_seg(const FwdArgs &a, int nw, int ls, hipStream_t st) {
-    switch (nw * 1000 + ls) {
-        case 16008: return launch_seg<16, 8>(a, st);
-        case 16016: return launch_seg<16, 16>(a, st);
-        case 8016: return launch_seg<8, 16>(a, st);
-        case 8032: return launch_seg<8, 32>(a, st);
-        case 4032: return launch_seg<4, 32>(a, st);
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_forward_seg(const FwdArgs &a, int nseg, int ls, int cw, hipStream_t st) {
+#define X(NSEG, LS, CW) \
+    if (nseg == NSEG && ls == LS && cw == CW) return launch_seg<NSEG * CW / 64, LS, CW>(a, st);
+    WKV_SEG_VARIANTS(X)
+#undef X
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_state_copy(int64_t lanes, const float *s_in, float *s_out, hipStream_t st) {

@@ -33,16 +33,22 @@ struct BwdArgs {
 
 // forward (wkv_forward.hip)
 hipError_t launch_forward_lane(const FwdArgs &a, hipStream_t st);
-bool forward_seg_supported(int nw, int ls);
-hipError_t launch_forward_seg(const FwdArgs &a, int nw, int ls, hipStream_t st);
+bool forward_seg_supported(int nseg, int ls, int cw);
+hipError_t launch_forward_seg(const FwdArgs &a, int nseg, int ls, int cw, hipStream_t st);
 hipError_t launch_state_copy(int64_t lanes, const float *s_in, float *s_out, hipStream_t st);
 
 // forward with decoupled look-back (wkv_lookback.hip)
-bool forward_lookback_supported(int nw, int ls);
-int64_t lookback_tiles(int64_t B, int64_t T, int64_t C, int nw, int ls);
-size_t lookback_scratch_bytes(int64_t ntiles);
-hipError_t launch_forward_lookback(const FwdArgs &a, int nw, int ls, void *scratch,
-                                   hipStream_t st);
+struct LookbackScratch {
+    void *base;      // zero-initialised when allocated
+    uint32_t epoch;  // distinct for every launch on it, never 0
+};
+// (cg, ns, ls): groups of 64 channels side by side, segments stacked, tokens
+// per segment
+bool forward_lookback_supported(int cg, int ns, int ls);
+bool lookback_grid_ok(int64_t B, int64_t T, int64_t C, int cg, int ns, int ls);
+size_t lookback_scratch_bytes(int64_t B, int64_t T, int64_t C, int ns, int ls);
+hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,
+                                   const LookbackScratch &sc, hipStream_t st);
 
 // step (wkv_step.hip)
 hipError_t launch_step(const StepArgs &a, hipStream_t st);

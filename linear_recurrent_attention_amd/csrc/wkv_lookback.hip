@@ -3,26 +3,42 @@
 //
 // Same result as the other forward kernels (RWKV architecture deep dive,
 // youngju.dev, "WKV mechanism: core computation"; state carried as in the
-// rwkv-architecture skill page, "Quick start").  The sequence of every
-// (b, 64-channel group) lane group is cut into blocks of NW*LS tokens, and each
-// block is one small workgroup: wave s loads its LS tokens of k, v (one 256-byte
-// row per load), folds them into a summary, the NW summaries are composed
-// through LDS, and the block's aggregate is published.  Wave 0 then walks back
-// over earlier blocks of the same lane group, composing their published states
-// until it meets one that already holds the whole prefix, publishes the
-// block's inclusive state, and every wave re-sweeps its tokens from its own
-// starting state, writing y.  Each workgroup touches its k, v and y once, so
-// HBM traffic is the algorithmic 12 bytes per lane-token; many independent
-// workgroups per CU hide the memory latency.
+// rwkv-architecture skill page, "Quick start").  Every sequence is cut into
+// blocks of NS*LS tokens and its channels into groups of 64 (one wave wide).
+// A workgroup takes one block of CG adjacent groups of one sequence: CG waves
+// side by side (so each token row is read 256*CG bytes at a time) times NS
+// waves stacked along the block.  Wave (g, s) loads its LS tokens of group g,
+// folds them into a summary, and the NS summaries of a group compose through
+// LDS into the block's aggregate, which is published.  The workgroup then
+// looks back over earlier blocks of each of its groups, folding their
+// published states until it meets one that holds the whole prefix, publishes
+// its own inclusive state, and every wave re-sweeps its tokens from its own
+// starting state, writing y.  Each workgroup reads its k and v once and
+// writes its y once, so HBM traffic is the algorithmic 12 bytes per
+// lane-token; the workgroups are small and short-lived, so many of them per
+// CU keep the memory system busy while others wait.
 //
-// Ordering and progress.  Workgroups take tickets from an atomic counter and
-// process blocks in ticket order, all lane groups' block 0 first, then block 1,
-// and so on; a block waits only on blocks with smaller tickets, which started
-// earlier and are resident or finished, so the look-back always terminates.
-// Flags carry an epoch that the last workgroup of a launch advances (and it
-// resets the counters), so consecutive launches on one stream need no clearing
-// of the scratch buffer in between.  Every spin is bounded: past the bound the
-// block's outputs become NaN instead of hanging.
+// Publishing without fences.  A release fence at device scope writes back the
+// issuing die's whole L2 and costs ~0.1 us per workgroup on MI355X, serialised,
+// which would dominate.  Instead every published value is its own 64-bit word:
+// the high half is a tag (launch epoch and status), the low half the float's
+// bits.  A word is written and read with relaxed device-scope atomics, which
+// are single-copy atomic and coherent across the dies, so a reader that sees
+// the expected tag on a word also sees its value; no ordering between words is
+// needed because each word validates itself.  A block's aggregate and its
+// inclusive state go to separate slots, fetched together: a reader that
+// catches the inclusive slot half-way through being written still has the
+// whole aggregate to fold.
+//
+// Ordering and progress.  Workgroups are numbered block-major (channel set
+// fastest, then sequence, then block) and the hardware dispatches them in that
+// order, so every workgroup of block j is dispatched after every workgroup of
+// blocks < j.  A workgroup waits only on
+// blocks before its own, so the earliest unfinished workgroup never waits on
+// one that has not started, and the look-back always terminates.  The host
+// gives each launch a fresh epoch (per stream), so nothing on the device has to
+// be reset between launches.  Every spin is bounded as well: past the bound the
+// affected outputs become NaN instead of the kernel hanging.
 #include "wkv_device.hpp"
 #include "wkv_internal.hpp"
 
@@ -31,296 +47,379 @@ namespace wkv {
 namespace {
 
 constexpr uint32_t kAgg = 1u;   // block aggregate published
-constexpr uint32_t kIncl = 2u;  // inclusive prefix (state after the block) published
-constexpr int kWindow = 8;      // predecessors examined per look-back round
-constexpr uint32_t kMaxSpin = 1u << 20;
+constexpr uint32_t kIncl = 2u;  // inclusive state (after the block) published
+constexpr uint32_t kMaxSpin = 1u << 16;
 
-// Scratch layout (bytes): header | flags[ntiles] | agg[ntiles][4][64] | incl[ntiles][4][64]
-struct LbHeader {
-    uint32_t ticket;
-    uint32_t done;
-    uint32_t epoch;
-    uint32_t pad[61];
-};
+// One published state: [4][64] tagged words (a, b, e0, n per lane).
+using Word = unsigned long long;
+constexpr int kSlotWords = 4 * 64;
 
-__device__ __forceinline__ uint32_t ld_flag(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void publish(Word *slot, int lane, const Lane &L, uint32_t tag) {
+    const Word t = (Word)tag << 32;
+    const float v[4] = {L.a, L.b, L.e0, L.n};
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+        __hip_atomic_store(&slot[f * 64 + lane], t | __builtin_bit_cast(uint32_t, v[f]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void put_state(float *slot, int lane, const Lane &L) {
-    slot[0 * 64 + lane] = L.a;
-    slot[1 * 64 + lane] = L.b;
-    slot[2 * 64 + lane] = L.e0;
-    slot[3 * 64 + lane] = L.n;
+// Reads one slot; returns whether all four words of this lane carry `tag`.
+__device__ __forceinline__ bool fetch(const Word *slot, int lane, uint32_t tag, Lane &L) {
+    Word w[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+        w[f] = __hip_atomic_load(&slot[f * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    L = Lane{__builtin_bit_cast(float, (uint32_t)w[0]), __builtin_bit_cast(float, (uint32_t)w[1]),
+             __builtin_bit_cast(float, (uint32_t)w[2]), __builtin_bit_cast(float, (uint32_t)w[3])};
+    bool ok = true;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) ok = ok && (uint32_t)(w[f] >> 32) == tag;
+    return ok;
 }
 
-__device__ __forceinline__ Lane get_state(const float *slot, int lane) {
-    return Lane{slot[0 * 64 + lane], slot[1 * 64 + lane], slot[2 * 64 + lane], slot[3 * 64 + lane]};
-}
-
-template <int NW, int LS>
+template <int CG, int NS>
 struct LbShared {
-    float s[4][NW][64];  // segment summaries
-    float p[4][64];      // state at the start of the block
-    uint32_t ticket;
-    uint32_t epoch;
-    uint32_t failed;
+    float s[4][NS][CG][64];    // segment summaries
+    float pv[4][NS][CG][64];   // predecessor states fetched this round
+    uint32_t pst[NS][CG];      // their status: 0 not ready, kAgg, kIncl
+    uint32_t gdone[CG];        // group has its whole prefix (or gave up)
 };
 
-template <int NW, int LS, bool SAFE>
-__device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const Chan &ch, int64_t bb,
-                                        int64_t c, bool active, int64_t j, int64_t NLG, int64_t lg,
-                                        uint32_t ticket, uint32_t epoch, const float *kseq,
-                                        const float *vseq, float *yseq, uint32_t voff,
-                                        const float *__restrict__ s_in, float *__restrict__ s_out,
-                                        uint32_t *flags, float *aggv, float *inclv,
-                                        LbShared<NW, LS> &sh) {
-    constexpr int TB = NW * LS;
-    const int lane = threadIdx.x & 63;
-    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t rowb = (uint32_t)(C * 4);
-    const int64_t t0 = j * TB + (int64_t)s * LS;
+template <int CG, int NS>
+__device__ __forceinline__ Lane lds_lane(const float (&a)[4][NS][CG][64], int s, int g, int lane) {
+    return Lane{a[0][s][g][lane], a[1][s][g][lane], a[2][s][g][lane], a[3][s][g][lane]};
+}
 
-    // load this wave's tokens (rows past the end of the sequence are not read)
-    float K[LS], V[LS];
-    {
-        const TileRows kr(kseq + t0 * C, voff, rowb), vr(vseq + t0 * C, voff, rowb);
-        if (t0 + LS <= T) {
-#pragma unroll
-            for (int q = 0; q < LS; ++q) {
-                K[q] = kr.ld(q);
-                V[q] = vr.ld(q);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < LS; ++q) {
-                K[q] = (t0 + q < T) ? kr.ld(q) : 0.0f;
-                V[q] = (t0 + q < T) ? vr.ld(q) : 0.0f;
-            }
-        }
-    }
+template <int CG, int NS>
+__device__ __forceinline__ void lds_put(float (&a)[4][NS][CG][64], int s, int g, int lane,
+                                        const Lane &L) {
+    a[0][s][g][lane] = L.a;
+    a[1][s][g][lane] = L.b;
+    a[2][s][g][lane] = L.e0;
+    a[3][s][g][lane] = L.n;
+}
 
-    // (1) segment summary from the empty state
+// Per-wave view of the block: which group and segment it holds, where its rows
+// are.
+struct LbWave {
+    int lane, g, s;          // lane, group within the workgroup, segment
+    int64_t bb, j;           // sequence, block
+    int64_t grp;             // group index within the sequence
+    bool gok;                // the group exists (C may end inside the last set)
+    bool active;             // this lane's channel exists
+    int64_t c;               // channel
+    int64_t t0;              // first token of the segment
+    uint32_t voff, rowb;     // lane byte offset, row pitch
+};
+
+// FULL: the whole block lies inside the sequence, so no token needs a bounds
+// test (a workgroup-uniform property: only the last block can be partial).
+template <int CG, int NS, int LS, bool SAFE, bool FULL>
+__device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const Chan &ch,
+                                        const LbWave &q, const float (&K)[LS], const float (&V)[LS],
+                                        float *yseq, const float *__restrict__ s_in,
+                                        float *__restrict__ s_out, Word *aggs, Word *incls,
+                                        uint32_t epoch, LbShared<CG, NS> &sh) {
+    constexpr int TB = NS * LS;
+    const int lane = q.lane, g = q.g, s = q.s;
+    const int64_t j = q.j;
+    const int64_t ngroups = (C + 63) >> 6;
+    // slot offset of (block, sequence, group)
+    auto slot_of = [&](int64_t blk) { return ((blk * B + q.bb) * ngroups + q.grp) * kSlotWords; };
+    const uint32_t tag_agg = (epoch << 2) | kAgg, tag_incl = (epoch << 2) | kIncl;
+
+    // (1) segment summary from the empty state, shared through LDS
     Lane S = lane_empty();
 #pragma unroll
-    for (int q = 0; q < LS; ++q)
-        if (t0 + q < T) absorb(S, K[q] * kLog2e, V[q], ch);
-    sh.s[0][s][lane] = S.a;
-    sh.s[1][s][lane] = S.b;
-    sh.s[2][s][lane] = S.e0;
-    sh.s[3][s][lane] = S.n;
+    for (int t = 0; t < LS; ++t)
+        if (FULL || q.t0 + t < T) absorb(S, K[t] * kLog2e, V[t], ch);
+    lds_put(sh.s, s, g, lane, S);
     __syncthreads();
+    // the block's aggregate (the summaries stay in LDS: the segment prefixes
+    // are recomputed from them after the look-back, which keeps fewer registers
+    // live while it waits)
+    Lane agg = lds_lane(sh.s, 0, g, lane);
+#pragma unroll
+    for (int w = 1; w < NS; ++w) compose(agg, lds_lane(sh.s, w, g, lane), ch.W, (float)LS);
 
-    if (s == 0) {
-        // aggregate of the block: segments 0..NW-1
-        Lane agg = S;
-#pragma unroll
-        for (int w = 1; w < NW; ++w)
-            compose(agg, Lane{sh.s[0][w][lane], sh.s[1][w][lane], sh.s[2][w][lane], sh.s[3][w][lane]},
-                    ch.W, (float)LS);
-        Lane P = lane_empty();  // state at the start of the block
-        bool failed = false;
-        if (j == 0) {
-            if (s_in && active)
-                P = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
-                            o_in(s_in[(2 * B + bb) * C + c]));
-        } else {
-            // publish the aggregate, then walk back
-            put_state(aggv + (int64_t)ticket * 256, lane, agg);
-            __threadfence();
-            if (lane == 0)
-                __hip_atomic_store(&flags[ticket], (epoch << 2) | kAgg, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            int64_t base = j - 1;   // nearest block not yet folded into P
-            float covered = 0.0f;   // tokens covered by P
-            uint32_t spins = 0;
-            for (;;) {
-                // lane q < kWindow looks at block base - q
-                const int64_t pj = base - lane;
-                uint32_t f = 0;
-                if (lane < kWindow && pj >= 0) f = ld_flag(&flags[pj * NLG + lg]);
-                const bool ready = lane < kWindow && pj >= 0 && (f >> 2) == (epoch & 0x3fffffffu) &&
-                                   (f & 3u) != 0;
-                const bool incl = ready && (f & 3u) == kIncl;
-                const uint64_t not_ready = __ballot(!ready && lane < kWindow && pj >= 0);
-                const uint64_t inc = __ballot(incl);
-                // consume the leading ready blocks, up to and including the first
+    // (2) state at the start of the block, per group
+    Lane P = lane_empty();
+    bool failed = false;
+    if (j == 0) {
+        // only segment 0 reads state_in, before this group's inclusive state is
+        // published: the last block may write state_out over it (in-place
+        // update) as soon as that state is visible, and it depends on the values
+        // read here
+        if (s == 0 && s_in && q.active)
+            P = lane_at(s_in[(0 * B + q.bb) * C + q.c], s_in[(1 * B + q.bb) * C + q.c],
+                        o_in(s_in[(2 * B + q.bb) * C + q.c]));
+        if (s == 0) lds_put(sh.pv, 0, g, lane, P);
+        __syncthreads();
+        P = lds_lane(sh.pv, 0, g, lane);
+    } else {
+        if (s == 0 && q.gok) publish(aggs + slot_of(j), lane, agg, tag_agg);
+        int64_t base = j - 1;  // nearest block of this group not yet folded into P
+        float covered = 0.0f;  // tokens covered by P
+        uint32_t spins = 0;
+        bool done = !q.gok;
+        for (;;) {
+            // wave (g, s) examines block base - s of its group
+            if (!done) {
+                const int64_t pj = base - s;
+                uint32_t st = 0;
+                Lane X = lane_empty();
+                if (pj >= 0) {
+                    Lane Xi, Xa;
+                    const bool oi = fetch(incls + slot_of(pj), lane, tag_incl, Xi);
+                    const bool oa = fetch(aggs + slot_of(pj), lane, tag_agg, Xa);
+                    if (__all(oi)) {
+                        st = kIncl;
+                        X = Xi;
+                    } else if (__all(oa)) {
+                        st = kAgg;
+                        X = Xa;
+                    }
+                }
+                lds_put(sh.pv, s, g, lane, X);
+                if (lane == 0) sh.pst[s][g] = st;
+            }
+            __syncthreads();
+            if (!done) {
+                // fold the leading ready blocks, nearest first, up to the first
                 // inclusive one
-                const int first_nr = not_ready ? __builtin_ctzll(not_ready) : kWindow;
-                const int first_in = inc ? __builtin_ctzll(inc) : kWindow;
-                const int avail = (int)((base + 1) < kWindow ? (base + 1) : kWindow);
-                int use = first_nr < avail ? first_nr : avail;
-                bool done = false;
-                if (first_in < use) {
-                    use = first_in + 1;
-                    done = true;
-                }
-                if (use == 0) {
-                    if (++spins > kMaxSpin) {
-                        failed = true;
+                int use = 0;
+                for (int w = 0; w < NS && base - w >= 0; ++w) {
+                    const uint32_t stw = sh.pst[w][g];
+                    if (stw == 0) break;
+                    Lane Y = lds_lane(sh.pv, w, g, lane);
+                    compose(Y, P, ch.W, covered);
+                    P = Y;
+                    covered += (float)TB;
+                    ++use;
+                    if (stw == kIncl) {
+                        done = true;
                         break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                // fold blocks base, base-1, ..., base-use+1 (nearest first)
-                Lane X[kWindow];
-#pragma unroll
-                for (int q = 0; q < kWindow; ++q) {
-                    if (q < use) {
-                        const int64_t slot = (base - q) * NLG + lg;
-                        const bool isin = (inc >> q) & 1ull;
-                        X[q] = get_state((isin ? inclv : aggv) + slot * 256, lane);
-                    }
-                }
-#pragma unroll
-                for (int q = 0; q < kWindow; ++q) {
-                    if (q < use) {
-                        compose(X[q], P, ch.W, covered);
-                        P = X[q];
-                        covered += (float)TB;
                     }
                 }
                 base -= use;
-                if (done || base < 0) break;
+                if (base < 0) done = true;
+                if (!done && use == 0) {
+                    if (++spins > kMaxSpin) {
+                        failed = true;
+                        done = true;
+                    } else {
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
             }
+            if (s == 0 && lane == 0) sh.gdone[g] = done;
+            // also orders this round's LDS reads before the next round's writes
+            __syncthreads();
+            bool all = true;
+#pragma unroll
+            for (int h = 0; h < CG; ++h) all = all && sh.gdone[h] != 0;
+            if (all) break;
         }
-        // inclusive state of this block
+    }
+    if (s == 0 && q.gok) {
         Lane incl = P;
         compose(incl, agg, ch.W, (float)TB);
-        put_state(inclv + (int64_t)ticket * 256, lane, incl);
-        __threadfence();
-        if (lane == 0)
-            __hip_atomic_store(&flags[ticket], (epoch << 2) | kIncl, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        sh.p[0][lane] = P.a;
-        sh.p[1][lane] = P.b;
-        sh.p[2][lane] = P.e0;
-        sh.p[3][lane] = P.n;
-        if (lane == 0) sh.failed = failed ? 1u : 0u;
+        publish(incls + slot_of(j), lane, incl, tag_incl);
     }
-    __syncthreads();
 
-    // (3) re-sweep from this segment's starting state, writing y
-    Lane R{sh.p[0][lane], sh.p[1][lane], sh.p[2][lane], sh.p[3][lane]};
-    for (int w = 0; w < s; ++w)
-        compose(R, Lane{sh.s[0][w][lane], sh.s[1][w][lane], sh.s[2][w][lane], sh.s[3][w][lane]},
-                ch.W, (float)LS);
-    const float poison = sh.failed ? __builtin_nanf("") : 0.0f;
-    const TileRows yr(yseq + t0 * C, voff, rowb);
+    // (3) re-sweep from this segment's starting state, writing y: in one frame
+    // when the whole wave's range allows it, else token by token
+    Lane R = P;
+    for (int w = 0; w < s; ++w) compose(R, lds_lane(sh.s, w, g, lane), ch.W, (float)LS);
+    const float poison = failed ? __builtin_nanf("") : 0.0f;
+    if (q.gok) {
+        const TileRows yr(yseq + q.t0 * C, q.voff, q.rowb);
+        bool framed = false;
+        if constexpr (FULL && !SAFE) {
+            SegFrame f;
+            const bool ok = seg_frame(R, lds_lane(sh.s, s, g, lane), ch.W, (float)LS,
+                                      K[0] * kLog2e, f);
+            if (__all(ok || !q.active)) {
+                framed = true;
+                float A = f.alpha, Bs = f.beta;
 #pragma unroll
-    for (int q = 0; q < LS; ++q) {
-        if (t0 + q < T) {
-            const float yv = step<SAFE>(R, K[q] * kLog2e, V[q], ch) + poison;
-            if (active) yr.st(q, yv);
+                for (int t = 0; t < LS; ++t) {
+                    const float yv =
+                        frame_token(A, Bs, f, K[t] * kLog2e, V[t], (float)(LS - 1 - t), ch) + poison;
+                    if (q.active) yr.st(t, yv);
+                }
+                R = Lane{A, Bs, f.Ae, f.An};
+            }
+        }
+        if (!framed) {
+#pragma unroll
+            for (int t = 0; t < LS; ++t) {
+                if (FULL || q.t0 + t < T) {
+                    const float yv = step<SAFE>(R, K[t] * kLog2e, V[t], ch) + poison;
+                    if (q.active) yr.st(t, yv);
+                }
+            }
         }
     }
-    if (s_out && active && t0 <= T - 1 && T - 1 < t0 + LS) {
-        s_out[(0 * B + bb) * C + c] = R.a + poison;
-        s_out[(1 * B + bb) * C + c] = R.b + poison;
-        s_out[(2 * B + bb) * C + c] = o_out(lane_o(R, ch.W)) + poison;
+    if (s_out && q.active && q.t0 <= T - 1 && T - 1 < q.t0 + LS) {
+        s_out[(0 * B + q.bb) * C + q.c] = R.a + poison;
+        s_out[(1 * B + q.bb) * C + q.c] = R.b + poison;
+        s_out[(2 * B + q.bb) * C + q.c] = o_out(lane_o(R, ch.W)) + poison;
     }
 }
 
-template <int NW, int LS>
-__global__ __launch_bounds__(NW * 64) void fwd_lookback_kernel(
+// 1-D grid over (block, sequence, set of CG groups), set fastest; the host
+// guarantees nsets * B < 2^31 so the decode stays in 32 bits
+// Waves per SIMD the register allocation must allow: the token registers
+// (2 LS per lane) dominate, and the occupancy they leave decides how much of
+// the memory latency other workgroups hide.
+constexpr int lb_waves_per_simd(int ls) { return ls <= 8 ? 7 : (ls <= 16 ? 6 : 3); }
+
+template <int CG, int NS, int LS>
+__global__ __launch_bounds__(CG * NS * 64)
+__attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS)))) void fwd_lookback_kernel(
     int64_t B, int64_t T, int64_t C, const float *__restrict__ w, const float *__restrict__ u,
     const float *__restrict__ k, const float *__restrict__ v, float *__restrict__ y,
-    const float *s_in, float *s_out, LbHeader *hdr, uint32_t *flags, float *aggv, float *inclv) {
-    __shared__ LbShared<NW, LS> sh;
-    constexpr int TB = NW * LS;
-    if (threadIdx.x == 0) {
-        sh.ticket = atomicAdd(&hdr->ticket, 1u);
-        sh.epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    // tickets run 0..gridDim.x-1 within a launch; the modulo only keeps a
-    // counter left behind by an aborted launch from indexing past the scratch
-    const uint32_t ticket = sh.ticket % gridDim.x;
-    const uint32_t epoch = sh.epoch;
-    const int64_t ngroups = (C + 63) / 64;
-    const int64_t NLG = B * ngroups;
-    const int64_t j = ticket / NLG;
-    const int64_t lg = ticket - j * NLG;
-    const int64_t bb = lg / ngroups;
-    const int64_t g = lg - bb * ngroups;
-    const int lane = threadIdx.x & 63;
-    const int64_t c = g * 64 + lane;
-    const bool active = c < C;
-    const Chan ch = make_chan(active ? w[c] : 0.0f, active ? u[c] : 0.0f);
-    const bool fast = __syncthreads_and(chan_fast_ok(ch));
-    const int64_t base = bb * T * C + g * 64;
-    const uint32_t voff = active ? (uint32_t)lane * 4u : 0u;
-    if (fast)
-        lb_body<NW, LS, false>(B, T, C, ch, bb, c, active, j, NLG, lg, ticket, epoch, k + base,
-                               v + base, y + base, voff, s_in, s_out, flags, aggv, inclv, sh);
-    else
-        lb_body<NW, LS, true>(B, T, C, ch, bb, c, active, j, NLG, lg, ticket, epoch, k + base,
-                              v + base, y + base, voff, s_in, s_out, flags, aggv, inclv, sh);
-    // the last workgroup of the launch readies the scratch for the next one
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t total = gridDim.x;
-        if (atomicAdd(&hdr->done, 1u) == total - 1) {
-            __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const float *s_in, float *s_out, Word *aggs, Word *incls, uint32_t epoch, uint32_t nsets) {
+    constexpr int TB = NS * LS;
+    __shared__ LbShared<CG, NS> sh;
+    LbWave q;
+    q.lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    q.g = wave % CG;
+    q.s = wave / CG;
+    const uint32_t per_block = nsets * (uint32_t)B;
+    const uint32_t jb = blockIdx.x / per_block;
+    const uint32_t rem = blockIdx.x - jb * per_block;
+    const uint32_t bb = rem / nsets;
+    const uint32_t set = rem - bb * nsets;
+    q.bb = bb;
+    q.j = jb;
+    const int64_t ngroups = (C + 63) >> 6;
+    q.grp = (int64_t)set * CG + q.g;
+    q.gok = q.grp < ngroups;
+    q.c = q.grp * 64 + q.lane;
+    q.active = q.gok && q.c < C;
+    q.t0 = q.j * TB + (int64_t)q.s * LS;
+    q.rowb = (uint32_t)(C * 4);
+    q.voff = q.active ? (uint32_t)q.lane * 4u : 0u;
+    const int64_t base = q.bb * T * C + (q.gok ? q.grp * 64 : 0);
+
+    // channel constants, then this wave's tokens, all issued before any wait:
+    // waiting for w and u (issued first) leaves the token loads in flight.
+    const int64_t cc = q.active ? q.c : 0;  // a valid channel for every lane
+    const float wc = w[cc], uc = u[cc];
+    // Every token load is issued unconditionally, back to back, with no branch
+    // around them (a branch would make the compiler's wait counts assume the
+    // shorter path and wait for all of them at once): rows past the end of the
+    // sequence re-read its last row, and a wave whose group lies past the last
+    // channel reads group 0 -- valid addresses whose values are never used,
+    // since every token loop stops at T and such a wave stores nothing.
+    float K[LS], V[LS];
+    {
+        const int64_t t0c = q.t0 < T ? q.t0 : T - 1;  // T >= 1 here
+        const int64_t left = T - 1 - t0c;
+        const uint32_t tmax =
+            __builtin_amdgcn_readfirstlane(left < LS - 1 ? (uint32_t)left : (uint32_t)(LS - 1));
+        const TileRows kr(k + base + t0c * C, q.voff, q.rowb), vr(v + base + t0c * C, q.voff, q.rowb);
+#pragma unroll
+        for (int t = 0; t < LS; ++t) {
+            const uint32_t r = (uint32_t)t < tmax ? (uint32_t)t : tmax;
+            K[t] = kr.ld((int)r);
+            V[t] = vr.ld((int)r);
         }
     }
-    (void)TB;
+    // keep the loads here, in flight while the rest of the prologue runs (the
+    // compiler would otherwise sink them into the branches below)
+    asm volatile("" ::: "memory");
+    const Chan ch = make_chan(q.active ? wc : 0.0f, q.active ? uc : 0.0f);
+    const bool fast = __syncthreads_and(chan_fast_ok(ch));
+    const bool full = (q.j + 1) * TB <= T;  // the whole block lies inside the sequence
+    if (fast) {
+        if (full)
+            lb_body<CG, NS, LS, false, true>(B, T, C, ch, q, K, V, y + base, s_in, s_out, aggs,
+                                             incls, epoch, sh);
+        else
+            lb_body<CG, NS, LS, false, false>(B, T, C, ch, q, K, V, y + base, s_in, s_out, aggs,
+                                              incls, epoch, sh);
+    } else {
+        if (full)
+            lb_body<CG, NS, LS, true, true>(B, T, C, ch, q, K, V, y + base, s_in, s_out, aggs,
+                                            incls, epoch, sh);
+        else
+            lb_body<CG, NS, LS, true, false>(B, T, C, ch, q, K, V, y + base, s_in, s_out, aggs,
+                                             incls, epoch, sh);
+    }
 }
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// (CG, NS, LS) variants: CG groups of 64 channels side by side, NS segments of
+// LS tokens stacked
+#define WKV_LB_VARIANTS(X) \
+    X(1, 4, 16)            \
+    X(1, 8, 16)            \
+    X(1, 4, 32)            \
+    X(1, 8, 8)             \
+    X(2, 4, 16)            \
+    X(2, 2, 16)            \
+    X(2, 2, 32)            \
+    X(2, 4, 8)             \
+    X(4, 2, 16)            \
+    X(4, 2, 8)
+
+constexpr int lb_key(int cg, int ns, int ls) { return (cg * 64 + ns) * 1024 + ls; }
+
+template <int CG, int NS, int LS>
+hipError_t launch_lb(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st) {
+    const int64_t ngroups = (a.C + 63) / 64;
+    const int64_t nsets = (ngroups + CG - 1) / CG;
+    const int64_t nblocks = (a.T + NS * LS - 1) / (NS * LS);
+    const int64_t nslots = nblocks * a.B * ngroups;
+    Word *aggs = (Word *)sc.base;
+    Word *incls = (Word *)((char *)sc.base + align_up((size_t)nslots * kSlotWords * sizeof(Word)));
+    hipLaunchKernelGGL((fwd_lookback_kernel<CG, NS, LS>), dim3((unsigned)(nsets * a.B * nblocks)),
+                       dim3(CG * NS * 64), 0, st, a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.y, a.s_in,
+                       a.s_out, aggs, incls, sc.epoch, (uint32_t)nsets);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-bool forward_lookback_supported(int nw, int ls) {
-    switch (nw * 1000 + ls) {
-        case 4016: case 8016: case 4032: case 8008: case 16008:
-            return true;
+bool forward_lookback_supported(int cg, int ns, int ls) {
+    switch (lb_key(cg, ns, ls)) {
+#define X(CG, NS, LS) case lb_key(CG, NS, LS):
+        WKV_LB_VARIANTS(X)
+#undef X
+        return true;
         default:
             return false;
     }
 }
 
-int64_t lookback_tiles(int64_t B, int64_t T, int64_t C, int nw, int ls) {
-    const int64_t TB = (int64_t)nw * ls;
-    return ((T + TB - 1) / TB) * B * ((C + 63) / 64);
+bool lookback_grid_ok(int64_t B, int64_t T, int64_t C, int cg, int ns, int ls) {
+    const int64_t nsets = ((C + 63) / 64 + cg - 1) / cg;
+    const int64_t nblocks = (T + (int64_t)ns * ls - 1) / ((int64_t)ns * ls);
+    // nsets * B * nblocks < 2^31 (grid size; also bounds the 32-bit decode)
+    return nsets <= 0x7fffffffLL / B && nsets * B <= 0x7fffffffLL / nblocks;
 }
 
-size_t lookback_scratch_bytes(int64_t ntiles) {
-    return align_up(sizeof(LbHeader)) + align_up((size_t)ntiles * 4) +
-           2 * align_up((size_t)ntiles * 256 * sizeof(float));
+size_t lookback_scratch_bytes(int64_t B, int64_t T, int64_t C, int ns, int ls) {
+    const int64_t nblocks = (T + (int64_t)ns * ls - 1) / ((int64_t)ns * ls);
+    const int64_t nslots = nblocks * B * ((C + 63) / 64);
+    return 2 * align_up((size_t)nslots * kSlotWords * sizeof(Word));
 }
 
-template <int NW, int LS>
-static hipError_t launch_lb(const FwdArgs &a, void *scratch, int64_t ntiles, hipStream_t st) {
-    char *p = (char *)scratch;
-    LbHeader *hdr = (LbHeader *)p;
-    p += align_up(sizeof(LbHeader));
-    uint32_t *flags = (uint32_t *)p;
-    p += align_up((size_t)ntiles * 4);
-    float *aggv = (float *)p;
-    p += align_up((size_t)ntiles * 256 * sizeof(float));
-    float *inclv = (float *)p;
-    hipLaunchKernelGGL((fwd_lookback_kernel<NW, LS>), dim3((unsigned)ntiles), dim3(NW * 64), 0, st,
-                       a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.y, a.s_in, a.s_out, hdr, flags, aggv,
-                       inclv);
-    return hipGetLastError();
-}
-
-hipError_t launch_forward_lookback(const FwdArgs &a, int nw, int ls, void *scratch,
-                                   hipStream_t st) {
-    const int64_t ntiles = lookback_tiles(a.B, a.T, a.C, nw, ls);
-    switch (nw * 1000 + ls) {
-        case 4016: return launch_lb<4, 16>(a, scratch, ntiles, st);
-        case 8016: return launch_lb<8, 16>(a, scratch, ntiles, st);
-        case 4032: return launch_lb<4, 32>(a, scratch, ntiles, st);
-        case 8008: return launch_lb<8, 8>(a, scratch, ntiles, st);
-        case 16008: return launch_lb<16, 8>(a, scratch, ntiles, st);
-        default: return hipErrorInvalidValue;
+hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,
+                                   const LookbackScratch &sc, hipStream_t st) {
+    switch (lb_key(cg, ns, ls)) {
+#define X(CG, NS, LS) \
+    case lb_key(CG, NS, LS): return launch_lb<CG, NS, LS>(a, sc, st);
+        WKV_LB_VARIANTS(X)
+#undef X
+        default:
+            return hipErrorInvalidValue;
     }
 }
 

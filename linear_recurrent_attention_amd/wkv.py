@@ -49,7 +49,7 @@ class WkvError(RuntimeError):
 
 class ForwardPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("segments", ctypes.c_int32),
-                ("seg_len", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("seg_len", ctypes.c_int32), ("channels", ctypes.c_int32)]
 
 
 _lib = None
@@ -123,7 +123,8 @@ def wkv_forward(w, u, k, v, y=None, state_in=None, state_out=None, stream=None, 
 
     ``state_out`` is written when given (it may be ``state_in`` itself for an
     in-place update); pass ``state_out=True`` to have one allocated.  ``plan``
-    is an optional (kernel, segments, seg_len) triple for ``wkv_forward_ex``.
+    is an optional (kernel, segments, seg_len[, channels]) tuple for
+    ``wkv_forward_ex``.
     """
     B, T, C = _bundle_shape(k, state_in)
     if y is None:
@@ -136,7 +137,7 @@ def wkv_forward(w, u, k, v, y=None, state_in=None, state_out=None, stream=None, 
     if plan is None:
         _check("wkv_forward", lib.wkv_forward(*args, _stream(stream)))
     else:
-        p = ForwardPlan(*plan, 0) if len(plan) == 3 else ForwardPlan(*plan)
+        p = ForwardPlan(*plan) if len(plan) == 4 else ForwardPlan(*plan, 0)
         _check("wkv_forward_ex", lib.wkv_forward_ex(*args, ctypes.byref(p), _stream(stream)))
     return y, state_out
 
@@ -144,7 +145,7 @@ def wkv_forward(w, u, k, v, y=None, state_in=None, state_out=None, stream=None, 
 def wkv_forward_plan_auto(B: int, T: int, C: int):
     p = ForwardPlan()
     _check("wkv_forward_plan_auto", load_library().wkv_forward_plan_auto(B, T, C, ctypes.byref(p)))
-    return (p.kernel, p.segments, p.seg_len)
+    return (p.kernel, p.segments, p.seg_len, p.channels)
 
 
 def wkv_step(w, u, k, v, state_in, state_out=None, y=None, stream=None):

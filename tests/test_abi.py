@@ -131,7 +131,8 @@ def test_forward_ex_rejects_unknown_plans(lib):
     args = [2, 8, 16, vp(P), vp(P + 0x1000), vp(P + 0x100000), vp(P + 0x10000000),
             vp(P + 0x20000000), None, None]
     for plan in ((9, 0, 0, 0), (W.WKV_KERNEL_SEGMENTED, 3, 16, 0),
-                 (W.WKV_KERNEL_SEGMENTED, 16, 7, 0), (W.WKV_KERNEL_LANE, 0, 0, 1)):
+                 (W.WKV_KERNEL_SEGMENTED, 16, 7, 0), (W.WKV_KERNEL_LANE, 0, 0, 32),
+                 (W.WKV_KERNEL_SEGMENTED, 16, 16, 48), (W.WKV_KERNEL_LOOKBACK, 4, 16, 32)):
         p = W.ForwardPlan(*plan)
         assert lib.wkv_forward_ex(*args, ctypes.byref(p), None) == W.WKV_ERR_UNSUPPORTED
 

@@ -25,11 +25,21 @@ PLANS = {
     "seg8x16": (wkv.WKV_KERNEL_SEGMENTED, 8, 16),
     "seg8x32": (wkv.WKV_KERNEL_SEGMENTED, 8, 32),
     "seg4x32": (wkv.WKV_KERNEL_SEGMENTED, 4, 32),
+    "seg16x16c32": (wkv.WKV_KERNEL_SEGMENTED, 16, 16, 32),
+    "seg32x8c32": (wkv.WKV_KERNEL_SEGMENTED, 32, 8, 32),
+    "seg16x8c32": (wkv.WKV_KERNEL_SEGMENTED, 16, 8, 32),
+    "seg16x16c16": (wkv.WKV_KERNEL_SEGMENTED, 16, 16, 16),
+    "seg32x8c16": (wkv.WKV_KERNEL_SEGMENTED, 32, 8, 16),
     "lb4x16": (wkv.WKV_KERNEL_LOOKBACK, 4, 16),
     "lb8x16": (wkv.WKV_KERNEL_LOOKBACK, 8, 16),
     "lb4x32": (wkv.WKV_KERNEL_LOOKBACK, 4, 32),
     "lb8x8": (wkv.WKV_KERNEL_LOOKBACK, 8, 8),
-    "lb16x8": (wkv.WKV_KERNEL_LOOKBACK, 16, 8),
+    "lb2x16c128": (wkv.WKV_KERNEL_LOOKBACK, 2, 16, 128),
+    "lb4x16c128": (wkv.WKV_KERNEL_LOOKBACK, 4, 16, 128),
+    "lb2x32c128": (wkv.WKV_KERNEL_LOOKBACK, 2, 32, 128),
+    "lb4x8c128": (wkv.WKV_KERNEL_LOOKBACK, 4, 8, 128),
+    "lb2x16c256": (wkv.WKV_KERNEL_LOOKBACK, 2, 16, 256),
+    "lb2x8c256": (wkv.WKV_KERNEL_LOOKBACK, 2, 8, 256),
 }
 
 
@@ -101,7 +111,8 @@ def test_wide_exponents_match_oracle(oracle, plan):
     assert_state_close(f64(so), sr)
 
 
-@pytest.mark.parametrize("plan", ["lane", "seg16x16", "seg8x32"])
+@pytest.mark.parametrize("plan", ["lane", "seg16x16", "seg8x32", "seg32x8c16", "lb4x16",
+                                  "lb4x16c128"])
 def test_extreme_bonus_takes_the_two_exponential_path(oracle, plan):
     """|u - w| beyond the one-exponential step's range on some channels."""
     d = synth.make(synth.TINY, index=3, B=2, T=200, C=128)
@@ -114,7 +125,8 @@ def test_extreme_bonus_takes_the_two_exponential_path(oracle, plan):
     assert_state_close(f64(so), sr)
 
 
-@pytest.mark.parametrize("plan", ["auto", "lane", "seg16x16"])
+@pytest.mark.parametrize("plan", ["auto", "lane", "seg16x16", "seg16x16c32", "lb4x16", "lb8x8",
+                                  "lb2x16c256"])
 def test_state_updated_in_place(oracle, plan):
     B, T, C = 2, 333, 80
     d = synth.make(synth.GPT, index=4, B=B, T=T, C=C)
