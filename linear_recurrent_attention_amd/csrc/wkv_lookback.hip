@@ -128,11 +128,13 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
     auto slot_of = [&](int64_t blk) { return ((blk * B + q.bb) * ngroups + q.grp) * kSlotWords; };
     const uint32_t tag_agg = (epoch << 2) | kAgg, tag_incl = (epoch << 2) | kIncl;
 
+    // K holds the keys in log2 units (k log2 e)
+
     // (1) segment summary from the empty state, shared through LDS
     Lane S = lane_empty();
 #pragma unroll
     for (int t = 0; t < LS; ++t)
-        if (FULL || q.t0 + t < T) absorb(S, K[t] * kLog2e, V[t], ch);
+        if (FULL || q.t0 + t < T) absorb(S, K[t], V[t], ch);
     lds_put(sh.s, s, g, lane, S);
     __syncthreads();
     // the block's aggregate (the summaries stay in LDS: the segment prefixes
@@ -238,14 +240,14 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
         if constexpr (FULL && !SAFE) {
             SegFrame f;
             const bool ok = seg_frame(R, lds_lane(sh.s, s, g, lane), ch.W, (float)LS,
-                                      K[0] * kLog2e, f);
+                                      K[0], f);
             if (__all(ok || !q.active)) {
                 framed = true;
                 float A = f.alpha, Bs = f.beta;
 #pragma unroll
                 for (int t = 0; t < LS; ++t) {
                     const float yv =
-                        frame_token(A, Bs, f, K[t] * kLog2e, V[t], (float)(LS - 1 - t), ch) + poison;
+                        frame_token(A, Bs, f, K[t], V[t], (float)(LS - 1 - t), ch) + poison;
                     if (q.active) yr.st(t, yv);
                 }
                 R = Lane{A, Bs, f.Ae, f.An};
@@ -255,7 +257,7 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
 #pragma unroll
             for (int t = 0; t < LS; ++t) {
                 if (FULL || q.t0 + t < T) {
-                    const float yv = step<SAFE>(R, K[t] * kLog2e, V[t], ch) + poison;
+                    const float yv = step<SAFE>(R, K[t], V[t], ch) + poison;
                     if (q.active) yr.st(t, yv);
                 }
             }
@@ -273,7 +275,7 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
 // Waves per SIMD the register allocation must allow: the token registers
 // (2 LS per lane) dominate, and the occupancy they leave decides how much of
 // the memory latency other workgroups hide.
-constexpr int lb_waves_per_simd(int ls) { return ls <= 8 ? 7 : (ls <= 16 ? 6 : 3); }
+constexpr int lb_waves_per_simd(int ls) { return ls <= 8 ? 8 : (ls <= 16 ? 6 : 4); }
 
 template <int CG, int NS, int LS>
 __global__ __launch_bounds__(CG * NS * 64)
@@ -333,6 +335,8 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS)))) void fwd_lookback_ke
     // compiler would otherwise sink them into the branches below)
     asm volatile("" ::: "memory");
     const Chan ch = make_chan(q.active ? wc : 0.0f, q.active ? uc : 0.0f);
+#pragma unroll
+    for (int t = 0; t < LS; ++t) K[t] *= kLog2e;
     const bool fast = __syncthreads_and(chan_fast_ok(ch));
     const bool full = (q.j + 1) * TB <= T;  // the whole block lies inside the sequence
     if (fast) {
@@ -359,6 +363,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // LS tokens stacked
 #define WKV_LB_VARIANTS(X) \
     X(1, 4, 16)            \
+    X(1, 8, 32)            \
+    X(2, 4, 32)            \
     X(1, 8, 16)            \
     X(1, 4, 32)            \
     X(1, 8, 8)             \

@@ -40,6 +40,8 @@ PLANS = {
     "lb4x8c128": (wkv.WKV_KERNEL_LOOKBACK, 4, 8, 128),
     "lb2x16c256": (wkv.WKV_KERNEL_LOOKBACK, 2, 16, 256),
     "lb2x8c256": (wkv.WKV_KERNEL_LOOKBACK, 2, 8, 256),
+    "lb8x32": (wkv.WKV_KERNEL_LOOKBACK, 8, 32),
+    "lb4x32c128": (wkv.WKV_KERNEL_LOOKBACK, 4, 32, 128),
 }
 
 
