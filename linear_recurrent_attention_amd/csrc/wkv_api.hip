@@ -101,9 +101,11 @@ hipError_t launch_with_scratch(const FwdArgs &a, int cg, int ns, int ls, size_t 
     }
     const wkv::LookbackScratch sc{s.p, s.epoch};
     e = wkv::launch_forward_lookback(a, cg, ns, ls, sc, st);
-    if (e == hipSuccess) {
-        s.epoch = (s.epoch + 1) & 0x3fffffffu;
-        if (s.epoch == 0) s.epoch = 1;
+    if (e == hipSuccess && ++s.epoch > 0x3fffffffu) {
+        // end of the 30-bit tag range: clear the slots, so that no stale tag
+        // can match a reused epoch
+        if ((e = hipMemsetAsync(s.p, 0, s.bytes, st)) != hipSuccess) return e;
+        s.epoch = 1;
     }
     return e;
 }
