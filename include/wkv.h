@@ -40,6 +40,10 @@
  *   - Every call is asynchronous on `stream` (0 = the default stream) and
  *     runs on the device that is current on the calling thread.  Calls on one
  *     stream run in order.
+ *   - Calls may be captured into a HIP graph (on a non-default stream).  Under
+ *     capture, wkv_forward uses a kernel that keeps no state between launches
+ *     (the look-back kernel's per-launch tags cannot be replayed), and a plan
+ *     that forces the look-back kernel returns WKV_ERR_UNSUPPORTED.
  *   - Indexing is 64-bit: a single call may exceed 2^31 elements.
  *
  * Errors

@@ -223,7 +223,20 @@ WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *
         if (!state_out || state_out == state_in) return WKV_OK;
         return from_hip(wkv::launch_state_copy(lanes, state_in, state_out, stream));
     }
-    if (p.kernel == WKV_KERNEL_AUTO) p = auto_plan(B, T, C, device_cus());
+    // The look-back kernel tags what it publishes with a per-launch epoch that
+    // the host advances; a captured graph would replay one epoch forever, so
+    // under stream capture the segmented kernel (no state across workgroups)
+    // runs instead, and an explicit look-back plan is refused.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (stream != nullptr && hipStreamIsCapturing(stream, &cap) != hipSuccess)
+        return WKV_ERR_HIP;
+    const bool capturing = cap != hipStreamCaptureStatusNone;
+    if (p.kernel == WKV_KERNEL_AUTO) {
+        p = auto_plan(B, T, C, device_cus());
+        if (capturing && p.kernel == WKV_KERNEL_LOOKBACK) p = wkv_forward_plan{WKV_KERNEL_SEGMENTED, 16, 16, 64};
+    } else if (capturing && p.kernel == WKV_KERNEL_LOOKBACK) {
+        return WKV_ERR_UNSUPPORTED;
+    }
     const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out};
     if (p.kernel == WKV_KERNEL_LANE) {
         if ((lanes + 255) / 256 > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
