@@ -10,16 +10,18 @@
 //   fwd_lane_kernel  one thread per lane, sequential over T.  Each wave reads
 //                    64 consecutive channels of one token row per load (256 B,
 //                    coalesced).  Enough parallelism only when B*C is large.
-//   fwd_seg_kernel   one workgroup per (sequence b, 64 channels); NW waves, wave
-//                    s owns segment s of every tile of NW*LS tokens.  Per tile:
-//                    (1) each wave folds its LS tokens into a summary from the
-//                    empty state; (2) the NW summaries are scanned across waves
-//                    through LDS, composing with the decay 2^{-W len}; (3) each
-//                    wave re-sweeps its LS tokens from its prefix state, emitting
-//                    y.  k and v stay in registers between (1) and (3), and the
-//                    next tile's k and v are loaded while the current one is
-//                    processed.  The section "Parallel training formulation"
-//                    says the sequence is computed with a scan; this is one.
+//   fwd_seg_kernel   one workgroup per (sequence b, CW channels: 64, 32 or 16);
+//                    NW waves, each wave holding 64/CW segments side by side,
+//                    so that a tile of NSEG = NW*64/CW segments of LS tokens
+//                    is covered.  Per tile: (1) each segment's tokens fold into
+//                    a summary from the empty state; (2) the NSEG summaries are
+//                    scanned through LDS, composing with the decay 2^{-W len};
+//                    (3) each segment is re-swept from its prefix state,
+//                    emitting y.  k and v stay in registers between (1) and
+//                    (3), and the next tile's k and v are loaded while the
+//                    current one is processed.  The section "Parallel training
+//                    formulation" says the sequence is computed with a scan;
+//                    this is one.
 #include "wkv_device.hpp"
 #include "wkv_internal.hpp"
 
