@@ -319,7 +319,7 @@ def bench_stability(args, torch, wkv, synth, backward: bool):
                              dv=outs[i][1], dw=dwu[0], du=dwu[1], workspace=ws, stream=stream)
         algo = 20 * lane_tok + 16 * C
         name, kname = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32", \
-            "bwd_seg_kernel<16,8>"
+            "bwd_seg_kernel<16, 8>"
     else:
         ys = [torch.empty_like(s["k"]) for s in sets]
 
