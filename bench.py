@@ -92,6 +92,22 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
+def timed_oracle(fn, budget_s: float):
+    """Calls fn(i) for i = 0, 1, ... until budget_s seconds of oracle time
+    have been spent (at least one call).  fn returns (lane-tokens, seconds of
+    oracle compute) for its sample, or None when there is no sample left.
+    Returns (lane-tokens, seconds, calls)."""
+    done, elapsed, i = 0, 0.0, 0
+    while i == 0 or elapsed < budget_s:
+        r = fn(i)
+        if r is None:
+            break
+        done += r[0]
+        elapsed += r[1]
+        i += 1
+    return done, elapsed, i
+
+
 def cpu_baseline_gpt(torch, synth, inputs_fn, budget_s: float):
     """The oracle's O(T) recurrence on whole layers of the same workload."""
     import oracle
@@ -243,6 +259,25 @@ def bench_stream(args, torch, wkv, synth):
     lane_tok = TC * C
     algo = 12 * lane_tok + 8 * C + 24 * C
     chosen = plan or wkv.wkv_forward_plan_auto(1, TC, C)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = host_cores()
+        w64, u64 = w.double().cpu().numpy(), u.double().cpu().numpy()
+        carried = [None]
+
+        def chunk(j):
+            if j >= NCH:
+                return None
+            kk, vv = k[j].double().cpu().numpy(), v[j].double().cpu().numpy()
+            t0 = time.perf_counter()
+            _, carried[0] = oracle.forward_scan(w64, u64, kk, vv, carried[0], nthreads=cores)
+            return TC * C, time.perf_counter() - t0
+
+        done, secs, calls = timed_oracle(chunk, args.cpu_seconds)
+        cpu = {"value": done / secs, "unit": "tok·ch/s", "cores": cores, "kind": "oracle",
+               "sample": f"the first {calls} of the 1024 chunks (B=1 T=1024 C=5120 each), state "
+                         f"carried, float64 O(T) recurrence on {cores} threads ({secs:.1f} s)"}
     return {"metric": "WKV streaming fwd tokens·channels/sec, B=1 C=5120, 1024 chunks x 1024",
             "value": lane_tok * NCH * args.steps / (ms * 1e-3), "unit": "tok·ch/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -254,7 +289,8 @@ def bench_stream(args, torch, wkv, synth):
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": algo / (per_call * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "traffic": measured_traffic(kernel_name(chosen, wkv), "stream"),
-                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per_call * 1e3}}
+                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per_call * 1e3},
+            "cpu_baseline": cpu}
 
 
 def bench_decode(args, torch, wkv, synth):
@@ -287,6 +323,28 @@ def bench_decode(args, torch, wkv, synth):
     per = ms / nsteps
     lanes = L * B * C
     algo = 36 * lanes + 8 * L * C
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = host_cores()
+        # one step of layer l (B x C lanes) from the current state, per sample
+        def layer(l):
+            if l >= L:
+                return None
+            a = [t.double().cpu().numpy() for t in (w_all[l], u_all[l], ring[0][0][l:l + 1],
+                                                     ring[0][1][l:l + 1])]
+            kk = a[2].reshape(B, 1, C)
+            vv = a[3].reshape(B, 1, C)
+            s_in = state[l].double().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.forward_scan(a[0], a[1], kk, vv, s_in, nthreads=cores)
+            return B * C, time.perf_counter() - t0
+
+        done, secs, calls = timed_oracle(layer, args.cpu_seconds)
+        cpu = {"value": done / secs / lanes, "unit": "steps/s", "cores": cores, "kind": "oracle",
+               "sample": f"{calls} of the 24 layers (B=1024 C=4096 lanes each) stepped once, "
+                         f"float64, on {cores} threads ({secs:.1f} s), extrapolated per lane-step "
+                         f"to the whole L=24 step"}
     return {"metric": "WKV decode steps/sec, L=24 B=1024 C=4096 fp32", "value": 1e3 / per,
             "unit": "steps/s", "n_gpus": 1, "steps": nsteps, "warmup": args.warmup * 8,
             "ms_per_step": per, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -298,7 +356,8 @@ def bench_decode(args, torch, wkv, synth):
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": algo / (per * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "traffic": measured_traffic("step_kernel<4>", "decode"),
-                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3}}
+                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3},
+            "cpu_baseline": cpu}
 
 
 def bench_stability(args, torch, wkv, synth, backward: bool):
@@ -340,6 +399,30 @@ def bench_stability(args, torch, wkv, synth, backward: bool):
     ms = tm.stop_ms()
     per = ms / n
     wl = "stability_bwd" if backward else "stability_fwd"
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = host_cores()
+
+        def seq(i):  # one sequence (T x C lanes) of the first input set per sample
+            if i >= B:
+                return None
+            st_ = sets[0]
+            a = [st_[n].double().cpu().numpy() for n in ("w", "u")]
+            kk, vv = (st_[n][i:i + 1].double().cpu().numpy() for n in ("k", "v"))
+            t0 = time.perf_counter()
+            if backward:
+                oracle.backward_scan(a[0], a[1], kk, vv, st_["dy"][i:i + 1].double().cpu().numpy(),
+                                     nthreads=cores)
+            else:
+                oracle.forward_scan(a[0], a[1], kk, vv, nthreads=cores)
+            return T * C, time.perf_counter() - t0
+
+        done, secs, calls = timed_oracle(seq, args.cpu_seconds)
+        cpu = {"value": done / secs, "unit": "tok·ch/s", "cores": cores, "kind": "oracle",
+               "sample": f"{calls} of the 8 sequences (T=4096 C=2048 each), float64 O(T) "
+                         f"{'reverse scan' if backward else 'recurrence'} on {cores} threads "
+                         f"({secs:.1f} s)"}
     return {"metric": name, "value": lane_tok / (per * 1e-3), "unit": "tok·ch/s",
             "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": per,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -349,7 +432,8 @@ def bench_stability(args, torch, wkv, synth, backward: bool):
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": algo / (per * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "traffic": measured_traffic(kname, wl),
-                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3}}
+                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3},
+            "cpu_baseline": cpu}
 
 
 def bench_copy(args, torch, wkv, synth):
