@@ -47,8 +47,10 @@ def _load():
         lib.wkvo_backward_brute.argtypes = [i64, i64, i64, D, D, D, D, D, D, D, D, D]
         lib.wkvo_backward_scan.argtypes = [i64, i64, i64, D, D, D, D, D, D, D, D, D,
                                            ctypes.c_int]
+        lib.wkvo_gate.argtypes = [i64, D, D, D]
+        lib.wkvo_token_shift.argtypes = [i64, i64, i64, i64, D, D, D, D, D]
         for f in (lib.wkvo_forward_brute, lib.wkvo_forward_scan, lib.wkvo_backward_brute,
-                  lib.wkvo_backward_scan):
+                  lib.wkvo_backward_scan, lib.wkvo_gate, lib.wkvo_token_shift):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -130,6 +132,41 @@ def backward_scan(w, u, k, v, dy, nthreads: int = 1):
     if rc:
         raise RuntimeError(f"wkvo_backward_scan failed ({rc})")
     return dk, dv, dw, du
+
+
+def gate(y, r):
+    """Receptance gate: sigmoid(r) * y, elementwise, float64."""
+    y, r = _f64(y), _f64(r)
+    if y.shape != r.shape:
+        raise ValueError("y and r must have the same shape")
+    out = np.empty(y.shape)
+    rc = _load().wkvo_gate(int(y.size), _ptr(y), _ptr(r), _ptr(out))
+    if rc:
+        raise RuntimeError(f"wkvo_gate failed ({rc})")
+    return out
+
+
+def token_shift(mu, x, x_prev=None):
+    """Token shift of x [B][T][C] by M weight vectors mu [M][C], with the last
+    token of the previous call x_prev [B][C] (None: zeros).  Returns
+    (out [M][B][T][C], x_prev_out [B][C])."""
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("x must be [B][T][C]")
+    B, T, C = x.shape
+    mu = _f64(mu)
+    if mu.ndim != 2 or mu.shape[1] != C:
+        raise ValueError("mu must be [M][C]")
+    M = mu.shape[0]
+    xp = None if x_prev is None else _f64(x_prev)
+    if xp is not None and xp.shape != (B, C):
+        raise ValueError("x_prev must be [B][C]")
+    out = np.empty((M, B, T, C))
+    xpo = np.empty((B, C))
+    rc = _load().wkvo_token_shift(B, T, C, M, _ptr(mu), _ptr(x), _ptr(xp), _ptr(out), _ptr(xpo))
+    if rc:
+        raise RuntimeError(f"wkvo_token_shift failed ({rc})")
+    return out, xpo
 
 
 def canonical_state(state):

@@ -18,6 +18,14 @@
  *               zero-initialised running sums, bonus only on the current token.
  *   [QuickStart] rwkv-architecture skill page, section "Quick start" (GPT mode
  *               vs RNN mode with the state carried between calls).
+ *   [Block]     RWKV architecture deep dive, section "RWKV architecture
+ *               overview", block figure: the time-mixing output is the
+ *               receptance gate sigmoid(r_t) times wkv_t.
+ *   [Shift]     same article, section "Token shift": the input of each
+ *               projection mixes x_t with x_{t-1} by a per-channel weight mu.
+ *   [States]    rwkv-architecture skill page, "Advanced topics": the
+ *               time-mixing sublayer carries att_x_prev (the last x) between
+ *               calls, beside the WKV state.
  *
  * Conventions (all arrays row-major, float64):
  *   k, v, y, dy, dk, dv : [B][T][C]   (channel fastest)
@@ -35,6 +43,9 @@
  *   wkvo_forward_scan      pinned (brute force, chunking identity)
  *   wkvo_backward_brute    pinned (central finite differences, invariants)
  *   wkvo_backward_scan     pinned (brute-force backward, finite differences)
+ *   wkvo_gate              pinned (library logistic function, limits, r = 0)
+ *   wkvo_token_shift       pinned (hand-computed fixture, mu = 0 and mu = 1
+ *                          limits, chunking identity)
  */
 #include <math.h>
 #include <pthread.h>
@@ -411,5 +422,69 @@ int wkvo_backward_scan(int64_t B, int64_t T, int64_t C, const double *w, const d
     }
     free(dw_lane);
     free(du_lane);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Receptance gate [Block]: out = sigmoid(r) * y, elementwise over n values.  */
+/* ------------------------------------------------------------------------ */
+/*
+ * sigmoid(r) = 1 / (1 + e^{-r}).  For r < 0 the same value is written as
+ * e^{r} / (1 + e^{r}) so that e^{-r} never overflows; both forms are the
+ * logistic function.
+ */
+int wkvo_gate(int64_t n, const double *y, const double *r, double *out) {
+    if (n < 0 || (n > 0 && (!y || !r || !out))) return 1;
+    for (int64_t i = 0; i < n; ++i) {
+        double s;
+        if (r[i] >= 0.0) {
+            s = 1.0 / (1.0 + exp(-r[i]));
+        } else {
+            const double e = exp(r[i]);
+            s = e / (1.0 + e);
+        }
+        out[i] = s * y[i];
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Token shift [Shift], with the carried last token of [States].              */
+/* ------------------------------------------------------------------------ */
+/*
+ * For each of M mixes (one weight vector mu[m][C] per projection input):
+ *     out[m][b][t][c] = mu[m][c] * x[b][t][c] + (1 - mu[m][c]) * x[b][t-1][c]
+ * where x[b][-1][c] is x_prev[b][c], the last token of the previous call, or 0
+ * for a fresh sequence (x_prev == NULL).  x_prev_out[b][c] receives the last
+ * token of this call, x[b][T-1][c], or x_prev (0 when fresh) when T == 0.
+ */
+int wkvo_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const double *mu,
+                     const double *x, const double *x_prev, double *out,
+                     double *x_prev_out) {
+    if (B < 0 || T < 0 || C < 0 || M < 0) return 1;
+    if (B * T * C > 0 && (!x || (M > 0 && (!mu || !out)))) return 1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t c = 0; c < C; ++c) {
+                    const double cur = x[IDX(b, t, c)];
+                    double prev;
+                    if (t > 0)
+                        prev = x[IDX(b, t - 1, c)];
+                    else
+                        prev = x_prev ? x_prev[b * C + c] : 0.0;
+                    const double g = mu[m * C + c];
+                    out[(int64_t)m * B * T * C + IDX(b, t, c)] = g * cur + (1.0 - g) * prev;
+                }
+    if (x_prev_out)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t c = 0; c < C; ++c) {
+                double last;
+                if (T > 0)
+                    last = x[IDX(b, T - 1, c)];
+                else
+                    last = x_prev ? x_prev[b * C + c] : 0.0;
+                x_prev_out[b * C + c] = last;
+            }
     return 0;
 }

@@ -376,3 +376,89 @@ def test_threads_do_not_change_results(oracle):
     g4 = oracle.backward_scan(d["w"], d["u"], d["k"], d["v"], d["dy"], nthreads=4)
     for a, b in zip(g1, g4):
         np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------------- receptance gate, shift ---
+# RWKV architecture deep dive: "RWKV architecture overview" (block figure:
+# the time-mixing output is sigmoid(r_t) * wkv_t) and "Token shift".
+
+def test_gate_is_the_logistic_function(oracle):
+    """sigmoid(r) * y against scipy's logistic function, including the tails
+    where exp(-r) overflows a double."""
+    from scipy.special import expit
+    rng = np.random.default_rng(11)
+    r = np.concatenate([rng.normal(0.0, 3.0, 500), [0.0, 30.0, -30.0, 745.0, -745.0, 1e300,
+                                                     -1e300]])
+    y = rng.normal(0.0, 2.0, r.size)
+    got = oracle.gate(y, r)
+    np.testing.assert_allclose(got, expit(r) * y, rtol=1e-15, atol=1e-300)
+
+
+def test_gate_limits_and_symmetry(oracle):
+    y = np.array([3.0, -1.5, 7.25])
+    np.testing.assert_array_equal(oracle.gate(y, np.zeros(3)), y / 2)      # sigmoid(0) = 1/2
+    np.testing.assert_array_equal(oracle.gate(y, np.full(3, 800.0)), y)     # open gate
+    np.testing.assert_array_equal(oracle.gate(y, np.full(3, -800.0)), 0 * y)  # closed gate
+    r = np.linspace(-20, 20, 81)
+    one = np.ones_like(r)
+    np.testing.assert_allclose(oracle.gate(one, r) + oracle.gate(one, -r), one, rtol=1e-15)
+
+
+def _shift_fixture():
+    rows = {"x": [], "mu": [], "out": {}, "prev": None, "last": None}
+    with open(os.path.join(GOLDEN, "token_shift_worked.txt")) as f:
+        for line in f:
+            p = line.split()
+            if not p or p[0].startswith("#"):
+                continue
+            if p[0] in ("x", "mu"):
+                rows[p[0]].append([float(a) for a in p[1:]])
+            elif p[0] == "out":
+                rows["out"].setdefault(int(p[1]), []).append([float(a) for a in p[2:]])
+            else:
+                rows[p[0]] = [float(a) for a in p[1:]]
+    return rows
+
+
+def test_token_shift_worked_example(oracle):
+    g = _shift_fixture()
+    x = np.array(g["x"])[None]                  # [1][3][2]
+    out, last = oracle.token_shift(np.array(g["mu"]), x, np.array(g["prev"])[None])
+    for m, rows in g["out"].items():
+        np.testing.assert_array_equal(out[m, 0], np.array(rows))
+    np.testing.assert_array_equal(last[0], np.array(g["last"]))
+
+
+def test_token_shift_limits(oracle):
+    """mu = 1 passes x_t through; mu = 0 gives the previous token (the carried
+    one first, zero for a fresh sequence)."""
+    rng = np.random.default_rng(12)
+    x = rng.normal(size=(2, 9, 5))
+    prev = rng.normal(size=(2, 5))
+    mu = np.stack([np.ones(5), np.zeros(5)])
+    for p, first in ((prev, prev), (None, np.zeros((2, 5)))):
+        out, last = oracle.token_shift(mu, x, p)
+        np.testing.assert_array_equal(out[0], x)
+        np.testing.assert_array_equal(out[1][:, 0], first)
+        np.testing.assert_array_equal(out[1][:, 1:], x[:, :-1])
+        np.testing.assert_array_equal(last, x[:, -1])
+
+
+@pytest.mark.parametrize("cuts", [[4, 1, 6], [1] * 11, [11]])
+def test_token_shift_chunking(oracle, cuts):
+    """Calls over chunks with the last token carried equal one call (the
+    state contract of Quick start, applied to the shift's state)."""
+    rng = np.random.default_rng(13)
+    x = rng.normal(size=(3, 11, 4))
+    mu = rng.uniform(0, 1, size=(3, 4))
+    whole, last = oracle.token_shift(mu, x, None)
+    parts, p, t = [], None, 0
+    for n in cuts:
+        o, p = oracle.token_shift(mu, x[:, t:t + n], p)
+        parts.append(o)
+        t += n
+    np.testing.assert_array_equal(np.concatenate(parts, axis=2), whole)
+    np.testing.assert_array_equal(p, last)
+    o, p2 = oracle.token_shift(mu, x[:, :0], p)       # empty call keeps the state
+    assert o.shape == (3, 3, 0, 4)
+    np.testing.assert_array_equal(p2, p)
