@@ -200,6 +200,64 @@ WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *
 /* The plan wkv_forward would use for this shape on the current device. */
 WKV_API wkv_status wkv_forward_plan_auto(int64_t B, int64_t T, int64_t C, wkv_forward_plan *plan);
 
+/*
+ * Time-mixing output gate fused into the forward: y = sigmoid(r) * wkv
+ * elementwise, where wkv is what wkv_forward_ex computes and r is the
+ * receptance.  Cites: RWKV architecture deep dive, section "RWKV architecture
+ * overview" (block figure: the time-mixing output is sigmoid(r_t) * wkv_t).
+ *
+ *   r          [B][T][C]  receptance (before the sigmoid); required when
+ *                         B*T*C > 0; must not overlap y
+ *   all other arguments, the state semantics and the errors as for
+ *   wkv_forward_ex.  The state carried is that of the ungated operator.
+ * The look-back kernel is compiled for the gate only with seg_len <= 16: an
+ * explicit look-back plan with a longer seg_len returns WKV_ERR_UNSUPPORTED,
+ * and the automatic choice stays within the compiled variants.
+ */
+WKV_API wkv_status wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w,
+                                     const float *u, const float *k, const float *v,
+                                     const float *r, float *y, const float *state_in,
+                                     float *state_out, const wkv_forward_plan *plan,
+                                     hipStream_t stream);
+
+/*
+ * wkv_step with the same gate: y = sigmoid(r) * wkv for every (layer,
+ * sequence, channel).  Cites: as wkv_forward_gated and wkv_step.
+ *   r          [L][B][C]  required when L*B*C > 0; must not overlap y
+ * Other arguments and errors as for wkv_step.
+ */
+WKV_API wkv_status wkv_step_gated(int64_t L, int64_t B, int64_t C, const float *w,
+                                  const float *u, const float *k, const float *v,
+                                  const float *r, float *y, const float *state_in,
+                                  float *state_out, hipStream_t stream);
+
+/* Largest number of mixes wkv_token_shift takes in one call. */
+#define WKV_TOKEN_SHIFT_MAX_MIXES 8
+
+/*
+ * Token shift of the time-mixing block, for M projection inputs at once:
+ *   out[m][b][t][c] = mu[m][c] * x[b][t][c] + (1 - mu[m][c]) * x[b][t-1][c]
+ * where x[b][-1][c] is x_prev[b][c], the last token of the previous call (the
+ * att_x_prev state), or 0 for a fresh sequence (x_prev NULL).  Cites: RWKV
+ * architecture deep dive, section "Token shift" (the mix, per-channel mu);
+ * rwkv-architecture skill page, "Advanced topics" (att_x_prev is carried
+ * between calls like the WKV state).
+ *
+ *   mu          [M][C]      mix weights; required when M*C > 0
+ *   x           [B][T][C]   input tokens; required when B*T*C > 0
+ *   x_prev      [B][C]      or NULL (zeros)
+ *   out         [M][B][T][C] output, fully overwritten; required when M*B*T*C > 0;
+ *                           must not overlap any other argument
+ *   x_prev_out  [B][C]      receives x[b][T-1] (x_prev, or zeros, when T == 0),
+ *                           or NULL to discard it; may equal x_prev (in place)
+ *                           but may not overlap it partially, nor x, mu or out
+ * 0 <= M <= WKV_TOKEN_SHIFT_MAX_MIXES, else WKV_ERR_UNSUPPORTED.  Other errors
+ * as for wkv_forward.
+ */
+WKV_API wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const float *mu,
+                                   const float *x, const float *x_prev, float *out,
+                                   float *x_prev_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwkv.so")
 SOURCES = ["wkv_api.hip", "wkv_forward.hip", "wkv_lookback.hip", "wkv_step.hip",
-           "wkv_backward.hip"]
+           "wkv_backward.hip", "wkv_shift.hip"]
 ARCH = "gfx950"
 
 

@@ -137,9 +137,23 @@ wkv_forward_plan auto_plan(int64_t B, int64_t T, int64_t C, int cus) {
     return wkv_forward_plan{WKV_KERNEL_LOOKBACK, 4, ls, 64};
 }
 
+// The automatic plan for the gated forward: the same choice, kept within the
+// variants compiled with the gate (look-back blocks of the same length, cut
+// into segments of at most 16 tokens).
+wkv_forward_plan gated_plan(wkv_forward_plan p) {
+    if (p.kernel == WKV_KERNEL_LOOKBACK && p.seg_len > 16) {
+        p.segments = p.segments * p.seg_len / 16;
+        p.seg_len = 16;
+        if (!wkv::forward_lookback_supported(p.channels / 64, p.segments, p.seg_len, true))
+            p = wkv_forward_plan{WKV_KERNEL_LOOKBACK, 8, 16, 64};
+    }
+    return p;
+}
+
+// r: the gate's receptance (same layout as k), NULL for the plain forward.
 wkv_status check_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                          const float *k, const float *v, const float *y, const float *s_in,
-                         const float *s_out) {
+                         const float *s_out, const float *r = nullptr, bool gated = false) {
     if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
     const int64_t seq = bytes_of(B, T, C);
     const int64_t st = bytes_of(3, B, C);
@@ -147,18 +161,114 @@ wkv_status check_forward(int64_t B, int64_t T, int64_t C, const float *w, const 
     if (seq < 0 || st < 0 || ch < 0) return WKV_ERR_OVERFLOW;
     if (B * C > 0 && (!w || !u)) return WKV_ERR_NULL;
     if (seq > 0 && (!k || !v || !y)) return WKV_ERR_NULL;
+    if (gated && seq > 0 && !r) return WKV_ERR_NULL;
     const Range rw = rng(w, B * C > 0 ? ch : 0), ru = rng(u, B * C > 0 ? ch : 0);
     const Range rk = rng(k, seq), rv = rng(v, seq), ry = rng(y, seq);
-    const Range ri = rng(s_in, st), ro = rng(s_out, st);
-    for (Range r : {rw, ru, rk, rv, ri, ro})
-        if (overlap(ry, r)) return WKV_ERR_ALIAS;
-    for (Range r : {rw, ru, rk, rv})
-        if (overlap(ro, r)) return WKV_ERR_ALIAS;
+    const Range ri = rng(s_in, st), ro = rng(s_out, st), rr = rng(r, seq);
+    for (Range x : {rw, ru, rk, rv, ri, ro, rr})
+        if (overlap(ry, x)) return WKV_ERR_ALIAS;
+    for (Range x : {rw, ru, rk, rv, rr})
+        if (overlap(ro, x)) return WKV_ERR_ALIAS;
     if (overlap(ro, ri) && s_out != (float *)s_in) return WKV_ERR_ALIAS;
     return WKV_OK;
 }
 
 wkv_status from_hip(hipError_t e) { return e == hipSuccess ? WKV_OK : WKV_ERR_HIP; }
+
+// wkv_forward_ex and wkv_forward_gated: r is NULL for the plain forward.
+wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                        const float *k, const float *v, const float *r, float *y,
+                        const float *state_in, float *state_out, const wkv_forward_plan *plan,
+                        bool gated, hipStream_t stream) {
+    wkv_status st = check_forward(B, T, C, w, u, k, v, y, state_in, state_out, r, gated);
+    if (st != WKV_OK) return st;
+    wkv_forward_plan p{WKV_KERNEL_AUTO, 0, 0, 0};
+    if (plan) p = *plan;
+    switch (p.kernel) {
+        case WKV_KERNEL_AUTO:
+        case WKV_KERNEL_LANE:
+            if (p.channels != 0) return WKV_ERR_UNSUPPORTED;
+            break;
+        case WKV_KERNEL_SEGMENTED:
+            if (p.segments == 0) p.segments = 16;
+            if (p.seg_len == 0) p.seg_len = 16;
+            if (p.channels == 0) p.channels = 64;
+            if (!wkv::forward_seg_supported(p.segments, p.seg_len, p.channels))
+                return WKV_ERR_UNSUPPORTED;
+            break;
+        case WKV_KERNEL_LOOKBACK:
+            if (p.segments == 0) p.segments = 4;
+            if (p.seg_len == 0) p.seg_len = 16;
+            if (p.channels == 0) p.channels = 64;
+            if (p.channels % 64 != 0 ||
+                !wkv::forward_lookback_supported(p.channels / 64, p.segments, p.seg_len, gated))
+                return WKV_ERR_UNSUPPORTED;
+            break;
+        default:
+            return WKV_ERR_UNSUPPORTED;
+    }
+    const int64_t lanes = B * C;
+    if (lanes == 0) return WKV_OK;
+    if (T == 0) {
+        if (!state_out || state_out == state_in) return WKV_OK;
+        return from_hip(wkv::launch_state_copy(lanes, state_in, state_out, stream));
+    }
+    // The look-back kernel tags what it publishes with a per-launch epoch that
+    // the host advances; a captured graph would replay one epoch forever, so
+    // under stream capture the segmented kernel (no state across workgroups)
+    // runs instead, and an explicit look-back plan is refused.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (stream != nullptr && hipStreamIsCapturing(stream, &cap) != hipSuccess)
+        return WKV_ERR_HIP;
+    const bool capturing = cap != hipStreamCaptureStatusNone;
+    if (p.kernel == WKV_KERNEL_AUTO) {
+        p = auto_plan(B, T, C, device_cus());
+        if (gated) p = gated_plan(p);
+        if (capturing && p.kernel == WKV_KERNEL_LOOKBACK)
+            p = wkv_forward_plan{WKV_KERNEL_SEGMENTED, 16, 16, 64};
+    } else if (capturing && p.kernel == WKV_KERNEL_LOOKBACK) {
+        return WKV_ERR_UNSUPPORTED;
+    }
+    const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr};
+    if (p.kernel == WKV_KERNEL_LANE) {
+        if ((lanes + 255) / 256 > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
+        return from_hip(wkv::launch_forward_lane(a, stream));
+    }
+    if (p.kernel == WKV_KERNEL_LOOKBACK) {
+        const int cg = p.channels / 64;
+        if (!wkv::lookback_grid_ok(B, T, C, cg, p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
+        const size_t need = wkv::lookback_scratch_bytes(B, T, C, p.segments, p.seg_len);
+        if (need > kLookbackScratchMax) return WKV_ERR_UNSUPPORTED;
+        return from_hip(launch_with_scratch(a, cg, p.segments, p.seg_len, need, stream));
+    }
+    if (B * ((C + p.channels - 1) / p.channels) > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
+    return from_hip(wkv::launch_forward_seg(a, p.segments, p.seg_len, p.channels, stream));
+}
+
+// wkv_step and wkv_step_gated: r is NULL for the plain step.
+wkv_status step_impl(int64_t L, int64_t B, int64_t C, const float *w, const float *u,
+                     const float *k, const float *v, const float *r, float *y,
+                     const float *state_in, float *state_out, bool gated, hipStream_t stream) {
+    if (L < 0 || B < 0 || C < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(L, B, C);
+    const int64_t st = bytes_of(3 * L, B, C);
+    const int64_t ch = bytes_of(L, 1, C);
+    if (seq < 0 || st < 0 || ch < 0 || L > INT64_MAX / 3) return WKV_ERR_OVERFLOW;
+    if (seq == 0) return WKV_OK;
+    if (!w || !u || !k || !v || !y || !state_in || !state_out) return WKV_ERR_NULL;
+    if (gated && !r) return WKV_ERR_NULL;
+    const Range rw = rng(w, ch), ru = rng(u, ch), rk = rng(k, seq), rv = rng(v, seq),
+                ry = rng(y, seq), ri = rng(state_in, st), ro = rng(state_out, st),
+                rr = rng(r, seq);
+    for (Range x : {rw, ru, rk, rv, ri, ro, rr})
+        if (overlap(ry, x)) return WKV_ERR_ALIAS;
+    for (Range x : {rw, ru, rk, rv, rr})
+        if (overlap(ro, x)) return WKV_ERR_ALIAS;
+    if (overlap(ro, ri) && state_out != (float *)state_in) return WKV_ERR_ALIAS;
+    if (L * B > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
+    const StepArgs a{L, B, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr};
+    return from_hip(wkv::launch_step(a, stream));
+}
 
 }  // namespace
 
@@ -190,67 +300,16 @@ WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *
                                   const float *k, const float *v, float *y,
                                   const float *state_in, float *state_out,
                                   const wkv_forward_plan *plan, hipStream_t stream) {
-    wkv_status st = check_forward(B, T, C, w, u, k, v, y, state_in, state_out);
-    if (st != WKV_OK) return st;
-    wkv_forward_plan p{WKV_KERNEL_AUTO, 0, 0, 0};
-    if (plan) p = *plan;
-    switch (p.kernel) {
-        case WKV_KERNEL_AUTO:
-        case WKV_KERNEL_LANE:
-            if (p.channels != 0) return WKV_ERR_UNSUPPORTED;
-            break;
-        case WKV_KERNEL_SEGMENTED:
-            if (p.segments == 0) p.segments = 16;
-            if (p.seg_len == 0) p.seg_len = 16;
-            if (p.channels == 0) p.channels = 64;
-            if (!wkv::forward_seg_supported(p.segments, p.seg_len, p.channels))
-                return WKV_ERR_UNSUPPORTED;
-            break;
-        case WKV_KERNEL_LOOKBACK:
-            if (p.segments == 0) p.segments = 4;
-            if (p.seg_len == 0) p.seg_len = 16;
-            if (p.channels == 0) p.channels = 64;
-            if (p.channels % 64 != 0 ||
-                !wkv::forward_lookback_supported(p.channels / 64, p.segments, p.seg_len))
-                return WKV_ERR_UNSUPPORTED;
-            break;
-        default:
-            return WKV_ERR_UNSUPPORTED;
-    }
-    const int64_t lanes = B * C;
-    if (lanes == 0) return WKV_OK;
-    if (T == 0) {
-        if (!state_out || state_out == state_in) return WKV_OK;
-        return from_hip(wkv::launch_state_copy(lanes, state_in, state_out, stream));
-    }
-    // The look-back kernel tags what it publishes with a per-launch epoch that
-    // the host advances; a captured graph would replay one epoch forever, so
-    // under stream capture the segmented kernel (no state across workgroups)
-    // runs instead, and an explicit look-back plan is refused.
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (stream != nullptr && hipStreamIsCapturing(stream, &cap) != hipSuccess)
-        return WKV_ERR_HIP;
-    const bool capturing = cap != hipStreamCaptureStatusNone;
-    if (p.kernel == WKV_KERNEL_AUTO) {
-        p = auto_plan(B, T, C, device_cus());
-        if (capturing && p.kernel == WKV_KERNEL_LOOKBACK) p = wkv_forward_plan{WKV_KERNEL_SEGMENTED, 16, 16, 64};
-    } else if (capturing && p.kernel == WKV_KERNEL_LOOKBACK) {
-        return WKV_ERR_UNSUPPORTED;
-    }
-    const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out};
-    if (p.kernel == WKV_KERNEL_LANE) {
-        if ((lanes + 255) / 256 > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
-        return from_hip(wkv::launch_forward_lane(a, stream));
-    }
-    if (p.kernel == WKV_KERNEL_LOOKBACK) {
-        const int cg = p.channels / 64;
-        if (!wkv::lookback_grid_ok(B, T, C, cg, p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
-        const size_t need = wkv::lookback_scratch_bytes(B, T, C, p.segments, p.seg_len);
-        if (need > kLookbackScratchMax) return WKV_ERR_UNSUPPORTED;
-        return from_hip(launch_with_scratch(a, cg, p.segments, p.seg_len, need, stream));
-    }
-    if (B * ((C + p.channels - 1) / p.channels) > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
-    return from_hip(wkv::launch_forward_seg(a, p.segments, p.seg_len, p.channels, stream));
+    return forward_impl(B, T, C, w, u, k, v, nullptr, y, state_in, state_out, plan, false,
+                        stream);
+}
+
+WKV_API wkv_status wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w,
+                                     const float *u, const float *k, const float *v,
+                                     const float *r, float *y, const float *state_in,
+                                     float *state_out, const wkv_forward_plan *plan,
+                                     hipStream_t stream) {
+    return forward_impl(B, T, C, w, u, k, v, r, y, state_in, state_out, plan, true, stream);
 }
 
 WKV_API wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -262,23 +321,40 @@ WKV_API wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, 
 WKV_API wkv_status wkv_step(int64_t L, int64_t B, int64_t C, const float *w, const float *u,
                             const float *k, const float *v, float *y, const float *state_in,
                             float *state_out, hipStream_t stream) {
-    if (L < 0 || B < 0 || C < 0) return WKV_ERR_DIM;
-    const int64_t seq = bytes_of(L, B, C);
-    const int64_t st = bytes_of(3 * L, B, C);
-    const int64_t ch = bytes_of(L, 1, C);
-    if (seq < 0 || st < 0 || ch < 0 || L > INT64_MAX / 3) return WKV_ERR_OVERFLOW;
-    if (seq == 0) return WKV_OK;
-    if (!w || !u || !k || !v || !y || !state_in || !state_out) return WKV_ERR_NULL;
-    const Range rw = rng(w, ch), ru = rng(u, ch), rk = rng(k, seq), rv = rng(v, seq),
-                ry = rng(y, seq), ri = rng(state_in, st), ro = rng(state_out, st);
-    for (Range r : {rw, ru, rk, rv, ri, ro})
-        if (overlap(ry, r)) return WKV_ERR_ALIAS;
-    for (Range r : {rw, ru, rk, rv})
-        if (overlap(ro, r)) return WKV_ERR_ALIAS;
-    if (overlap(ro, ri) && state_out != (float *)state_in) return WKV_ERR_ALIAS;
-    if (L * B > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
-    const StepArgs a{L, B, C, w, u, k, v, y, state_in, state_out};
-    return from_hip(wkv::launch_step(a, stream));
+    return step_impl(L, B, C, w, u, k, v, nullptr, y, state_in, state_out, false, stream);
+}
+
+WKV_API wkv_status wkv_step_gated(int64_t L, int64_t B, int64_t C, const float *w,
+                                  const float *u, const float *k, const float *v,
+                                  const float *r, float *y, const float *state_in,
+                                  float *state_out, hipStream_t stream) {
+    return step_impl(L, B, C, w, u, k, v, r, y, state_in, state_out, true, stream);
+}
+
+WKV_API wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const float *mu,
+                                   const float *x, const float *x_prev, float *out,
+                                   float *x_prev_out, hipStream_t stream) {
+    if (B < 0 || T < 0 || C < 0 || M < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(B, T, C);
+    const int64_t lanes = bytes_of(1, B, C);
+    const int64_t mus = bytes_of(M, 1, C);
+    const int64_t outs = seq < 0 ? -1 : bytes_of(M, 1, seq, 1);
+    if (seq < 0 || lanes < 0 || mus < 0 || outs < 0) return WKV_ERR_OVERFLOW;
+    if (M > WKV_TOKEN_SHIFT_MAX_MIXES) return WKV_ERR_UNSUPPORTED;
+    if (lanes == 0) return WKV_OK;
+    if (seq > 0 && !x) return WKV_ERR_NULL;
+    if (outs > 0 && (!mu || !out)) return WKV_ERR_NULL;
+    const Range rmu = rng(mu, seq > 0 ? mus : 0), rx = rng(x, seq), rp = rng(x_prev, lanes);
+    const Range ro = rng(out, outs), rpo = rng(x_prev_out, lanes);
+    for (Range q : {rmu, rx, rp, rpo})
+        if (overlap(ro, q)) return WKV_ERR_ALIAS;
+    for (Range q : {rmu, rx})
+        if (overlap(rpo, q)) return WKV_ERR_ALIAS;
+    if (overlap(rpo, rp) && x_prev_out != (float *)x_prev) return WKV_ERR_ALIAS;
+    if (!x_prev_out && outs == 0) return WKV_OK;
+    const wkv::ShiftArgs a{B, T, C, M, mu, x, x_prev, out, x_prev_out};
+    const bool in_place = x_prev_out != nullptr && x_prev_out == (float *)x_prev;
+    return from_hip(wkv::launch_token_shift(a, in_place, stream));
 }
 
 WKV_API size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {

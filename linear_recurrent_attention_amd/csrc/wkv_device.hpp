@@ -247,6 +247,11 @@ struct TileRows {
     static constexpr int kNT = 2;
 };
 
+// Receptance gate of the time-mixing block (RWKV architecture deep dive,
+// "RWKV architecture overview", block figure): sigmoid(r) = 1 / (1 + 2^{-r log2 e}).
+// The tails saturate cleanly: 2^{+large} = inf gives 0, 2^{-large} = 0 gives 1.
+__device__ __forceinline__ float gate_of(float r) { return rcp(1.0f + ex2(-r * kLog2e)); }
+
 // ABI state (natural-log exponent) -> kernel exponent (log2), mapping -inf and
 // anything below the empty sentinel onto it.
 __device__ __forceinline__ float o_in(float o_nat) { return fmaxf(o_nat * kLog2e, kEmpty2); }

@@ -4,7 +4,9 @@
 // core computation", with the state of "Numerical stability via log-space
 // computation" carried in and out as in the rwkv-architecture skill page,
 // "Quick start"): for each lane (b, c), y[b][t][c] for t = 0..T-1 and the state
-// after the last token.
+// after the last token.  Given a receptance tensor r (layout of k), every
+// kernel stores the time-mixing block's gated output sigmoid(r) * wkv instead
+// (block figure of "RWKV architecture overview"); r is read with k and v.
 //
 // Two kernels:
 //   fwd_lane_kernel  one thread per lane, sequential over T.  Each wave reads
@@ -30,30 +32,43 @@ namespace wkv {
 // ---------------------------------------------------------------------------
 // One thread per lane.
 // ---------------------------------------------------------------------------
-template <bool SAFE>
+// GATE: y = sigmoid(r) * wkv with r read beside k and v.
+template <bool SAFE, bool GATE>
 __device__ __forceinline__ void lane_sweep(int64_t T, int64_t C, const float *__restrict__ kp,
-                                           const float *__restrict__ vp, float *__restrict__ yp,
+                                           const float *__restrict__ vp,
+                                           const float *__restrict__ rp, float *__restrict__ yp,
                                            Lane &L, const Chan &ch) {
     int64_t t = 0;
     constexpr int U8 = 8;
     for (; t + U8 <= T; t += U8) {
-        float K[U8], V[U8];
+        float K[U8], V[U8], R[U8];
 #pragma unroll
         for (int j = 0; j < U8; ++j) {
             K[j] = kp[(t + j) * C];
             V[j] = vp[(t + j) * C];
+            if constexpr (GATE) R[j] = rp[(t + j) * C];
         }
 #pragma unroll
-        for (int j = 0; j < U8; ++j) yp[(t + j) * C] = step<SAFE>(L, K[j] * kLog2e, V[j], ch);
+        for (int j = 0; j < U8; ++j) {
+            float yv = step<SAFE>(L, K[j] * kLog2e, V[j], ch);
+            if constexpr (GATE) yv *= gate_of(R[j]);
+            yp[(t + j) * C] = yv;
+        }
     }
-    for (; t < T; ++t) yp[t * C] = step<SAFE>(L, kp[t * C] * kLog2e, vp[t * C], ch);
+    for (; t < T; ++t) {
+        float yv = step<SAFE>(L, kp[t * C] * kLog2e, vp[t * C], ch);
+        if constexpr (GATE) yv *= gate_of(rp[t * C]);
+        yp[t * C] = yv;
+    }
 }
 
+template <bool GATE>
 __global__ __launch_bounds__(256) void fwd_lane_kernel(int64_t B, int64_t T, int64_t C,
                                                        const float *__restrict__ w,
                                                        const float *__restrict__ u,
                                                        const float *__restrict__ k,
                                                        const float *__restrict__ v,
+                                                       const float *__restrict__ r,
                                                        float *__restrict__ y,
                                                        const float *__restrict__ s_in,
                                                        float *__restrict__ s_out) {
@@ -70,10 +85,11 @@ __global__ __launch_bounds__(256) void fwd_lane_kernel(int64_t B, int64_t T, int
         L = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
                     o_in(s_in[(2 * B + bb) * C + c]));
     const int64_t base = bb * T * C + c;
+    const float *rp = GATE ? r + base : nullptr;
     if (wave_fast)
-        lane_sweep<false>(T, C, k + base, v + base, y + base, L, ch);
+        lane_sweep<false, GATE>(T, C, k + base, v + base, rp, y + base, L, ch);
     else
-        lane_sweep<true>(T, C, k + base, v + base, y + base, L, ch);
+        lane_sweep<true, GATE>(T, C, k + base, v + base, rp, y + base, L, ch);
     if (s_out) {
         s_out[(0 * B + bb) * C + c] = L.a;
         s_out[(1 * B + bb) * C + c] = L.b;
@@ -128,6 +144,14 @@ __device__ __forceinline__ void seg_load(float (&K)[LS], float (&V)[LS], const T
     }
 }
 
+// The same rows of the gate's receptance.
+template <int LS, bool FULL>
+__device__ __forceinline__ void seg_load_r(float (&R)[LS], const TileRows &rr, int64_t t0,
+                                           int64_t T) {
+#pragma unroll
+    for (int j = 0; j < LS; ++j) R[j] = (FULL || t0 + j < T) ? rr.ld(j) : 0.0f;
+}
+
 // Per-lane geometry of the segmented kernel.
 template <int NW, int LS, int CW>
 struct SegGeom {
@@ -143,9 +167,9 @@ struct SegGeom {
 // One tile: this lane's LS tokens of k, v are in registers (K, V); `carry` is
 // the state before the tile and leaves as the state after it.  FULL: T is a
 // whole number of tiles, so no token test is needed (straight-line code).
-template <int NW, int LS, int CW, bool SAFE, bool FULL>
+template <int NW, int LS, int CW, bool SAFE, bool FULL, bool GATE>
 __device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], const float (&V)[LS],
-                                         Lane &carry, const SegGeom<NW, LS, CW> &G, int64_t B,
+                                         const float (&Rg)[GATE ? LS : 1], Lane &carry, const SegGeom<NW, LS, CW> &G, int64_t B,
                                          int64_t T, int64_t C, int64_t bb, int64_t c, bool active,
                                          const Chan &ch, float *yseq, uint32_t voff,
                                          float *__restrict__ s_out, SegShared<NW> &sh) {
@@ -191,14 +215,16 @@ __device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], con
     if (FULL || t0 + LS <= T) {
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
-            const float yv = step<SAFE>(R, K[j] * kLog2e, V[j], ch);
+            float yv = step<SAFE>(R, K[j] * kLog2e, V[j], ch);
+            if constexpr (GATE) yv *= gate_of(Rg[j]);
             if (active) yr.st(j, yv);
         }
     } else {
 #pragma unroll
         for (int j = 0; j < LS; ++j)
             if (t0 + j < T) {
-                const float yv = step<SAFE>(R, K[j] * kLog2e, V[j], ch);
+                float yv = step<SAFE>(R, K[j] * kLog2e, V[j], ch);
+                if constexpr (GATE) yv *= gate_of(Rg[j]);
                 if (active) yr.st(j, yv);
             }
     }
@@ -214,21 +240,35 @@ __device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], con
 // next tile's k, v loaded while the current one is processed.  Two register
 // sets take turns (A holds even tiles, B odd ones) so that no register copy
 // ties a prefetch to the current tile's arithmetic.
-template <int NW, int LS, int CW, bool SAFE, bool FULL>
+template <int NW, int LS, int CW, bool SAFE, bool FULL, bool GATE>
 __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_t bb, int64_t c,
                                          bool active, const Chan &ch,
                                          const SegGeom<NW, LS, CW> &G, const float *kseq,
-                                         const float *vseq, float *yseq, uint32_t voff,
+                                         const float *vseq, const float *rseq, float *yseq,
+                                         uint32_t voff,
                                          const float *__restrict__ s_in, float *__restrict__ s_out,
                                          SegShared<NW> &sh) {
     using Geo = SegGeom<NW, LS, CW>;
     const int64_t ntiles = (T + Geo::TT - 1) / Geo::TT;
     const uint32_t rowb = (uint32_t)(C * 4);
+    constexpr int NR = GATE ? LS : 1;
     auto load = [&](float (&K)[LS], float (&V)[LS], int64_t tile) {
         const int64_t tw = tile * Geo::TT + (int64_t)G.wave * Geo::SPW * LS;
         seg_load<LS, FULL>(K, V, TileRows(kseq + tw * C, voff, rowb),
                            TileRows(vseq + tw * C, voff, rowb),
                            tile * Geo::TT + (int64_t)G.seg * LS, T);
+    };
+    // The receptance of a tile is loaded just before the next tile's k and v:
+    // loads complete in order, so waiting for it in the re-sweep leaves that
+    // prefetch in flight, and one register set suffices.
+    auto load_r = [&](float (&R)[NR], int64_t tile) {
+        if constexpr (GATE) {
+            const int64_t tw = tile * Geo::TT + (int64_t)G.wave * Geo::SPW * LS;
+            seg_load_r<LS, FULL>(R, TileRows(rseq + tw * C, voff, rowb),
+                                 tile * Geo::TT + (int64_t)G.seg * LS, T);
+        } else {
+            R[0] = 0.0f;
+        }
     };
 
     // carry: the state before the current tile
@@ -237,28 +277,33 @@ __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_
         carry = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
                         o_in(s_in[(2 * B + bb) * C + c]));
 
-    float KA[LS], VA[LS], KB[LS], VB[LS];
+    float KA[LS], VA[LS], KB[LS], VB[LS], Rc[NR];
     load(KA, VA, 0);
     int64_t tile = 0;
     for (; tile + 1 < ntiles; tile += 2) {
+        load_r(Rc, tile);
         load(KB, VB, tile + 1);
-        seg_tile<NW, LS, CW, SAFE, FULL>(tile, KA, VA, carry, G, B, T, C, bb, c, active, ch, yseq,
-                                         voff, s_out, sh);
+        seg_tile<NW, LS, CW, SAFE, FULL, GATE>(tile, KA, VA, Rc, carry, G, B, T, C, bb, c, active,
+                                               ch, yseq, voff, s_out, sh);
+        load_r(Rc, tile + 1);
         if (tile + 2 < ntiles) load(KA, VA, tile + 2);
-        seg_tile<NW, LS, CW, SAFE, FULL>(tile + 1, KB, VB, carry, G, B, T, C, bb, c, active, ch,
-                                         yseq, voff, s_out, sh);
+        seg_tile<NW, LS, CW, SAFE, FULL, GATE>(tile + 1, KB, VB, Rc, carry, G, B, T, C, bb, c,
+                                               active, ch, yseq, voff, s_out, sh);
     }
-    if (tile < ntiles)
-        seg_tile<NW, LS, CW, SAFE, FULL>(tile, KA, VA, carry, G, B, T, C, bb, c, active, ch, yseq,
-                                         voff, s_out, sh);
+    if (tile < ntiles) {
+        load_r(Rc, tile);
+        seg_tile<NW, LS, CW, SAFE, FULL, GATE>(tile, KA, VA, Rc, carry, G, B, T, C, bb, c, active,
+                                               ch, yseq, voff, s_out, sh);
+    }
 }
 
-template <int NW, int LS, int CW>
+template <int NW, int LS, int CW, bool GATE>
 __global__ __launch_bounds__(NW * 64) void fwd_seg_kernel(int64_t B, int64_t T, int64_t C,
                                                           const float *__restrict__ w,
                                                           const float *__restrict__ u,
                                                           const float *__restrict__ k,
                                                           const float *__restrict__ v,
+                                                          const float *__restrict__ r,
                                                           float *__restrict__ y,
                                                           const float *__restrict__ s_in,
                                                           float *__restrict__ s_out) {
@@ -285,18 +330,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_seg_kernel(int64_t B, int64_t T, 
     const uint32_t voff = (active ? (uint32_t)ch_local * 4u : 0u) +
                           (uint32_t)(G.lane / CW) * (uint32_t)LS * (uint32_t)(C * 4);
     const bool full = T % Geo::TT == 0;
+    const float *rs = GATE ? r + base : nullptr;
     if (fast && full)
-        seg_body<NW, LS, CW, false, true>(B, T, C, bb, c, active, ch, G, k + base, v + base,
-                                          y + base, voff, s_in, s_out, sh);
+        seg_body<NW, LS, CW, false, true, GATE>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+                                                rs, y + base, voff, s_in, s_out, sh);
     else if (fast)
-        seg_body<NW, LS, CW, false, false>(B, T, C, bb, c, active, ch, G, k + base, v + base,
-                                           y + base, voff, s_in, s_out, sh);
+        seg_body<NW, LS, CW, false, false, GATE>(B, T, C, bb, c, active, ch, G, k + base,
+                                                 v + base, rs, y + base, voff, s_in, s_out, sh);
     else if (full)
-        seg_body<NW, LS, CW, true, true>(B, T, C, bb, c, active, ch, G, k + base, v + base,
-                                         y + base, voff, s_in, s_out, sh);
+        seg_body<NW, LS, CW, true, true, GATE>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+                                               rs, y + base, voff, s_in, s_out, sh);
     else
-        seg_body<NW, LS, CW, true, false>(B, T, C, bb, c, active, ch, G, k + base, v + base,
-                                          y + base, voff, s_in, s_out, sh);
+        seg_body<NW, LS, CW, true, false, GATE>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+                                                rs, y + base, voff, s_in, s_out, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -320,16 +366,26 @@ __global__ __launch_bounds__(256) void state_copy_kernel(int64_t n, const float 
 hipError_t launch_forward_lane(const FwdArgs &a, hipStream_t st) {
     const int64_t lanes = a.B * a.C;
     const int64_t grid = (lanes + 255) / 256;
-    hipLaunchKernelGGL(fwd_lane_kernel, dim3((unsigned)grid), dim3(256), 0, st, a.B, a.T, a.C,
-                       a.w, a.u, a.k, a.v, a.y, a.s_in, a.s_out);
+    if (a.r)
+        hipLaunchKernelGGL(fwd_lane_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st, a.B,
+                           a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y, a.s_in, a.s_out);
+    else
+        hipLaunchKernelGGL(fwd_lane_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st, a.B,
+                           a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y, a.s_in, a.s_out);
     return hipGetLastError();
 }
 
 template <int NW, int LS, int CW>
 static hipError_t launch_seg(const FwdArgs &a, hipStream_t st) {
     const int64_t grid = a.B * ((a.C + CW - 1) / CW);
-    hipLaunchKernelGGL((fwd_seg_kernel<NW, LS, CW>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
-                       a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.y, a.s_in, a.s_out);
+    if (a.r)
+        hipLaunchKernelGGL((fwd_seg_kernel<NW, LS, CW, true>), dim3((unsigned)grid),
+                           dim3(NW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y,
+                           a.s_in, a.s_out);
+    else
+        hipLaunchKernelGGL((fwd_seg_kernel<NW, LS, CW, false>), dim3((unsigned)grid),
+                           dim3(NW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y,
+                           a.s_in, a.s_out);
     return hipGetLastError();
 }
 

@@ -8,12 +8,15 @@
 
 namespace wkv {
 
+// r: receptance of the time-mixing gate, same layout as k; NULL: y = wkv,
+// else y = sigmoid(r) * wkv.
 struct FwdArgs {
     int64_t B, T, C;
     const float *w, *u, *k, *v;
     float *y;
     const float *s_in;
     float *s_out;
+    const float *r;
 };
 
 struct StepArgs {
@@ -22,6 +25,13 @@ struct StepArgs {
     float *y;
     const float *s_in;
     float *s_out;
+    const float *r;
+};
+
+struct ShiftArgs {
+    int64_t B, T, C, M;
+    const float *mu, *x, *x_prev;
+    float *out, *x_prev_out;
 };
 
 struct BwdArgs {
@@ -44,7 +54,8 @@ struct LookbackScratch {
 };
 // (cg, ns, ls): groups of 64 channels side by side, segments stacked, tokens
 // per segment
-bool forward_lookback_supported(int cg, int ns, int ls);
+// (the gated kernel is compiled for the variants with ls <= 16 only)
+bool forward_lookback_supported(int cg, int ns, int ls, bool gated);
 bool lookback_grid_ok(int64_t B, int64_t T, int64_t C, int cg, int ns, int ls);
 size_t lookback_scratch_bytes(int64_t B, int64_t T, int64_t C, int ns, int ls);
 hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,
@@ -52,6 +63,10 @@ hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,
 
 // step (wkv_step.hip)
 hipError_t launch_step(const StepArgs &a, hipStream_t st);
+
+// token shift (wkv_shift.hip); largest number of mixes per call
+constexpr int64_t kMaxMixes = 8;
+hipError_t launch_token_shift(const ShiftArgs &a, bool in_place_state, hipStream_t st);
 
 // backward (wkv_backward.hip)
 size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);

@@ -114,9 +114,11 @@ struct LbWave {
 
 // FULL: the whole block lies inside the sequence, so no token needs a bounds
 // test (a workgroup-uniform property: only the last block can be partial).
-template <int CG, int NS, int LS, bool SAFE, bool FULL>
+// GATE: Rg holds the wave's receptance rows and y is sigmoid(r) * wkv.
+template <int CG, int NS, int LS, bool SAFE, bool FULL, bool GATE>
 __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const Chan &ch,
                                         const LbWave &q, const float (&K)[LS], const float (&V)[LS],
+                                        const float (&Rg)[GATE ? LS : 1],
                                         float *yseq, const float *__restrict__ s_in,
                                         float *__restrict__ s_out, Word *aggs, Word *incls,
                                         uint32_t epoch, LbShared<CG, NS> &sh) {
@@ -246,8 +248,8 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
                 float A = f.alpha, Bs = f.beta;
 #pragma unroll
                 for (int t = 0; t < LS; ++t) {
-                    const float yv =
-                        frame_token(A, Bs, f, K[t], V[t], (float)(LS - 1 - t), ch) + poison;
+                    float yv = frame_token(A, Bs, f, K[t], V[t], (float)(LS - 1 - t), ch) + poison;
+                    if constexpr (GATE) yv *= gate_of(Rg[t]);
                     if (q.active) yr.st(t, yv);
                 }
                 R = Lane{A, Bs, f.Ae, f.An};
@@ -257,7 +259,8 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
 #pragma unroll
             for (int t = 0; t < LS; ++t) {
                 if (FULL || q.t0 + t < T) {
-                    const float yv = step<SAFE>(R, K[t], V[t], ch) + poison;
+                    float yv = step<SAFE>(R, K[t], V[t], ch) + poison;
+                    if constexpr (GATE) yv *= gate_of(Rg[t]);
                     if (q.active) yr.st(t, yv);
                 }
             }
@@ -275,14 +278,18 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
 // Waves per SIMD the register allocation must allow: the token registers
 // (2 LS per lane) dominate, and the occupancy they leave decides how much of
 // the memory latency other workgroups hide.
-constexpr int lb_waves_per_simd(int ls) { return ls <= 8 ? 8 : (ls <= 16 ? 6 : 4); }
+// The gate's receptance rows add LS registers more.
+constexpr int lb_waves_per_simd(int ls, bool gate) {
+    return gate ? (ls <= 8 ? 7 : 5) : (ls <= 8 ? 8 : (ls <= 16 ? 6 : 4));
+}
 
-template <int CG, int NS, int LS>
+template <int CG, int NS, int LS, bool GATE>
 __global__ __launch_bounds__(CG * NS * 64)
-__attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS)))) void fwd_lookback_kernel(
+__attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookback_kernel(
     int64_t B, int64_t T, int64_t C, const float *__restrict__ w, const float *__restrict__ u,
-    const float *__restrict__ k, const float *__restrict__ v, float *__restrict__ y,
-    const float *s_in, float *s_out, Word *aggs, Word *incls, uint32_t epoch, uint32_t nsets) {
+    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ r,
+    float *__restrict__ y, const float *s_in, float *s_out, Word *aggs, Word *incls,
+    uint32_t epoch, uint32_t nsets) {
     constexpr int TB = NS * LS;
     __shared__ LbShared<CG, NS> sh;
     LbWave q;
@@ -318,6 +325,7 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS)))) void fwd_lookback_ke
     // channel reads group 0 -- valid addresses whose values are never used,
     // since every token loop stops at T and such a wave stores nothing.
     float K[LS], V[LS];
+    float Rg[GATE ? LS : 1];  // receptance rows, issued after k and v: used last
     {
         const int64_t t0c = q.t0 < T ? q.t0 : T - 1;  // T >= 1 here
         const int64_t left = T - 1 - t0c;
@@ -326,9 +334,17 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS)))) void fwd_lookback_ke
         const TileRows kr(k + base + t0c * C, q.voff, q.rowb), vr(v + base + t0c * C, q.voff, q.rowb);
 #pragma unroll
         for (int t = 0; t < LS; ++t) {
-            const uint32_t r = (uint32_t)t < tmax ? (uint32_t)t : tmax;
-            K[t] = kr.ld((int)r);
-            V[t] = vr.ld((int)r);
+            const uint32_t row = (uint32_t)t < tmax ? (uint32_t)t : tmax;
+            K[t] = kr.ld((int)row);
+            V[t] = vr.ld((int)row);
+        }
+        if constexpr (GATE) {
+            const TileRows rr(r + base + t0c * C, q.voff, q.rowb);
+#pragma unroll
+            for (int t = 0; t < LS; ++t)
+                Rg[t] = rr.ld((int)((uint32_t)t < tmax ? (uint32_t)t : tmax));
+        } else {
+            Rg[0] = 0.0f;
         }
     }
     // keep the loads here, in flight while the rest of the prologue runs (the
@@ -341,18 +357,18 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS)))) void fwd_lookback_ke
     const bool full = (q.j + 1) * TB <= T;  // the whole block lies inside the sequence
     if (fast) {
         if (full)
-            lb_body<CG, NS, LS, false, true>(B, T, C, ch, q, K, V, y + base, s_in, s_out, aggs,
-                                             incls, epoch, sh);
+            lb_body<CG, NS, LS, false, true, GATE>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
+                                                   s_out, aggs, incls, epoch, sh);
         else
-            lb_body<CG, NS, LS, false, false>(B, T, C, ch, q, K, V, y + base, s_in, s_out, aggs,
-                                              incls, epoch, sh);
+            lb_body<CG, NS, LS, false, false, GATE>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
+                                                    s_out, aggs, incls, epoch, sh);
     } else {
         if (full)
-            lb_body<CG, NS, LS, true, true>(B, T, C, ch, q, K, V, y + base, s_in, s_out, aggs,
-                                            incls, epoch, sh);
+            lb_body<CG, NS, LS, true, true, GATE>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
+                                                  s_out, aggs, incls, epoch, sh);
         else
-            lb_body<CG, NS, LS, true, false>(B, T, C, ch, q, K, V, y + base, s_in, s_out, aggs,
-                                             incls, epoch, sh);
+            lb_body<CG, NS, LS, true, false, GATE>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
+                                                   s_out, aggs, incls, epoch, sh);
     }
 }
 
@@ -360,7 +376,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // (CG, NS, LS) variants: CG groups of 64 channels side by side, NS segments of
-// LS tokens stacked
+// LS tokens stacked.  The gated kernel holds a third row array (r), so it is
+// compiled only where LS <= 16 leaves the registers for it.
 #define WKV_LB_VARIANTS(X) \
     X(1, 4, 16)            \
     X(1, 8, 32)            \
@@ -377,7 +394,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int lb_key(int cg, int ns, int ls) { return (cg * 64 + ns) * 1024 + ls; }
 
-template <int CG, int NS, int LS>
+template <int CG, int NS, int LS, bool GATE>
 hipError_t launch_lb(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st) {
     const int64_t ngroups = (a.C + 63) / 64;
     const int64_t nsets = (ngroups + CG - 1) / CG;
@@ -385,15 +402,17 @@ hipError_t launch_lb(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st
     const int64_t nslots = nblocks * a.B * ngroups;
     Word *aggs = (Word *)sc.base;
     Word *incls = (Word *)((char *)sc.base + align_up((size_t)nslots * kSlotWords * sizeof(Word)));
-    hipLaunchKernelGGL((fwd_lookback_kernel<CG, NS, LS>), dim3((unsigned)(nsets * a.B * nblocks)),
-                       dim3(CG * NS * 64), 0, st, a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.y, a.s_in,
-                       a.s_out, aggs, incls, sc.epoch, (uint32_t)nsets);
+    hipLaunchKernelGGL((fwd_lookback_kernel<CG, NS, LS, GATE>),
+                       dim3((unsigned)(nsets * a.B * nblocks)), dim3(CG * NS * 64), 0, st, a.B,
+                       a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y, a.s_in, a.s_out, aggs, incls,
+                       sc.epoch, (uint32_t)nsets);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool forward_lookback_supported(int cg, int ns, int ls) {
+bool forward_lookback_supported(int cg, int ns, int ls, bool gated) {
+    if (gated && ls > 16) return false;
     switch (lb_key(cg, ns, ls)) {
 #define X(CG, NS, LS) case lb_key(CG, NS, LS):
         WKV_LB_VARIANTS(X)
@@ -419,9 +438,13 @@ size_t lookback_scratch_bytes(int64_t B, int64_t T, int64_t C, int ns, int ls) {
 
 hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,
                                    const LookbackScratch &sc, hipStream_t st) {
+    const bool gated = a.r != nullptr;
+    if (gated && ls > 16) return hipErrorInvalidValue;
     switch (lb_key(cg, ns, ls)) {
-#define X(CG, NS, LS) \
-    case lb_key(CG, NS, LS): return launch_lb<CG, NS, LS>(a, sc, st);
+#define X(CG, NS, LS)                                                              \
+    case lb_key(CG, NS, LS):                                                      \
+        return gated ? launch_lb<CG, NS, (LS <= 16 ? LS : 16), true>(a, sc, st)    \
+                     : launch_lb<CG, NS, LS, false>(a, sc, st);
         WKV_LB_VARIANTS(X)
 #undef X
         default:

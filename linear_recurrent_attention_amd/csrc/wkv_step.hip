@@ -8,6 +8,9 @@
 // and out).  A thread handles four consecutive channels with 16-byte
 // non-temporal loads and stores; a workgroup covers 1024 channels of one
 // (layer, sequence) row, so every access of a wave is 1 KiB contiguous.
+// With a receptance tensor r ([L][B][C], read beside k and v) the output is
+// the time-mixing block's gated sigmoid(r) * wkv (block figure of "RWKV
+// architecture overview"): 4 more bytes per lane.
 #include "wkv_device.hpp"
 #include "wkv_internal.hpp"
 
@@ -31,13 +34,14 @@ __device__ __forceinline__ float step_one(float &a, float &b, float &o, float k,
 }
 
 // VEC = 4: C % 4 == 0 and every pointer 16-byte aligned; VEC = 1 otherwise.
-template <int VEC>
+template <int VEC, bool GATE>
 __global__ __launch_bounds__(256) void step_kernel(int64_t L, int64_t B, int64_t C,
                                                    uint32_t blocks_per_row,
                                                    const float *__restrict__ w,
                                                    const float *__restrict__ u,
                                                    const float *__restrict__ k,
                                                    const float *__restrict__ v,
+                                                   const float *__restrict__ r,
                                                    float *__restrict__ y,
                                                    const float *s_in, float *s_out) {
     // rows are (layer, sequence) pairs; s_in may equal s_out (in place), so
@@ -64,11 +68,14 @@ __global__ __launch_bounds__(256) void step_kernel(int64_t L, int64_t B, int64_t
         f4 oo = __builtin_nontemporal_load((const f4 *)(s_in + so));
         const f4 ww = *(const f4 *)(w + wc);
         const f4 uu = *(const f4 *)(u + wc);
+        f4 rr = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (GATE) rr = __builtin_nontemporal_load((const f4 *)(r + kv));
         f4 yy;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float a = aa[j], b = bq[j], o = oo[j];
             yy[j] = step_one(a, b, o, kk[j], vv[j], ww[j], uu[j]);
+            if constexpr (GATE) yy[j] *= gate_of(rr[j]);
             aa[j] = a;
             bq[j] = b;
             oo[j] = o;
@@ -79,7 +86,8 @@ __global__ __launch_bounds__(256) void step_kernel(int64_t L, int64_t B, int64_t
         __builtin_nontemporal_store(oo, (f4 *)(s_out + so));
     } else {
         float a = s_in[sa], b = s_in[sb], o = s_in[so];
-        const float yy = step_one(a, b, o, k[kv], v[kv], w[wc], u[wc]);
+        float yy = step_one(a, b, o, k[kv], v[kv], w[wc], u[wc]);
+        if constexpr (GATE) yy *= gate_of(r[kv]);
         y[kv] = yy;
         s_out[sa] = a;
         s_out[sb] = b;
@@ -89,7 +97,8 @@ __global__ __launch_bounds__(256) void step_kernel(int64_t L, int64_t B, int64_t
 
 hipError_t launch_step(const StepArgs &a, hipStream_t st) {
     const uintptr_t mis = (uintptr_t)a.w | (uintptr_t)a.u | (uintptr_t)a.k | (uintptr_t)a.v |
-                          (uintptr_t)a.y | (uintptr_t)a.s_in | (uintptr_t)a.s_out;
+                          (uintptr_t)a.y | (uintptr_t)a.s_in | (uintptr_t)a.s_out |
+                          (uintptr_t)a.r;
     const bool vec4 = (a.C % 4 == 0) && (mis % 16 == 0);
     const int vec = vec4 ? 4 : 1;
     const int64_t per_block = 256 * (int64_t)vec;
@@ -97,12 +106,18 @@ hipError_t launch_step(const StepArgs &a, hipStream_t st) {
     const int64_t rows = a.L * a.B;
     const int64_t grid = rows * bpr;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (vec4)
-        hipLaunchKernelGGL(step_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, a.L, a.B, a.C,
-                           (uint32_t)bpr, a.w, a.u, a.k, a.v, a.y, a.s_in, a.s_out);
+#define WKV_STEP_LAUNCH(VEC, GATE)                                                          \
+    hipLaunchKernelGGL((step_kernel<VEC, GATE>), dim3((unsigned)grid), dim3(256), 0, st, a.L, \
+                       a.B, a.C, (uint32_t)bpr, a.w, a.u, a.k, a.v, a.r, a.y, a.s_in, a.s_out)
+    if (vec4 && a.r)
+        WKV_STEP_LAUNCH(4, true);
+    else if (vec4)
+        WKV_STEP_LAUNCH(4, false);
+    else if (a.r)
+        WKV_STEP_LAUNCH(1, true);
     else
-        hipLaunchKernelGGL(step_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, a.L, a.B, a.C,
-                           (uint32_t)bpr, a.w, a.u, a.k, a.v, a.y, a.s_in, a.s_out);
+        WKV_STEP_LAUNCH(1, false);
+#undef WKV_STEP_LAUNCH
     return hipGetLastError();
 }
 

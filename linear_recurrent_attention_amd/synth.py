@@ -8,7 +8,9 @@ drawn in float32 on the requested device.  The oracle always reads back the
 exact float32 values the GPU consumed, so host and device generators never have
 to agree bit for bit.
 
-Tensor ids: 0 decay, 1 u, 2 k, 3 v, 4 dy, 5 outlier positions, 6 outlier signs.
+Tensor ids: 0 decay, 1 u, 2 k, 3 v, 4 dy, 5 outlier positions, 6 outlier signs,
+7 receptance r (the output gate's input), 8 token-shift input x, 9 token-shift
+weights mu, 10 carried last token x_prev.
 
 The distributions follow the workloads shaped like the pages' models
 (24 layers x 2048 wide, 4096 x 24, a 1M-token document in 1024-token chunks):
@@ -23,7 +25,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-TID_DECAY, TID_U, TID_K, TID_V, TID_DY, TID_POS, TID_SIGN = range(7)
+TID_DECAY, TID_U, TID_K, TID_V, TID_DY, TID_POS, TID_SIGN, TID_R, TID_X, TID_MU, TID_XPREV = \
+    range(11)
 
 
 def seed_of(workload: int, index: int, tensor_id: int, base: int = 0) -> int:
@@ -62,6 +65,7 @@ class Recipe:
     v_std: float = 1.0
     outlier_frac: float = 0.0     # fraction of k entries overwritten by +-outlier_mag
     outlier_mag: float = 60.0
+    r_std: float = 2.0            # receptance: sigmoid(r) spans most of (0, 1)
 
 
 # Workload ids and their recipes.
@@ -117,6 +121,21 @@ def sequence(workload: int, index: int, shape, device="cpu", recipe: Recipe = No
         return k, v
     dy = normal(shape, 1.0, seed_of(workload, index, TID_DY), device)
     return k, v, dy
+
+
+def receptance(workload: int, index: int, shape, device="cpu", recipe: Recipe = None):
+    """The gate's receptance r (before the sigmoid), float32 of the given shape."""
+    r = recipe or RECIPES[workload]
+    return normal(shape, r.r_std, seed_of(workload, index, TID_R), device)
+
+
+def shift_inputs(workload: int, index: int, B: int, T: int, C: int, M: int, device="cpu"):
+    """Token-shift inputs: mu [M][C] ~ U(0, 1) (an interpolation weight),
+    x [B][T][C] ~ N(0, 1) (a layer-normalised embedding), x_prev [B][C] ~ N(0, 1)."""
+    mu = uniform((M, C), 0.0, 1.0, seed_of(workload, index, TID_MU), device)
+    x = normal((B, T, C), 1.0, seed_of(workload, index, TID_X), device)
+    xp = normal((B, C), 1.0, seed_of(workload, index, TID_XPREV), device)
+    return mu, x, xp
 
 
 def make(workload: int, index: int = 0, device="cpu", B=None, T=None, C=None,

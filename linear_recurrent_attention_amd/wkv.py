@@ -8,8 +8,9 @@ float32 tensor on a HIP device, the call raises.
 
 Layouts (C-contiguous, channel fastest):
     w, u            [C]          (wkv_step: [L][C])
-    k, v, y, dy     [B][T][C]    (wkv_step: [L][B][C])
+    k, v, r, y, dy  [B][T][C]    (wkv_step: [L][B][C])
     state           [3][B][C]    planes a, b, o   (wkv_step: [L][3][B][C])
+    token shift     mu [M][C], x [B][T][C], x_prev [B][C], out [M][B][T][C]
 """
 from __future__ import annotations
 
@@ -38,7 +39,10 @@ WKV_KERNEL_SEGMENTED = 2
 WKV_KERNEL_LOOKBACK = 3
 
 EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backward",
-            "wkv_status_string", "wkv_forward_ex", "wkv_forward_plan_auto")
+            "wkv_status_string", "wkv_forward_ex", "wkv_forward_plan_auto",
+            "wkv_forward_gated", "wkv_step_gated", "wkv_token_shift")
+
+WKV_TOKEN_SHIFT_MAX_MIXES = 8
 
 
 class WkvError(RuntimeError):
@@ -77,6 +81,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_backward_workspace_size.restype = sz
     lib.wkv_backward.argtypes = [i64, i64, i64] + [vp] * 9 + [vp, sz, vp]
     lib.wkv_backward.restype = ctypes.c_int
+    lib.wkv_forward_gated.argtypes = ([i64, i64, i64] + [vp] * 8 +
+                                      [ctypes.POINTER(ForwardPlan), vp])
+    lib.wkv_forward_gated.restype = ctypes.c_int
+    lib.wkv_step_gated.argtypes = [i64, i64, i64] + [vp] * 8 + [vp]
+    lib.wkv_step_gated.restype = ctypes.c_int
+    lib.wkv_token_shift.argtypes = [i64, i64, i64, i64] + [vp] * 5 + [vp]
+    lib.wkv_token_shift.restype = ctypes.c_int
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -142,6 +153,30 @@ def wkv_forward(w, u, k, v, y=None, state_in=None, state_out=None, stream=None, 
     return y, state_out
 
 
+def _plan(plan):
+    if plan is None:
+        return None
+    p = ForwardPlan(*plan) if len(plan) == 4 else ForwardPlan(*plan, 0)
+    return ctypes.byref(p)
+
+
+def wkv_forward_gated(w, u, k, v, r, y=None, state_in=None, state_out=None, stream=None,
+                      plan=None):
+    """Forward with the time-mixing output gate: y = sigmoid(r) * wkv.
+    Arguments as for ``wkv_forward``; r has the layout of k.  Returns
+    (y, state_out)."""
+    B, T, C = _bundle_shape(k, state_in)
+    if y is None:
+        y = torch.empty_like(k)
+    if state_out is True:
+        state_out = torch.empty((3, B, C), device=k.device, dtype=torch.float32)
+    st = load_library().wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                          _ptr(y), _ptr(state_in), _ptr(state_out), _plan(plan),
+                                          _stream(stream))
+    _check("wkv_forward_gated", st)
+    return y, state_out
+
+
 def wkv_forward_plan_auto(B: int, T: int, C: int):
     p = ForwardPlan()
     _check("wkv_forward_plan_auto", load_library().wkv_forward_plan_auto(B, T, C, ctypes.byref(p)))
@@ -162,6 +197,41 @@ def wkv_step(w, u, k, v, state_in, state_out=None, y=None, stream=None):
                                  _ptr(state_in), _ptr(state_out), _stream(stream))
     _check("wkv_step", st)
     return y, state_out
+
+
+def wkv_step_gated(w, u, k, v, r, state_in, state_out=None, y=None, stream=None):
+    """``wkv_step`` with the output gate y = sigmoid(r) * wkv; r: [L][B][C]."""
+    if k.dim() != 3:
+        raise ValueError("k must be [L][B][C]")
+    L, B, C = (int(x) for x in k.shape)
+    if y is None:
+        y = torch.empty_like(k)
+    if state_out is None:
+        state_out = state_in
+    st = load_library().wkv_step_gated(L, B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                       _ptr(y), _ptr(state_in), _ptr(state_out), _stream(stream))
+    _check("wkv_step_gated", st)
+    return y, state_out
+
+
+def wkv_token_shift(mu, x, x_prev=None, out=None, x_prev_out=None, stream=None):
+    """Token shift of x [B][T][C] by the M weight vectors mu [M][C]:
+    out[m] = mu[m] * x_t + (1 - mu[m]) * x_{t-1}, with x_{-1} = x_prev [B][C]
+    (zeros when None).  ``x_prev_out`` receives x[:, T-1]; pass True to have it
+    allocated, or x_prev itself to update it in place.  Returns
+    (out, x_prev_out)."""
+    if x.dim() != 3 or mu.dim() != 2:
+        raise ValueError("x must be [B][T][C] and mu [M][C]")
+    B, T, C = (int(a) for a in x.shape)
+    M = int(mu.shape[0])
+    if out is None:
+        out = torch.empty((M, B, T, C), device=x.device, dtype=torch.float32)
+    if x_prev_out is True:
+        x_prev_out = torch.empty((B, C), device=x.device, dtype=torch.float32)
+    st = load_library().wkv_token_shift(B, T, C, M, _ptr(mu), _ptr(x), _ptr(x_prev), _ptr(out),
+                                        _ptr(x_prev_out), _stream(stream))
+    _check("wkv_token_shift", st)
+    return out, x_prev_out
 
 
 def wkv_backward_workspace_size(B: int, T: int, C: int) -> int:

@@ -137,6 +137,54 @@ def test_forward_ex_rejects_unknown_plans(lib):
         assert lib.wkv_forward_ex(*args, ctypes.byref(p), None) == W.WKV_ERR_UNSUPPORTED
 
 
+def test_gated_calls_reject_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    w, u, k, v = vp(P), vp(P + 0x1000), vp(P + 0x100000), vp(P + 0x10000000)
+    r, y = vp(P + 0x30000000), vp(P + 0x20000000)
+    g = lib.wkv_forward_gated
+    assert g(-1, 8, 16, w, u, k, v, r, y, None, None, None, None) == W.WKV_ERR_DIM
+    assert g(2, 8, 16, w, u, k, v, None, y, None, None, None, None) == W.WKV_ERR_NULL
+    assert g(2, 8, 16, w, u, k, v, vp(P + 0x20000000 + 4), y, None, None, None,
+             None) == W.WKV_ERR_ALIAS                                   # r overlaps y
+    assert g(2, 8, 16, w, u, k, v, r, y, None, vp(P + 0x30000000), None,
+             None) == W.WKV_ERR_ALIAS                                   # state_out on r
+    # the gated look-back kernel exists only for segments of <= 16 tokens
+    p = W.ForwardPlan(W.WKV_KERNEL_LOOKBACK, 4, 32, 64)
+    assert g(2, 8, 16, w, u, k, v, r, y, None, None, ctypes.byref(p), None) == \
+        W.WKV_ERR_UNSUPPORTED
+    p = W.ForwardPlan(W.WKV_KERNEL_LOOKBACK, 4, 16, 32)
+    assert g(2, 8, 16, w, u, k, v, r, y, None, None, ctypes.byref(p), None) == \
+        W.WKV_ERR_UNSUPPORTED
+    si, so = vp(P + 0x400000), vp(P + 0x400000)
+    base = [vp(P), vp(P + 0x1000), vp(P + 0x100000), vp(P + 0x200000)]
+    sg = lib.wkv_step_gated
+    assert sg(2, 2, 4, *base, None, vp(P + 0x300000), si, so, None) == W.WKV_ERR_NULL
+    assert sg(2, 2, 4, *base, vp(P + 0x300000), vp(P + 0x300000 + 8), si, so,
+              None) == W.WKV_ERR_ALIAS
+    assert sg(-2, 2, 4, *base, vp(P + 0x500000), vp(P + 0x300000), si, so, None) == W.WKV_ERR_DIM
+
+
+def test_token_shift_rejects_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    mu, x, xp = vp(P), vp(P + 0x100000), vp(P + 0x200000)
+    out, xpo = vp(P + 0x10000000), vp(P + 0x300000)
+    ts = lib.wkv_token_shift
+    assert ts(2, 8, 16, -1, mu, x, xp, out, xpo, None) == W.WKV_ERR_DIM
+    assert ts(2, 8, 16, 9, mu, x, xp, out, xpo, None) == W.WKV_ERR_UNSUPPORTED
+    assert ts(2, 8, 16, 3, None, x, xp, out, xpo, None) == W.WKV_ERR_NULL
+    assert ts(2, 8, 16, 3, mu, None, xp, out, xpo, None) == W.WKV_ERR_NULL
+    assert ts(2, 8, 16, 3, mu, x, xp, None, xpo, None) == W.WKV_ERR_NULL
+    assert ts(2, 8, 16, 3, mu, x, xp, vp(P + 0x100000 + 64), xpo, None) == W.WKV_ERR_ALIAS
+    assert ts(2, 8, 16, 3, mu, x, xp, out, vp(P + 0x200000 + 4), None) == W.WKV_ERR_ALIAS
+    assert ts(2, 8, 16, 3, mu, x, xp, out, vp(P + 0x100000), None) == W.WKV_ERR_ALIAS
+    assert ts(1 << 30, 1 << 20, 1 << 20, 3, mu, x, xp, out, xpo, None) == W.WKV_ERR_OVERFLOW
+    # nothing to write: returns before any launch
+    assert ts(2, 8, 16, 0, None, x, xp, None, None, None) == W.WKV_OK
+    assert ts(0, 8, 16, 3, mu, None, None, None, None, None) == W.WKV_OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     from linear_recurrent_attention_amd import wkv
     with pytest.raises(RuntimeError, match="missing"):
