@@ -14,9 +14,12 @@ wkv_forward).  Prints one JSON line with the lane-token throughput
 bytes per launch over its average launch time, measured with HIP events on the
 stream it runs on), and the float64 CPU oracle timed on this host as a baseline.
 
-Other workloads (--workload stream|decode|stability_fwd|stability_bwd) print
-their own line in the same format; they are parity workloads with extra
-measurements, not the headline.
+Other workloads print their own line in the same format; they are parity
+workloads with extra measurements, not the headline:
+    stream, decode, stability_fwd, stability_bwd   the other operator shapes
+    gpt_gated, decode_gated   the same with the output gate sigmoid(r) fused in
+    token_shift               the token shift at the GPT shape (3 mixes)
+    copy                      a 1 GiB device copy, the bandwidth reference
 """
 from __future__ import annotations
 
@@ -31,12 +34,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "WKV fwd tokens·channels/sec + HBM GB/s (% peak), B=8 T=1024 C=2048 fp32"
+METRIC_GATED = ("WKV fwd with the sigmoid(r) output gate, tokens·channels/sec, "
+                "B=8 T=1024 C=2048 fp32")
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["linear_recurrent_attention_amd/csrc/wkv_forward.hip",
                   "linear_recurrent_attention_amd/csrc/wkv_lookback.hip",
                   "linear_recurrent_attention_amd/csrc/wkv_step.hip",
                   "linear_recurrent_attention_amd/csrc/wkv_backward.hip",
+                  "linear_recurrent_attention_amd/csrc/wkv_shift.hip",
                   "linear_recurrent_attention_amd/csrc/wkv_device.hpp"]
 
 
@@ -115,20 +121,28 @@ def cpu_baseline_gpt(torch, synth, inputs_fn, budget_s: float):
     done = 0
     elapsed = 0.0
     layer = 0
+    gated = False
     while elapsed < budget_s and layer < 24:
         d = inputs_fn(layer)
         a = [d[n].double().cpu().numpy() for n in ("w", "u", "k", "v")]
+        r = d["r"].double().cpu().numpy() if "r" in d else None
         t0 = time.perf_counter()
-        oracle.forward_scan(*a, nthreads=cores)
+        y, _ = oracle.forward_scan(*a, nthreads=cores)
+        if r is not None:
+            gated = True
+            oracle.gate(y, r)
         elapsed += time.perf_counter() - t0
         done += d["k"].numel()
         layer += 1
+    what = "recurrence and gate (the gate single-threaded)" if gated else "recurrence"
     return {"value": done / elapsed, "unit": "tok·ch/s", "cores": cores, "kind": "oracle",
             "sample": f"{layer} of the 24 seeded B=8 T=1024 C=2048 layers, whole, "
-                      f"float64 O(T) recurrence on {cores} threads ({elapsed:.1f} s)"}
+                      f"float64 O(T) {what} on {cores} threads ({elapsed:.1f} s)"}
 
 
-def bench_gpt(args, torch, wkv, synth):
+def bench_gpt(args, torch, wkv, synth, gated: bool = False):
+    """GPT-mode forward of 24 seeded layers; gated: with the time-mixing output
+    gate y = sigmoid(r) * wkv fused in (r read beside k and v)."""
     sh = synth.SHAPES[synth.GPT]
     B, T, C, NL = sh["B"], sh["T"], sh["C"], sh["layers"]
     dev = torch.device("cuda")
@@ -139,13 +153,21 @@ def bench_gpt(args, torch, wkv, synth):
         d = synth.make(synth.GPT, index=l, device=dev)
         d["y"] = torch.empty_like(d["k"])
         d["s"] = torch.empty((3, B, C), device=dev)
+        if gated:
+            d["r"] = synth.receptance(synth.GPT, l, (B, T, C), device=dev)
         layers.append(d)
     plan = tuple(args.plan) if args.plan else None
     chosen = plan or wkv.wkv_forward_plan_auto(B, T, C)
+    if gated and not plan:
+        chosen = gated_auto_plan(chosen)
 
     def call(d):
-        wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=d["y"], state_out=d["s"],
-                        stream=stream, plan=plan)
+        if gated:
+            wkv.wkv_forward_gated(d["w"], d["u"], d["k"], d["v"], d["r"], y=d["y"],
+                                  state_out=d["s"], stream=stream, plan=plan)
+        else:
+            wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=d["y"], state_out=d["s"],
+                            stream=stream, plan=plan)
 
     for _ in range(args.warmup):
         for d in layers:
@@ -175,12 +197,14 @@ def bench_gpt(args, torch, wkv, synth):
     launches = args.steps * NL
     ms_launch = ms / launches
     lane_tok = B * T * C
-    algo_bytes = 12 * lane_tok + 8 * C + 12 * B * C      # k, v in, y out; w, u; state out
+    # k, v (and r) in, y out; w, u; state out
+    algo_bytes = (16 if gated else 12) * lane_tok + 8 * C + 12 * B * C
     achieved = algo_bytes / (ms_launch * 1e-3) / 1e9
-    kname = kernel_name(chosen, wkv)
-    traffic = measured_traffic(kname, "gpt")
+    kname = kernel_name(chosen, wkv, gated)
+    wl = "gpt_gated" if gated else "gpt"
+    traffic = measured_traffic(kname, wl)
     out = {
-        "metric": METRIC,
+        "metric": METRIC_GATED if gated else METRIC,
         "value": lane_tok * launches / (ms * 1e-3),
         "unit": "tok·ch/s",
         "n_gpus": 1,
@@ -191,8 +215,10 @@ def bench_gpt(args, torch, wkv, synth):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded; k, v ~ N(0,1) with k x2, decay ~ U(-5,1), u ~ N(0,0.5))",
-        "config": {"workload": "gpt_forward", "B": B, "T": T, "C": C, "layers": NL,
+        "data": "synthetic (seeded; k, v ~ N(0,1) with k x2, decay ~ U(-5,1), u ~ N(0,0.5)"
+                + (", r ~ N(0,2))" if gated else ")"),
+        "config": {"workload": "gpt_gated_forward" if gated else "gpt_forward", "B": B, "T": T,
+                   "C": C, "layers": NL,
                    "kernel": kname, "plan": list(chosen),
                    "mean_over_layers_of_median_ms": sum(per_layer) / len(per_layer),
                    "hbm_gbs": achieved, "pct_peak_hbm": 100 * achieved / PEAK_HBM_GBS,
@@ -204,23 +230,34 @@ def bench_gpt(args, torch, wkv, synth):
     }
     if not args.no_cpu_baseline:
         log("gpt: timing the CPU oracle")
+        names = ("w", "u", "k", "v", "r") if gated else ("w", "u", "k", "v")
         out["cpu_baseline"] = cpu_baseline_gpt(
-            torch, synth, lambda l: {n: layers[l][n] for n in ("w", "u", "k", "v")},
-            args.cpu_seconds)
+            torch, synth, lambda l: {n: layers[l][n] for n in names}, args.cpu_seconds)
     return out
 
 
-def kernel_name(plan, wkv) -> str:
+def kernel_name(plan, wkv, gated: bool = False) -> str:
     """Kernel symbol (template arguments as in the profiler's kernel names)."""
     kernel, nw, ls = plan[:3]
     cw = plan[3] if len(plan) > 3 and plan[3] else 64
+    g = "true" if gated else "false"
     if kernel == wkv.WKV_KERNEL_LANE:
-        return "fwd_lane_kernel"
+        return f"fwd_lane_kernel<{g}>"
     if kernel == wkv.WKV_KERNEL_SEGMENTED:
-        return f"fwd_seg_kernel<{nw * cw // 64}, {ls}, {cw}>"
+        return f"fwd_seg_kernel<{nw * cw // 64}, {ls}, {cw}, {g}>"
     if kernel == wkv.WKV_KERNEL_LOOKBACK:
-        return f"fwd_lookback_kernel<{cw // 64}, {nw}, {ls}>"
+        return f"fwd_lookback_kernel<{cw // 64}, {nw}, {ls}, {g}>"
     return f"kernel{kernel}<{nw}, {ls}>"
+
+
+def gated_auto_plan(plan):
+    """The plan the library's automatic choice takes for the gated forward: a
+    look-back block keeps its length, cut into segments of at most 16 tokens
+    (the gated look-back kernel is compiled for those only)."""
+    kernel, ns, ls = plan[:3]
+    if kernel == 3 and ls > 16:
+        return (kernel, ns * ls // 16, 16) + tuple(plan[3:])
+    return tuple(plan)
 
 
 def bench_stream(args, torch, wkv, synth):
@@ -293,9 +330,10 @@ def bench_stream(args, torch, wkv, synth):
             "cpu_baseline": cpu}
 
 
-def bench_decode(args, torch, wkv, synth):
+def bench_decode(args, torch, wkv, synth, gated: bool = False):
     """L=24 B=1024 C=4096 batched T=1 steps; state from 256 warm-up tokens;
-    inputs from a ring of 32 distinct [24][1024][4096] k, v sets."""
+    inputs from a ring of 32 distinct [24][1024][4096] k, v (and r) sets.
+    gated: the step with the output gate y = sigmoid(r) * wkv."""
     sh = synth.SHAPES[synth.DECODE]
     L, B, C, WU, RING = sh["L"], sh["B"], sh["C"], sh["warmup"], sh["ring"]
     dev = torch.device("cuda")
@@ -310,19 +348,32 @@ def bench_decode(args, torch, wkv, synth):
         del kk, vv
     log("decode: generating the input ring")
     ring = [synth.sequence(synth.DECODE, 1000 + r, (L, B, C), device=dev) for r in range(RING)]
+    if gated:
+        ring = [kv + (synth.receptance(synth.DECODE, 1000 + r, (L, B, C), device=dev),)
+                for r, kv in enumerate(ring)]
     y = torch.empty((L, B, C), device=dev)
     nsteps = args.steps * 64
+
+    def call(r):
+        e = ring[r % RING]
+        if gated:
+            wkv.wkv_step_gated(w_all, u_all, e[0], e[1], e[2], state, y=y, stream=stream)
+        else:
+            wkv.wkv_step(w_all, u_all, e[0], e[1], state, y=y, stream=stream)
+
     for r in range(args.warmup * 8):
-        wkv.wkv_step(w_all, u_all, ring[r % RING][0], ring[r % RING][1], state, y=y, stream=stream)
+        call(r)
     torch.cuda.synchronize()
     tm = Timer(torch, stream)
     tm.start()
     for r in range(nsteps):
-        wkv.wkv_step(w_all, u_all, ring[r % RING][0], ring[r % RING][1], state, y=y, stream=stream)
+        call(r)
     ms = tm.stop_ms()
     per = ms / nsteps
     lanes = L * B * C
-    algo = 36 * lanes + 8 * L * C
+    algo = (40 if gated else 36) * lanes + 8 * L * C
+    kname = f"step_kernel<4, {'true' if gated else 'false'}>"
+    wl = "decode_gated" if gated else "decode"
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -335,9 +386,12 @@ def bench_decode(args, torch, wkv, synth):
                                                      ring[0][1][l:l + 1])]
             kk = a[2].reshape(B, 1, C)
             vv = a[3].reshape(B, 1, C)
+            rr = ring[0][2][l].double().cpu().numpy() if gated else None
             s_in = state[l].double().cpu().numpy()
             t0 = time.perf_counter()
-            oracle.forward_scan(a[0], a[1], kk, vv, s_in, nthreads=cores)
+            yy, _ = oracle.forward_scan(a[0], a[1], kk, vv, s_in, nthreads=cores)
+            if gated:
+                oracle.gate(yy[:, 0, :], rr)
             return B * C, time.perf_counter() - t0
 
         done, secs, calls = timed_oracle(layer, args.cpu_seconds)
@@ -345,17 +399,19 @@ def bench_decode(args, torch, wkv, synth):
                "sample": f"{calls} of the 24 layers (B=1024 C=4096 lanes each) stepped once, "
                          f"float64, on {cores} threads ({secs:.1f} s), extrapolated per lane-step "
                          f"to the whole L=24 step"}
-    return {"metric": "WKV decode steps/sec, L=24 B=1024 C=4096 fp32", "value": 1e3 / per,
+    metric = ("WKV decode steps/sec with the sigmoid(r) output gate, L=24 B=1024 C=4096 fp32"
+              if gated else "WKV decode steps/sec, L=24 B=1024 C=4096 fp32")
+    return {"metric": metric, "value": 1e3 / per,
             "unit": "steps/s", "n_gpus": 1, "steps": nsteps, "warmup": args.warmup * 8,
             "ms_per_step": per, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f32", "data": "synthetic",
-            "config": {"workload": "decode_step", "L": L, "B": B, "C": C,
-                       "kernel": "step_kernel<4>",
+            "config": {"workload": "decode_gated_step" if gated else "decode_step", "L": L,
+                       "B": B, "C": C, "kernel": kname,
                        "state_gbs": 24 * lanes / (per * 1e-3) / 1e9},
             "roofline": {"bound": "hbm", "achieved": algo / (per * 1e-3) / 1e9,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": algo / (per * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "traffic": measured_traffic("step_kernel<4>", "decode"),
+                         "traffic": measured_traffic(kname, wl),
                          "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3},
             "cpu_baseline": cpu}
 
@@ -436,6 +492,72 @@ def bench_stability(args, torch, wkv, synth, backward: bool):
             "cpu_baseline": cpu}
 
 
+def bench_shift(args, torch, wkv, synth):
+    """Token shift at the GPT shape (B=8 T=1024 C=2048) with the three mixes of
+    the R, K and V inputs, the carried token updated in place; rotating over
+    4 input sets (1 GiB of traffic in all, beyond the 256 MB last-level
+    cache)."""
+    sh = synth.SHAPES[synth.GPT]
+    B, T, C, M, NSET = sh["B"], sh["T"], sh["C"], 3, 4
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    sets = []
+    for i in range(NSET):
+        mu, x, xp = synth.shift_inputs(synth.GPT, 100 + i, B, T, C, M, device=dev)
+        sets.append(dict(mu=mu, x=x, xp=xp,
+                         out=torch.empty((M, B, T, C), device=dev)))
+
+    def call(i):
+        e = sets[i % NSET]
+        wkv.wkv_token_shift(e["mu"], e["x"], e["xp"], out=e["out"], x_prev_out=e["xp"],
+                            stream=stream)
+
+    for i in range(args.warmup * NSET):
+        call(i)
+    torch.cuda.synchronize()
+    n = args.steps * 8
+    tm = Timer(torch, stream)
+    tm.start()
+    for i in range(n):
+        call(i)
+    ms = tm.stop_ms()
+    per = ms / n
+    elems = B * T * C
+    # x in, M outputs out; mu; carried token in and out
+    algo = (4 + 4 * M) * elems + 4 * M * C + 8 * B * C
+    kname = f"shift_kernel<4, {M}>"
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        def one(i):
+            if i >= NSET:
+                return None
+            e = sets[i]
+            a = [e[nm].double().cpu().numpy() for nm in ("mu", "x", "xp")]
+            t0 = time.perf_counter()
+            oracle.token_shift(*a)
+            return elems, time.perf_counter() - t0
+
+        done, secs, calls = timed_oracle(one, args.cpu_seconds)
+        cpu = {"value": done / secs, "unit": "tok·ch/s", "cores": 1, "kind": "oracle",
+               "sample": f"{calls} of the 4 input sets (B=8 T=1024 C=2048, M=3), float64 "
+                         f"loop on 1 thread ({secs:.1f} s)"}
+    return {"metric": "token shift tokens·channels/sec, B=8 T=1024 C=2048, 3 mixes, fp32",
+            "value": elems / (per * 1e-3), "unit": "tok·ch/s", "n_gpus": 1, "steps": n,
+            "warmup": args.warmup * NSET, "ms_per_step": per, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded; x, x_prev ~ N(0,1), mu ~ U(0,1))",
+            "config": {"workload": "token_shift", "B": B, "T": T, "C": C, "mixes": M,
+                       "kernel": kname},
+            "roofline": {"bound": "hbm", "achieved": algo / (per * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": algo / (per * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "traffic": measured_traffic(kname, "token_shift"),
+                         "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3},
+            "cpu_baseline": cpu}
+
+
 def bench_copy(args, torch, wkv, synth):
     """A plain device-to-device copy of 1 GiB (torch's copy kernel): the
     reference for scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE) read
@@ -468,7 +590,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt",
-                    choices=["gpt", "stream", "decode", "stability_fwd", "stability_bwd", "copy"])
+                    choices=["gpt", "gpt_gated", "stream", "decode", "decode_gated",
+                             "stability_fwd", "stability_bwd", "token_shift", "copy"])
     ap.add_argument("--plan", type=int, nargs="+", default=None,
                     metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
                     "(wkv_forward_ex plan)")
@@ -487,6 +610,9 @@ def main():
     from linear_recurrent_attention_amd import synth, wkv
     wkv.load_library()
     fn = {"gpt": bench_gpt, "stream": bench_stream, "decode": bench_decode, "copy": bench_copy,
+          "gpt_gated": lambda a, t, w, s: bench_gpt(a, t, w, s, True),
+          "decode_gated": lambda a, t, w, s: bench_decode(a, t, w, s, True),
+          "token_shift": bench_shift,
           "stability_fwd": lambda a, t, w, s: bench_stability(a, t, w, s, False),
           "stability_bwd": lambda a, t, w, s: bench_stability(a, t, w, s, True)}[args.workload]
     torch.cuda.synchronize()
