@@ -192,6 +192,12 @@ typedef struct wkv_forward_plan {
                           128 or 256; 0 = 64 */
 } wkv_forward_plan;
 
+/* Reproducibility: the lane and segmented kernels give the same bits on every
+ * call.  The look-back kernel composes a block's starting state from whichever
+ * earlier blocks' states are published first, so the rounding of its outputs,
+ * always within the documented accuracy, may differ in the last bits from one
+ * call to the next.  A caller who needs bitwise reproducible forwards forces
+ * WKV_KERNEL_SEGMENTED. */
 WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                                   const float *k, const float *v, float *y,
                                   const float *state_in, float *state_out,
@@ -229,6 +235,50 @@ WKV_API wkv_status wkv_forward_gated(int64_t B, int64_t T, int64_t C, const floa
 WKV_API wkv_status wkv_step_gated(int64_t L, int64_t B, int64_t C, const float *w,
                                   const float *u, const float *k, const float *v,
                                   const float *r, float *y, const float *state_in,
+                                  float *state_out, hipStream_t stream);
+
+/* Element format of k, v, r and y in the typed entry points.  w, u and the
+ * state stay float32 in every format. */
+typedef enum wkv_dtype {
+    WKV_DTYPE_F32 = 0,   /* IEEE binary32 */
+    WKV_DTYPE_F16 = 1,   /* IEEE binary16 */
+    WKV_DTYPE_BF16 = 2   /* bfloat16: the upper 16 bits of a binary32 */
+} wkv_dtype;
+
+/*
+ * Forward with 16-bit (or 32-bit) activations: k, v, r and y hold `dtype`
+ * elements, while w, u and the state are float32 and all arithmetic is
+ * float32.  Inputs widen exactly; y is rounded to `dtype` once, to nearest,
+ * ties to even.  The pages run the model in half precision (skill page,
+ * "Quick start": the 'cuda fp16' strategy) and train it in bfloat16
+ * ("Workflow 3: Fine-tuning RWKV").
+ *
+ *   k, v, y    [B][T][C] of dtype
+ *   r          [B][T][C] of dtype, or NULL: with r, y = sigmoid(r) * wkv (as
+ *              wkv_forward_gated); without, y = wkv
+ *   w, u, state_in, state_out, plan, stream: as for wkv_forward_ex
+ * WKV_DTYPE_F32 behaves exactly like wkv_forward_ex or wkv_forward_gated.  For
+ * the 16-bit formats the compiled kernels are the lane kernel, the segmented
+ * kernel with 16 segments of 16 tokens over 64 channels, and the look-back
+ * kernel with 64 channels and 4x16, 4x32 or 8x16 tokens (8x16 and 4x16 when
+ * gated); another explicit plan returns WKV_ERR_UNSUPPORTED, and the
+ * automatic choice stays within them.  An unknown dtype returns
+ * WKV_ERR_UNSUPPORTED.  Other errors as for wkv_forward, with byte sizes
+ * taken at the element size of dtype.
+ */
+WKV_API wkv_status wkv_forward_typed(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                     const float *w, const float *u, const void *k,
+                                     const void *v, const void *r, void *y,
+                                     const float *state_in, float *state_out,
+                                     const wkv_forward_plan *plan, hipStream_t stream);
+
+/*
+ * wkv_step with k, v, r and y of `dtype` (r NULL: ungated), w, u and the
+ * state float32, as for wkv_forward_typed.  Cites: as wkv_step.
+ */
+WKV_API wkv_status wkv_step_typed(int64_t L, int64_t B, int64_t C, wkv_dtype dtype,
+                                  const float *w, const float *u, const void *k, const void *v,
+                                  const void *r, void *y, const float *state_in,
                                   float *state_out, hipStream_t stream);
 
 /* Largest number of mixes wkv_token_shift takes in one call. */

@@ -144,18 +144,31 @@ wkv_forward_plan gated_plan(wkv_forward_plan p) {
     if (p.kernel == WKV_KERNEL_LOOKBACK && p.seg_len > 16) {
         p.segments = p.segments * p.seg_len / 16;
         p.seg_len = 16;
-        if (!wkv::forward_lookback_supported(p.channels / 64, p.segments, p.seg_len, true))
+        if (!wkv::forward_lookback_supported(p.channels / 64, p.segments, p.seg_len, true,
+                                             wkv::kIoF32))
             p = wkv_forward_plan{WKV_KERNEL_LOOKBACK, 8, 16, 64};
     }
     return p;
 }
 
+// Bytes per element of k, v, r, y for a wkv_dtype, 0 for an unknown one.
+int64_t elem_bytes(int dtype) {
+    switch (dtype) {
+        case WKV_DTYPE_F32: return 4;
+        case WKV_DTYPE_F16:
+        case WKV_DTYPE_BF16: return 2;
+        default: return 0;
+    }
+}
+
 // r: the gate's receptance (same layout as k), NULL for the plain forward.
+// esize: bytes per element of k, v, r and y.
 wkv_status check_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                         const float *k, const float *v, const float *y, const float *s_in,
-                         const float *s_out, const float *r = nullptr, bool gated = false) {
+                         const void *k, const void *v, const void *y, const float *s_in,
+                         const float *s_out, const void *r = nullptr, bool gated = false,
+                         int64_t esize = 4) {
     if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
-    const int64_t seq = bytes_of(B, T, C);
+    const int64_t seq = bytes_of(B, T, C, esize);
     const int64_t st = bytes_of(3, B, C);
     const int64_t ch = bytes_of(1, 1, C);
     if (seq < 0 || st < 0 || ch < 0) return WKV_ERR_OVERFLOW;
@@ -175,12 +188,15 @@ wkv_status check_forward(int64_t B, int64_t T, int64_t C, const float *w, const 
 
 wkv_status from_hip(hipError_t e) { return e == hipSuccess ? WKV_OK : WKV_ERR_HIP; }
 
-// wkv_forward_ex and wkv_forward_gated: r is NULL for the plain forward.
+// wkv_forward_ex, wkv_forward_gated and wkv_forward_typed: r is NULL for the
+// plain forward; io is the wkv_dtype of k, v, r and y.
 wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                        const float *k, const float *v, const float *r, float *y,
+                        const void *k, const void *v, const void *r, void *y,
                         const float *state_in, float *state_out, const wkv_forward_plan *plan,
-                        bool gated, hipStream_t stream) {
-    wkv_status st = check_forward(B, T, C, w, u, k, v, y, state_in, state_out, r, gated);
+                        bool gated, int io, hipStream_t stream) {
+    const int64_t esize = elem_bytes(io);
+    if (esize == 0) return WKV_ERR_UNSUPPORTED;
+    wkv_status st = check_forward(B, T, C, w, u, k, v, y, state_in, state_out, r, gated, esize);
     if (st != WKV_OK) return st;
     wkv_forward_plan p{WKV_KERNEL_AUTO, 0, 0, 0};
     if (plan) p = *plan;
@@ -193,7 +209,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
             if (p.segments == 0) p.segments = 16;
             if (p.seg_len == 0) p.seg_len = 16;
             if (p.channels == 0) p.channels = 64;
-            if (!wkv::forward_seg_supported(p.segments, p.seg_len, p.channels))
+            if (!wkv::forward_seg_supported(p.segments, p.seg_len, p.channels, io))
                 return WKV_ERR_UNSUPPORTED;
             break;
         case WKV_KERNEL_LOOKBACK:
@@ -201,7 +217,8 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
             if (p.seg_len == 0) p.seg_len = 16;
             if (p.channels == 0) p.channels = 64;
             if (p.channels % 64 != 0 ||
-                !wkv::forward_lookback_supported(p.channels / 64, p.segments, p.seg_len, gated))
+                !wkv::forward_lookback_supported(p.channels / 64, p.segments, p.seg_len, gated,
+                                                 io))
                 return WKV_ERR_UNSUPPORTED;
             break;
         default:
@@ -229,7 +246,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
     } else if (capturing && p.kernel == WKV_KERNEL_LOOKBACK) {
         return WKV_ERR_UNSUPPORTED;
     }
-    const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr};
+    const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr, io};
     if (p.kernel == WKV_KERNEL_LANE) {
         if ((lanes + 255) / 256 > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
         return from_hip(wkv::launch_forward_lane(a, stream));
@@ -245,12 +262,16 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
     return from_hip(wkv::launch_forward_seg(a, p.segments, p.seg_len, p.channels, stream));
 }
 
-// wkv_step and wkv_step_gated: r is NULL for the plain step.
+// wkv_step, wkv_step_gated and wkv_step_typed: r is NULL for the plain step;
+// io is the wkv_dtype of k, v, r and y.
 wkv_status step_impl(int64_t L, int64_t B, int64_t C, const float *w, const float *u,
-                     const float *k, const float *v, const float *r, float *y,
-                     const float *state_in, float *state_out, bool gated, hipStream_t stream) {
+                     const void *k, const void *v, const void *r, void *y,
+                     const float *state_in, float *state_out, bool gated, int io,
+                     hipStream_t stream) {
+    const int64_t esize = elem_bytes(io);
+    if (esize == 0) return WKV_ERR_UNSUPPORTED;
     if (L < 0 || B < 0 || C < 0) return WKV_ERR_DIM;
-    const int64_t seq = bytes_of(L, B, C);
+    const int64_t seq = bytes_of(L, B, C, esize);
     const int64_t st = bytes_of(3 * L, B, C);
     const int64_t ch = bytes_of(L, 1, C);
     if (seq < 0 || st < 0 || ch < 0 || L > INT64_MAX / 3) return WKV_ERR_OVERFLOW;
@@ -266,7 +287,7 @@ wkv_status step_impl(int64_t L, int64_t B, int64_t C, const float *w, const floa
         if (overlap(ro, x)) return WKV_ERR_ALIAS;
     if (overlap(ro, ri) && state_out != (float *)state_in) return WKV_ERR_ALIAS;
     if (L * B > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
-    const StepArgs a{L, B, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr};
+    const StepArgs a{L, B, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr, io};
     return from_hip(wkv::launch_step(a, stream));
 }
 
@@ -301,7 +322,7 @@ WKV_API wkv_status wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float *
                                   const float *state_in, float *state_out,
                                   const wkv_forward_plan *plan, hipStream_t stream) {
     return forward_impl(B, T, C, w, u, k, v, nullptr, y, state_in, state_out, plan, false,
-                        stream);
+                        WKV_DTYPE_F32, stream);
 }
 
 WKV_API wkv_status wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float *w,
@@ -309,7 +330,17 @@ WKV_API wkv_status wkv_forward_gated(int64_t B, int64_t T, int64_t C, const floa
                                      const float *r, float *y, const float *state_in,
                                      float *state_out, const wkv_forward_plan *plan,
                                      hipStream_t stream) {
-    return forward_impl(B, T, C, w, u, k, v, r, y, state_in, state_out, plan, true, stream);
+    return forward_impl(B, T, C, w, u, k, v, r, y, state_in, state_out, plan, true,
+                        WKV_DTYPE_F32, stream);
+}
+
+WKV_API wkv_status wkv_forward_typed(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                     const float *w, const float *u, const void *k,
+                                     const void *v, const void *r, void *y,
+                                     const float *state_in, float *state_out,
+                                     const wkv_forward_plan *plan, hipStream_t stream) {
+    return forward_impl(B, T, C, w, u, k, v, r, y, state_in, state_out, plan, r != nullptr,
+                        (int)dtype, stream);
 }
 
 WKV_API wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
@@ -321,14 +352,23 @@ WKV_API wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, 
 WKV_API wkv_status wkv_step(int64_t L, int64_t B, int64_t C, const float *w, const float *u,
                             const float *k, const float *v, float *y, const float *state_in,
                             float *state_out, hipStream_t stream) {
-    return step_impl(L, B, C, w, u, k, v, nullptr, y, state_in, state_out, false, stream);
+    return step_impl(L, B, C, w, u, k, v, nullptr, y, state_in, state_out, false, WKV_DTYPE_F32,
+                     stream);
 }
 
 WKV_API wkv_status wkv_step_gated(int64_t L, int64_t B, int64_t C, const float *w,
                                   const float *u, const float *k, const float *v,
                                   const float *r, float *y, const float *state_in,
                                   float *state_out, hipStream_t stream) {
-    return step_impl(L, B, C, w, u, k, v, r, y, state_in, state_out, true, stream);
+    return step_impl(L, B, C, w, u, k, v, r, y, state_in, state_out, true, WKV_DTYPE_F32, stream);
+}
+
+WKV_API wkv_status wkv_step_typed(int64_t L, int64_t B, int64_t C, wkv_dtype dtype,
+                                  const float *w, const float *u, const void *k, const void *v,
+                                  const void *r, void *y, const float *state_in,
+                                  float *state_out, hipStream_t stream) {
+    return step_impl(L, B, C, w, u, k, v, r, y, state_in, state_out, r != nullptr, (int)dtype,
+                     stream);
 }
 
 WKV_API wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const float *mu,

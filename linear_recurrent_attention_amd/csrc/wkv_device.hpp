@@ -213,39 +213,90 @@ __device__ __forceinline__ float frame_token(float &A, float &Bs, const SegFrame
     return y;
 }
 
-// Consecutive rows of a row-major [rows][C] float tensor, seen by one wave.
+// Element formats of k, v, r and y.  Arithmetic and the state are always
+// float32; 16-bit inputs widen exactly, and outputs round to nearest even.
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9 raw access)
+constexpr int kNT = 2;                    // cache-policy operand: non-temporal
+
+struct IoF32 {
+    using T = float;
+    static constexpr int kBytes = 4;
+    __device__ __forceinline__ static float to_f(T x) { return x; }
+    __device__ __forceinline__ static T from_f(float x) { return x; }
+    // The b32 buffer builtins move raw 32-bit words: bit-cast, never convert.
+    __device__ __forceinline__ static float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNT));
+    }
+    __device__ __forceinline__ static void st(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff, float x) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, kNT);
+    }
+};
+
+struct IoF16 {
+    using T = _Float16;
+    static constexpr int kBytes = 2;
+    __device__ __forceinline__ static float to_f(T x) { return (float)x; }
+    __device__ __forceinline__ static T from_f(float x) { return (T)x; }  // v_cvt_f16_f32, RNE
+    __device__ __forceinline__ static float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+        return (float)__builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kNT));
+    }
+    __device__ __forceinline__ static void st(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff, float x) {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f(x)), r,
+                                              voff, soff, kNT);
+    }
+};
+
+// bfloat16 is the upper half of a float32: widening is a shift; narrowing
+// rounds the dropped half to nearest, ties to even, and keeps NaN a NaN.
+struct IoBF16 {
+    using T = unsigned short;
+    static constexpr int kBytes = 2;
+    __device__ __forceinline__ static float to_f(T x) {
+        return __builtin_bit_cast(float, (uint32_t)x << 16);
+    }
+    __device__ __forceinline__ static T from_f(float x) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, x);
+        if ((u & 0x7fffffffu) > 0x7f800000u) return (T)((u >> 16) | 0x40u);
+        return (T)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+    __device__ __forceinline__ static float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+        return to_f(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kNT));
+    }
+    __device__ __forceinline__ static void st(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff, float x) {
+        __builtin_amdgcn_raw_buffer_store_b16(from_f(x), r, voff, soff, kNT);
+    }
+};
+
+// Consecutive rows of a row-major [rows][C] tensor of IO::T, seen by one wave.
 // `base` must be wave-uniform (it becomes a buffer descriptor in scalar
 // registers); `voff` is the lane's byte offset from `base` (its channel, plus a
 // whole number of rows when the lanes of a wave cover several row ranges) and
-// `rowb` = 4*C the row pitch.  Row j is addressed by the scalar offset j*rowb,
-// so an access is a single buffer instruction with one 32-bit vector offset.
-// Offsets stay below 2^32 bytes from `base`.  Accesses carry the non-temporal
-// hint: every k, v and y element is touched once.
-struct TileRows {
+// `rowb` = C * IO::kBytes the row pitch.  Row j is addressed by the scalar
+// offset j*rowb, so an access is a single buffer instruction with one 32-bit
+// vector offset.  Offsets stay below 2^32 bytes from `base`.  Accesses carry
+// the non-temporal hint: every k, v, r and y element is touched once.
+template <class IO>
+struct TileRowsT {
     __amdgpu_buffer_rsrc_t r;
     uint32_t voff;
     uint32_t rowb;
-    __device__ __forceinline__ TileRows(const float *base, uint32_t voff_, uint32_t rowb_)
-        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0,
+    __device__ __forceinline__ TileRowsT(const typename IO::T *base, uint32_t voff_,
+                                         uint32_t rowb_)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<typename IO::T *>(base), (short)0,
                                               (int)0xffffffffu, kBufferWord3)),
           voff(voff_), rowb(rowb_) {}
-    // The b32 buffer builtins move raw 32-bit words (unsigned int): bit-cast,
-    // never convert.
-    __device__ __forceinline__ float ld(int j) const {
-        return __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, (uint32_t)j * rowb, kNT));
-    }
+    __device__ __forceinline__ float ld(int j) const { return IO::ld(r, voff, (uint32_t)j * rowb); }
     __device__ __forceinline__ void st(int j, float x) const {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff,
-                                              (uint32_t)j * rowb, kNT);
+        IO::st(r, voff, (uint32_t)j * rowb, x);
     }
-
-    // Buffer descriptor word 3 for gfx9-family raw 32-bit accesses
-    // (DATA_FORMAT = 32 bits).
-    static constexpr int kBufferWord3 = 0x00020000;
-    // Cache-policy operand: non-temporal.
-    static constexpr int kNT = 2;
 };
+using TileRows = TileRowsT<IoF32>;
 
 // Receptance gate of the time-mixing block (RWKV architecture deep dive,
 // "RWKV architecture overview", block figure): sigmoid(r) = 1 / (1 + 2^{-r log2 e}).

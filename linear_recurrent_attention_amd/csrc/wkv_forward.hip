@@ -32,44 +32,46 @@ namespace wkv {
 // ---------------------------------------------------------------------------
 // One thread per lane.
 // ---------------------------------------------------------------------------
-// GATE: y = sigmoid(r) * wkv with r read beside k and v.
-template <bool SAFE, bool GATE>
-__device__ __forceinline__ void lane_sweep(int64_t T, int64_t C, const float *__restrict__ kp,
-                                           const float *__restrict__ vp,
-                                           const float *__restrict__ rp, float *__restrict__ yp,
-                                           Lane &L, const Chan &ch) {
+// GATE: y = sigmoid(r) * wkv with r read beside k and v.  IO: element format.
+template <bool SAFE, bool GATE, class IO>
+__device__ __forceinline__ void lane_sweep(int64_t T, int64_t C,
+                                           const typename IO::T *__restrict__ kp,
+                                           const typename IO::T *__restrict__ vp,
+                                           const typename IO::T *__restrict__ rp,
+                                           typename IO::T *__restrict__ yp, Lane &L,
+                                           const Chan &ch) {
     int64_t t = 0;
     constexpr int U8 = 8;
     for (; t + U8 <= T; t += U8) {
         float K[U8], V[U8], R[U8];
 #pragma unroll
         for (int j = 0; j < U8; ++j) {
-            K[j] = kp[(t + j) * C];
-            V[j] = vp[(t + j) * C];
-            if constexpr (GATE) R[j] = rp[(t + j) * C];
+            K[j] = IO::to_f(kp[(t + j) * C]);
+            V[j] = IO::to_f(vp[(t + j) * C]);
+            if constexpr (GATE) R[j] = IO::to_f(rp[(t + j) * C]);
         }
 #pragma unroll
         for (int j = 0; j < U8; ++j) {
             float yv = step<SAFE>(L, K[j] * kLog2e, V[j], ch);
             if constexpr (GATE) yv *= gate_of(R[j]);
-            yp[(t + j) * C] = yv;
+            yp[(t + j) * C] = IO::from_f(yv);
         }
     }
     for (; t < T; ++t) {
-        float yv = step<SAFE>(L, kp[t * C] * kLog2e, vp[t * C], ch);
-        if constexpr (GATE) yv *= gate_of(rp[t * C]);
-        yp[t * C] = yv;
+        float yv = step<SAFE>(L, IO::to_f(kp[t * C]) * kLog2e, IO::to_f(vp[t * C]), ch);
+        if constexpr (GATE) yv *= gate_of(IO::to_f(rp[t * C]));
+        yp[t * C] = IO::from_f(yv);
     }
 }
 
-template <bool GATE>
+template <bool GATE, class IO>
 __global__ __launch_bounds__(256) void fwd_lane_kernel(int64_t B, int64_t T, int64_t C,
                                                        const float *__restrict__ w,
                                                        const float *__restrict__ u,
-                                                       const float *__restrict__ k,
-                                                       const float *__restrict__ v,
-                                                       const float *__restrict__ r,
-                                                       float *__restrict__ y,
+                                                       const typename IO::T *__restrict__ k,
+                                                       const typename IO::T *__restrict__ v,
+                                                       const typename IO::T *__restrict__ r,
+                                                       typename IO::T *__restrict__ y,
                                                        const float *__restrict__ s_in,
                                                        float *__restrict__ s_out) {
     const int64_t lane = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -85,11 +87,11 @@ __global__ __launch_bounds__(256) void fwd_lane_kernel(int64_t B, int64_t T, int
         L = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
                     o_in(s_in[(2 * B + bb) * C + c]));
     const int64_t base = bb * T * C + c;
-    const float *rp = GATE ? r + base : nullptr;
+    const typename IO::T *rp = GATE ? r + base : nullptr;
     if (wave_fast)
-        lane_sweep<false, GATE>(T, C, k + base, v + base, rp, y + base, L, ch);
+        lane_sweep<false, GATE, IO>(T, C, k + base, v + base, rp, y + base, L, ch);
     else
-        lane_sweep<true, GATE>(T, C, k + base, v + base, rp, y + base, L, ch);
+        lane_sweep<true, GATE, IO>(T, C, k + base, v + base, rp, y + base, L, ch);
     if (s_out) {
         s_out[(0 * B + bb) * C + c] = L.a;
         s_out[(1 * B + bb) * C + c] = L.b;
@@ -126,9 +128,9 @@ struct SegShared {
 
 // This lane's LS tokens of one tile, rows t0.. of its segment (rows past the end
 // of the sequence are not read and hold 0).
-template <int LS, bool FULL>
-__device__ __forceinline__ void seg_load(float (&K)[LS], float (&V)[LS], const TileRows &kr,
-                                         const TileRows &vr, int64_t t0, int64_t T) {
+template <int LS, bool FULL, class TR>
+__device__ __forceinline__ void seg_load(float (&K)[LS], float (&V)[LS], const TR &kr,
+                                         const TR &vr, int64_t t0, int64_t T) {
     if (FULL || t0 + LS <= T) {
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
@@ -145,8 +147,8 @@ __device__ __forceinline__ void seg_load(float (&K)[LS], float (&V)[LS], const T
 }
 
 // The same rows of the gate's receptance.
-template <int LS, bool FULL>
-__device__ __forceinline__ void seg_load_r(float (&R)[LS], const TileRows &rr, int64_t t0,
+template <int LS, bool FULL, class TR>
+__device__ __forceinline__ void seg_load_r(float (&R)[LS], const TR &rr, int64_t t0,
                                            int64_t T) {
 #pragma unroll
     for (int j = 0; j < LS; ++j) R[j] = (FULL || t0 + j < T) ? rr.ld(j) : 0.0f;
@@ -167,11 +169,11 @@ struct SegGeom {
 // One tile: this lane's LS tokens of k, v are in registers (K, V); `carry` is
 // the state before the tile and leaves as the state after it.  FULL: T is a
 // whole number of tiles, so no token test is needed (straight-line code).
-template <int NW, int LS, int CW, bool SAFE, bool FULL, bool GATE>
+template <int NW, int LS, int CW, bool SAFE, bool FULL, bool GATE, class IO>
 __device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], const float (&V)[LS],
                                          const float (&Rg)[GATE ? LS : 1], Lane &carry, const SegGeom<NW, LS, CW> &G, int64_t B,
                                          int64_t T, int64_t C, int64_t bb, int64_t c, bool active,
-                                         const Chan &ch, float *yseq, uint32_t voff,
+                                         const Chan &ch, typename IO::T *yseq, uint32_t voff,
                                          float *__restrict__ s_out, SegShared<NW> &sh) {
     using Geo = SegGeom<NW, LS, CW>;
     const int64_t t0 = tile * Geo::TT + (int64_t)G.seg * LS;
@@ -211,7 +213,7 @@ __device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], con
 
     // (3) re-sweep from the prefix state, emitting y
     const int64_t tw = tile * Geo::TT + (int64_t)G.wave * Geo::SPW * LS;  // wave's first row
-    const TileRows yr(yseq + tw * C, voff, (uint32_t)(C * 4));
+    const TileRowsT<IO> yr(yseq + tw * C, voff, (uint32_t)(C * IO::kBytes));
     if (FULL || t0 + LS <= T) {
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
@@ -240,22 +242,22 @@ __device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], con
 // next tile's k, v loaded while the current one is processed.  Two register
 // sets take turns (A holds even tiles, B odd ones) so that no register copy
 // ties a prefetch to the current tile's arithmetic.
-template <int NW, int LS, int CW, bool SAFE, bool FULL, bool GATE>
+template <int NW, int LS, int CW, bool SAFE, bool FULL, bool GATE, class IO>
 __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_t bb, int64_t c,
                                          bool active, const Chan &ch,
-                                         const SegGeom<NW, LS, CW> &G, const float *kseq,
-                                         const float *vseq, const float *rseq, float *yseq,
-                                         uint32_t voff,
+                                         const SegGeom<NW, LS, CW> &G, const typename IO::T *kseq,
+                                         const typename IO::T *vseq, const typename IO::T *rseq,
+                                         typename IO::T *yseq, uint32_t voff,
                                          const float *__restrict__ s_in, float *__restrict__ s_out,
                                          SegShared<NW> &sh) {
     using Geo = SegGeom<NW, LS, CW>;
     const int64_t ntiles = (T + Geo::TT - 1) / Geo::TT;
-    const uint32_t rowb = (uint32_t)(C * 4);
+    const uint32_t rowb = (uint32_t)(C * IO::kBytes);
+    using TR = TileRowsT<IO>;
     constexpr int NR = GATE ? LS : 1;
     auto load = [&](float (&K)[LS], float (&V)[LS], int64_t tile) {
         const int64_t tw = tile * Geo::TT + (int64_t)G.wave * Geo::SPW * LS;
-        seg_load<LS, FULL>(K, V, TileRows(kseq + tw * C, voff, rowb),
-                           TileRows(vseq + tw * C, voff, rowb),
+        seg_load<LS, FULL>(K, V, TR(kseq + tw * C, voff, rowb), TR(vseq + tw * C, voff, rowb),
                            tile * Geo::TT + (int64_t)G.seg * LS, T);
     };
     // The receptance of a tile is loaded just before the next tile's k and v:
@@ -264,7 +266,7 @@ __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_
     auto load_r = [&](float (&R)[NR], int64_t tile) {
         if constexpr (GATE) {
             const int64_t tw = tile * Geo::TT + (int64_t)G.wave * Geo::SPW * LS;
-            seg_load_r<LS, FULL>(R, TileRows(rseq + tw * C, voff, rowb),
+            seg_load_r<LS, FULL>(R, TR(rseq + tw * C, voff, rowb),
                                  tile * Geo::TT + (int64_t)G.seg * LS, T);
         } else {
             R[0] = 0.0f;
@@ -283,28 +285,28 @@ __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_
     for (; tile + 1 < ntiles; tile += 2) {
         load_r(Rc, tile);
         load(KB, VB, tile + 1);
-        seg_tile<NW, LS, CW, SAFE, FULL, GATE>(tile, KA, VA, Rc, carry, G, B, T, C, bb, c, active,
+        seg_tile<NW, LS, CW, SAFE, FULL, GATE, IO>(tile, KA, VA, Rc, carry, G, B, T, C, bb, c, active,
                                                ch, yseq, voff, s_out, sh);
         load_r(Rc, tile + 1);
         if (tile + 2 < ntiles) load(KA, VA, tile + 2);
-        seg_tile<NW, LS, CW, SAFE, FULL, GATE>(tile + 1, KB, VB, Rc, carry, G, B, T, C, bb, c,
+        seg_tile<NW, LS, CW, SAFE, FULL, GATE, IO>(tile + 1, KB, VB, Rc, carry, G, B, T, C, bb, c,
                                                active, ch, yseq, voff, s_out, sh);
     }
     if (tile < ntiles) {
         load_r(Rc, tile);
-        seg_tile<NW, LS, CW, SAFE, FULL, GATE>(tile, KA, VA, Rc, carry, G, B, T, C, bb, c, active,
+        seg_tile<NW, LS, CW, SAFE, FULL, GATE, IO>(tile, KA, VA, Rc, carry, G, B, T, C, bb, c, active,
                                                ch, yseq, voff, s_out, sh);
     }
 }
 
-template <int NW, int LS, int CW, bool GATE>
+template <int NW, int LS, int CW, bool GATE, class IO>
 __global__ __launch_bounds__(NW * 64) void fwd_seg_kernel(int64_t B, int64_t T, int64_t C,
                                                           const float *__restrict__ w,
                                                           const float *__restrict__ u,
-                                                          const float *__restrict__ k,
-                                                          const float *__restrict__ v,
-                                                          const float *__restrict__ r,
-                                                          float *__restrict__ y,
+                                                          const typename IO::T *__restrict__ k,
+                                                          const typename IO::T *__restrict__ v,
+                                                          const typename IO::T *__restrict__ r,
+                                                          typename IO::T *__restrict__ y,
                                                           const float *__restrict__ s_in,
                                                           float *__restrict__ s_out) {
     using Geo = SegGeom<NW, LS, CW>;
@@ -327,21 +329,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_seg_kernel(int64_t B, int64_t T, 
     // channel and, when a wave holds several segments, its segment's rows.
     // Inactive lanes read the group's first channel and never store.
     const int64_t base = bb * T * C + g * CW;
-    const uint32_t voff = (active ? (uint32_t)ch_local * 4u : 0u) +
-                          (uint32_t)(G.lane / CW) * (uint32_t)LS * (uint32_t)(C * 4);
+    const uint32_t voff = (active ? (uint32_t)(ch_local * IO::kBytes) : 0u) +
+                          (uint32_t)(G.lane / CW) * (uint32_t)LS * (uint32_t)(C * IO::kBytes);
     const bool full = T % Geo::TT == 0;
-    const float *rs = GATE ? r + base : nullptr;
+    const typename IO::T *rs = GATE ? r + base : nullptr;
     if (fast && full)
-        seg_body<NW, LS, CW, false, true, GATE>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+        seg_body<NW, LS, CW, false, true, GATE, IO>(B, T, C, bb, c, active, ch, G, k + base, v + base,
                                                 rs, y + base, voff, s_in, s_out, sh);
     else if (fast)
-        seg_body<NW, LS, CW, false, false, GATE>(B, T, C, bb, c, active, ch, G, k + base,
+        seg_body<NW, LS, CW, false, false, GATE, IO>(B, T, C, bb, c, active, ch, G, k + base,
                                                  v + base, rs, y + base, voff, s_in, s_out, sh);
     else if (full)
-        seg_body<NW, LS, CW, true, true, GATE>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+        seg_body<NW, LS, CW, true, true, GATE, IO>(B, T, C, bb, c, active, ch, G, k + base, v + base,
                                                rs, y + base, voff, s_in, s_out, sh);
     else
-        seg_body<NW, LS, CW, true, false, GATE>(B, T, C, bb, c, active, ch, G, k + base, v + base,
+        seg_body<NW, LS, CW, true, false, GATE, IO>(B, T, C, bb, c, active, ch, G, k + base, v + base,
                                                 rs, y + base, voff, s_in, s_out, sh);
 }
 
@@ -363,39 +365,55 @@ __global__ __launch_bounds__(256) void state_copy_kernel(int64_t n, const float 
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-hipError_t launch_forward_lane(const FwdArgs &a, hipStream_t st) {
-    const int64_t lanes = a.B * a.C;
-    const int64_t grid = (lanes + 255) / 256;
-    if (a.r)
-        hipLaunchKernelGGL(fwd_lane_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st, a.B,
-                           a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y, a.s_in, a.s_out);
-    else
-        hipLaunchKernelGGL(fwd_lane_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st, a.B,
-                           a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y, a.s_in, a.s_out);
+template <bool GATE, class IO>
+static hipError_t launch_lane(const FwdArgs &a, hipStream_t st) {
+    using T = typename IO::T;
+    const int64_t grid = (a.B * a.C + 255) / 256;
+    hipLaunchKernelGGL((fwd_lane_kernel<GATE, IO>), dim3((unsigned)grid), dim3(256), 0, st, a.B,
+                       a.T, a.C, a.w, a.u, (const T *)a.k, (const T *)a.v, (const T *)a.r,
+                       (T *)a.y, a.s_in, a.s_out);
     return hipGetLastError();
 }
 
-template <int NW, int LS, int CW>
+template <bool GATE>
+static hipError_t launch_lane_io(const FwdArgs &a, hipStream_t st) {
+    switch (a.io) {
+        case kIoF32: return launch_lane<GATE, IoF32>(a, st);
+        case kIoF16: return launch_lane<GATE, IoF16>(a, st);
+        case kIoBF16: return launch_lane<GATE, IoBF16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_forward_lane(const FwdArgs &a, hipStream_t st) {
+    return a.r ? launch_lane_io<true>(a, st) : launch_lane_io<false>(a, st);
+}
+
+template <int NW, int LS, int CW, bool GATE, class IO>
 static hipError_t launch_seg(const FwdArgs &a, hipStream_t st) {
+    using T = typename IO::T;
     const int64_t grid = a.B * ((a.C + CW - 1) / CW);
-    if (a.r)
-        hipLaunchKernelGGL((fwd_seg_kernel<NW, LS, CW, true>), dim3((unsigned)grid),
-                           dim3(NW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y,
-                           a.s_in, a.s_out);
-    else
-        hipLaunchKernelGGL((fwd_seg_kernel<NW, LS, CW, false>), dim3((unsigned)grid),
-                           dim3(NW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y,
-                           a.s_in, a.s_out);
+    hipLaunchKernelGGL((fwd_seg_kernel<NW, LS, CW, GATE, IO>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, (const T *)a.k,
+                       (const T *)a.v, (const T *)a.r, (T *)a.y, a.s_in, a.s_out);
     return hipGetLastError();
+}
+
+template <int NW, int LS, int CW, class IO>
+static hipError_t launch_seg_gate(const FwdArgs &a, hipStream_t st) {
+    return a.r ? launch_seg<NW, LS, CW, true, IO>(a, st) : launch_seg<NW, LS, CW, false, IO>(a, st);
 }
 
 // Compiled variants of the segmented kernel, keyed by (segments per tile,
-// tokens per segment, channels per workgroup).
+// tokens per segment, channels per workgroup); the 16-bit formats have the
+// default variant only.
 #define WKV_SEG_VARIANTS(X)                                                            \
     X(16, 16, 64) X(16, 8, 64) X(8, 16, 64) X(8, 32, 64) X(4, 32, 64) X(16, 16, 32)   \
     X(32, 8, 32) X(16, 8, 32) X(16, 16, 16) X(32, 8, 16)
 
-bool forward_seg_supported(int nseg, int ls, int cw) {
+bool forward_seg_supported(int nseg, int ls, int cw, int io) {
+    if (io == kIoF16 || io == kIoBF16) return nseg == 16 && ls == 16 && cw == 64;
+    if (io != kIoF32) return false;
 #define X(NSEG, LS, CW) if (nseg == NSEG && ls == LS && cw == CW) return true;
     WKV_SEG_VARIANTS(X)
 #undef X
@@ -403,8 +421,11 @@ bool forward_seg_supported(int nseg, int ls, int cw) {
 }
 
 hipError_t launch_forward_seg(const FwdArgs &a, int nseg, int ls, int cw, hipStream_t st) {
+    if (!forward_seg_supported(nseg, ls, cw, a.io)) return hipErrorInvalidValue;
+    if (a.io == kIoF16) return launch_seg_gate<16, 16, 64, IoF16>(a, st);
+    if (a.io == kIoBF16) return launch_seg_gate<16, 16, 64, IoBF16>(a, st);
 #define X(NSEG, LS, CW) \
-    if (nseg == NSEG && ls == LS && cw == CW) return launch_seg<NSEG * CW / 64, LS, CW>(a, st);
+    if (nseg == NSEG && ls == LS && cw == CW) return launch_seg_gate<NSEG * CW / 64, LS, CW, IoF32>(a, st);
     WKV_SEG_VARIANTS(X)
 #undef X
     return hipErrorInvalidValue;

@@ -8,24 +8,32 @@
 
 namespace wkv {
 
+// Element format of k, v, r and y (the values of wkv_dtype); w, u and the
+// state are always float32.
+constexpr int kIoF32 = 0, kIoF16 = 1, kIoBF16 = 2;
+
 // r: receptance of the time-mixing gate, same layout as k; NULL: y = wkv,
-// else y = sigmoid(r) * wkv.
+// else y = sigmoid(r) * wkv.  k, v, r, y hold elements of format `io`.
 struct FwdArgs {
     int64_t B, T, C;
-    const float *w, *u, *k, *v;
-    float *y;
+    const float *w, *u;
+    const void *k, *v;
+    void *y;
     const float *s_in;
     float *s_out;
-    const float *r;
+    const void *r;
+    int io;
 };
 
 struct StepArgs {
     int64_t L, B, C;
-    const float *w, *u, *k, *v;
-    float *y;
+    const float *w, *u;
+    const void *k, *v;
+    void *y;
     const float *s_in;
     float *s_out;
-    const float *r;
+    const void *r;
+    int io;
 };
 
 struct ShiftArgs {
@@ -43,7 +51,8 @@ struct BwdArgs {
 
 // forward (wkv_forward.hip)
 hipError_t launch_forward_lane(const FwdArgs &a, hipStream_t st);
-bool forward_seg_supported(int nseg, int ls, int cw);
+// (16-bit formats: compiled for the default variant only)
+bool forward_seg_supported(int nseg, int ls, int cw, int io);
 hipError_t launch_forward_seg(const FwdArgs &a, int nseg, int ls, int cw, hipStream_t st);
 hipError_t launch_state_copy(int64_t lanes, const float *s_in, float *s_out, hipStream_t st);
 
@@ -54,8 +63,9 @@ struct LookbackScratch {
 };
 // (cg, ns, ls): groups of 64 channels side by side, segments stacked, tokens
 // per segment
-// (the gated kernel is compiled for the variants with ls <= 16 only)
-bool forward_lookback_supported(int cg, int ns, int ls, bool gated);
+// (the gated kernel is compiled for the variants with ls <= 16 only, and the
+// 16-bit formats for the variants the automatic choice uses)
+bool forward_lookback_supported(int cg, int ns, int ls, bool gated, int io);
 bool lookback_grid_ok(int64_t B, int64_t T, int64_t C, int cg, int ns, int ls);
 size_t lookback_scratch_bytes(int64_t B, int64_t T, int64_t C, int ns, int ls);
 hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,

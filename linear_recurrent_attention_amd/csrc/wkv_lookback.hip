@@ -115,11 +115,12 @@ struct LbWave {
 // FULL: the whole block lies inside the sequence, so no token needs a bounds
 // test (a workgroup-uniform property: only the last block can be partial).
 // GATE: Rg holds the wave's receptance rows and y is sigmoid(r) * wkv.
-template <int CG, int NS, int LS, bool SAFE, bool FULL, bool GATE>
+// IO: element format of y (IoF32, IoF16, IoBF16).
+template <int CG, int NS, int LS, bool SAFE, bool FULL, bool GATE, class IO>
 __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const Chan &ch,
                                         const LbWave &q, const float (&K)[LS], const float (&V)[LS],
                                         const float (&Rg)[GATE ? LS : 1],
-                                        float *yseq, const float *__restrict__ s_in,
+                                        typename IO::T *yseq, const float *__restrict__ s_in,
                                         float *__restrict__ s_out, Word *aggs, Word *incls,
                                         uint32_t epoch, LbShared<CG, NS> &sh) {
     constexpr int TB = NS * LS;
@@ -237,7 +238,7 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
     for (int w = 0; w < s; ++w) compose(R, lds_lane(sh.s, w, g, lane), ch.W, (float)LS);
     const float poison = failed ? __builtin_nanf("") : 0.0f;
     if (q.gok) {
-        const TileRows yr(yseq + q.t0 * C, q.voff, q.rowb);
+        const TileRowsT<IO> yr(yseq + q.t0 * C, q.voff, q.rowb);
         bool framed = false;
         if constexpr (FULL && !SAFE) {
             SegFrame f;
@@ -283,13 +284,13 @@ constexpr int lb_waves_per_simd(int ls, bool gate) {
     return gate ? (ls <= 8 ? 7 : 5) : (ls <= 8 ? 8 : (ls <= 16 ? 6 : 4));
 }
 
-template <int CG, int NS, int LS, bool GATE>
+template <int CG, int NS, int LS, bool GATE, class IO>
 __global__ __launch_bounds__(CG * NS * 64)
 __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookback_kernel(
     int64_t B, int64_t T, int64_t C, const float *__restrict__ w, const float *__restrict__ u,
-    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ r,
-    float *__restrict__ y, const float *s_in, float *s_out, Word *aggs, Word *incls,
-    uint32_t epoch, uint32_t nsets) {
+    const typename IO::T *__restrict__ k, const typename IO::T *__restrict__ v,
+    const typename IO::T *__restrict__ r, typename IO::T *__restrict__ y, const float *s_in,
+    float *s_out, Word *aggs, Word *incls, uint32_t epoch, uint32_t nsets) {
     constexpr int TB = NS * LS;
     __shared__ LbShared<CG, NS> sh;
     LbWave q;
@@ -310,8 +311,8 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
     q.c = q.grp * 64 + q.lane;
     q.active = q.gok && q.c < C;
     q.t0 = q.j * TB + (int64_t)q.s * LS;
-    q.rowb = (uint32_t)(C * 4);
-    q.voff = q.active ? (uint32_t)q.lane * 4u : 0u;
+    q.rowb = (uint32_t)(C * IO::kBytes);
+    q.voff = q.active ? (uint32_t)(q.lane * IO::kBytes) : 0u;
     const int64_t base = q.bb * T * C + (q.gok ? q.grp * 64 : 0);
 
     // channel constants, then this wave's tokens, all issued before any wait:
@@ -331,7 +332,8 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
         const int64_t left = T - 1 - t0c;
         const uint32_t tmax =
             __builtin_amdgcn_readfirstlane(left < LS - 1 ? (uint32_t)left : (uint32_t)(LS - 1));
-        const TileRows kr(k + base + t0c * C, q.voff, q.rowb), vr(v + base + t0c * C, q.voff, q.rowb);
+        const TileRowsT<IO> kr(k + base + t0c * C, q.voff, q.rowb);
+        const TileRowsT<IO> vr(v + base + t0c * C, q.voff, q.rowb);
 #pragma unroll
         for (int t = 0; t < LS; ++t) {
             const uint32_t row = (uint32_t)t < tmax ? (uint32_t)t : tmax;
@@ -339,7 +341,7 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
             V[t] = vr.ld((int)row);
         }
         if constexpr (GATE) {
-            const TileRows rr(r + base + t0c * C, q.voff, q.rowb);
+            const TileRowsT<IO> rr(r + base + t0c * C, q.voff, q.rowb);
 #pragma unroll
             for (int t = 0; t < LS; ++t)
                 Rg[t] = rr.ld((int)((uint32_t)t < tmax ? (uint32_t)t : tmax));
@@ -357,17 +359,17 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
     const bool full = (q.j + 1) * TB <= T;  // the whole block lies inside the sequence
     if (fast) {
         if (full)
-            lb_body<CG, NS, LS, false, true, GATE>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
+            lb_body<CG, NS, LS, false, true, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
                                                    s_out, aggs, incls, epoch, sh);
         else
-            lb_body<CG, NS, LS, false, false, GATE>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
+            lb_body<CG, NS, LS, false, false, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
                                                     s_out, aggs, incls, epoch, sh);
     } else {
         if (full)
-            lb_body<CG, NS, LS, true, true, GATE>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
+            lb_body<CG, NS, LS, true, true, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
                                                   s_out, aggs, incls, epoch, sh);
         else
-            lb_body<CG, NS, LS, true, false, GATE>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
+            lb_body<CG, NS, LS, true, false, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
                                                    s_out, aggs, incls, epoch, sh);
     }
 }
@@ -377,7 +379,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // (CG, NS, LS) variants: CG groups of 64 channels side by side, NS segments of
 // LS tokens stacked.  The gated kernel holds a third row array (r), so it is
-// compiled only where LS <= 16 leaves the registers for it.
+// compiled only where LS <= 16 leaves the registers for it.  The 16-bit
+// formats are compiled for the variants the automatic choice uses.
 #define WKV_LB_VARIANTS(X) \
     X(1, 4, 16)            \
     X(1, 8, 32)            \
@@ -391,28 +394,43 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
     X(2, 4, 8)             \
     X(4, 2, 16)            \
     X(4, 2, 8)
+#define WKV_LB_VARIANTS_16BIT(X) \
+    X(1, 4, 16)                  \
+    X(1, 4, 32)                  \
+    X(1, 8, 16)
 
 constexpr int lb_key(int cg, int ns, int ls) { return (cg * 64 + ns) * 1024 + ls; }
 
-template <int CG, int NS, int LS, bool GATE>
+template <int CG, int NS, int LS, bool GATE, class IO>
 hipError_t launch_lb(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st) {
+    using T = typename IO::T;
     const int64_t ngroups = (a.C + 63) / 64;
     const int64_t nsets = (ngroups + CG - 1) / CG;
     const int64_t nblocks = (a.T + NS * LS - 1) / (NS * LS);
     const int64_t nslots = nblocks * a.B * ngroups;
     Word *aggs = (Word *)sc.base;
     Word *incls = (Word *)((char *)sc.base + align_up((size_t)nslots * kSlotWords * sizeof(Word)));
-    hipLaunchKernelGGL((fwd_lookback_kernel<CG, NS, LS, GATE>),
+    hipLaunchKernelGGL((fwd_lookback_kernel<CG, NS, LS, GATE, IO>),
                        dim3((unsigned)(nsets * a.B * nblocks)), dim3(CG * NS * 64), 0, st, a.B,
-                       a.T, a.C, a.w, a.u, a.k, a.v, a.r, a.y, a.s_in, a.s_out, aggs, incls,
-                       sc.epoch, (uint32_t)nsets);
+                       a.T, a.C, a.w, a.u, (const T *)a.k, (const T *)a.v, (const T *)a.r,
+                       (T *)a.y, a.s_in, a.s_out, aggs, incls, sc.epoch, (uint32_t)nsets);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool forward_lookback_supported(int cg, int ns, int ls, bool gated) {
+bool forward_lookback_supported(int cg, int ns, int ls, bool gated, int io) {
     if (gated && ls > 16) return false;
+    if (io != kIoF32) {
+        switch (lb_key(cg, ns, ls)) {
+#define X(CG, NS, LS) case lb_key(CG, NS, LS):
+            WKV_LB_VARIANTS_16BIT(X)
+#undef X
+            return io == kIoF16 || io == kIoBF16;
+            default:
+                return false;
+        }
+    }
     switch (lb_key(cg, ns, ls)) {
 #define X(CG, NS, LS) case lb_key(CG, NS, LS):
         WKV_LB_VARIANTS(X)
@@ -436,16 +454,32 @@ size_t lookback_scratch_bytes(int64_t B, int64_t T, int64_t C, int ns, int ls) {
     return 2 * align_up((size_t)nslots * kSlotWords * sizeof(Word));
 }
 
+template <int CG, int NS, int LS, class IO>
+hipError_t launch_lb_gate(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st) {
+    // (a gated call never reaches LS > 16: forward_lookback_supported refuses it)
+    if (a.r) return launch_lb<CG, NS, (LS <= 16 ? LS : 16), true, IO>(a, sc, st);
+    return launch_lb<CG, NS, LS, false, IO>(a, sc, st);
+}
+
 hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,
                                    const LookbackScratch &sc, hipStream_t st) {
-    const bool gated = a.r != nullptr;
-    if (gated && ls > 16) return hipErrorInvalidValue;
+    if (!forward_lookback_supported(cg, ns, ls, a.r != nullptr, a.io)) return hipErrorInvalidValue;
+    if (a.io == kIoF32) {
+        switch (lb_key(cg, ns, ls)) {
+#define X(CG, NS, LS) \
+    case lb_key(CG, NS, LS): return launch_lb_gate<CG, NS, LS, IoF32>(a, sc, st);
+            WKV_LB_VARIANTS(X)
+#undef X
+            default:
+                return hipErrorInvalidValue;
+        }
+    }
     switch (lb_key(cg, ns, ls)) {
-#define X(CG, NS, LS)                                                              \
-    case lb_key(CG, NS, LS):                                                      \
-        return gated ? launch_lb<CG, NS, (LS <= 16 ? LS : 16), true>(a, sc, st)    \
-                     : launch_lb<CG, NS, LS, false>(a, sc, st);
-        WKV_LB_VARIANTS(X)
+#define X(CG, NS, LS)                                                      \
+    case lb_key(CG, NS, LS):                                              \
+        return a.io == kIoF16 ? launch_lb_gate<CG, NS, LS, IoF16>(a, sc, st) \
+                              : launch_lb_gate<CG, NS, LS, IoBF16>(a, sc, st);
+        WKV_LB_VARIANTS_16BIT(X)
 #undef X
         default:
             return hipErrorInvalidValue;

@@ -8,7 +8,8 @@ float32 tensor on a HIP device, the call raises.
 
 Layouts (C-contiguous, channel fastest):
     w, u            [C]          (wkv_step: [L][C])
-    k, v, r, y, dy  [B][T][C]    (wkv_step: [L][B][C])
+    k, v, r, y, dy  [B][T][C]    (wkv_step: [L][B][C]); float32, or float16 /
+                                 bfloat16 in the *_typed calls
     state           [3][B][C]    planes a, b, o   (wkv_step: [L][3][B][C])
     token shift     mu [M][C], x [B][T][C], x_prev [B][C], out [M][B][T][C]
 """
@@ -40,7 +41,15 @@ WKV_KERNEL_LOOKBACK = 3
 
 EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backward",
             "wkv_status_string", "wkv_forward_ex", "wkv_forward_plan_auto",
-            "wkv_forward_gated", "wkv_step_gated", "wkv_token_shift")
+            "wkv_forward_gated", "wkv_step_gated", "wkv_token_shift", "wkv_forward_typed",
+            "wkv_step_typed")
+
+# wkv_dtype values
+WKV_DTYPE_F32 = 0
+WKV_DTYPE_F16 = 1
+WKV_DTYPE_BF16 = 2
+_DTYPES = {torch.float32: WKV_DTYPE_F32, torch.float16: WKV_DTYPE_F16,
+           torch.bfloat16: WKV_DTYPE_BF16}
 
 WKV_TOKEN_SHIFT_MAX_MIXES = 8
 
@@ -88,6 +97,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_step_gated.restype = ctypes.c_int
     lib.wkv_token_shift.argtypes = [i64, i64, i64, i64] + [vp] * 5 + [vp]
     lib.wkv_token_shift.restype = ctypes.c_int
+    lib.wkv_forward_typed.argtypes = ([i64, i64, i64, ctypes.c_int] + [vp] * 8 +
+                                      [ctypes.POINTER(ForwardPlan), vp])
+    lib.wkv_forward_typed.restype = ctypes.c_int
+    lib.wkv_step_typed.argtypes = [i64, i64, i64, ctypes.c_int] + [vp] * 8 + [vp]
+    lib.wkv_step_typed.restype = ctypes.c_int
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -98,13 +112,13 @@ def wkv_status_string(status: int) -> str:
     return load_library().wkv_status_string(int(status)).decode()
 
 
-def _ptr(t):
+def _ptr(t, dtype=torch.float32):
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError("expected a torch.Tensor")
-    if t.dtype != torch.float32:
-        raise TypeError(f"expected float32, got {t.dtype}")
+    if t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
     if t.numel() > 0 and not t.is_cuda:
         raise TypeError("expected a tensor on a HIP device")
     if not t.is_contiguous():
@@ -177,6 +191,27 @@ def wkv_forward_gated(w, u, k, v, r, y=None, state_in=None, state_out=None, stre
     return y, state_out
 
 
+def wkv_forward_typed(w, u, k, v, r=None, y=None, state_in=None, state_out=None, stream=None,
+                      plan=None):
+    """Forward with k, v (r) and y in k's dtype (float32, float16 or bfloat16);
+    w, u and the state float32.  With r, y = sigmoid(r) * wkv.  Returns
+    (y, state_out)."""
+    if k.dtype not in _DTYPES:
+        raise TypeError(f"unsupported element type {k.dtype}")
+    dt = k.dtype
+    B, T, C = _bundle_shape(k, state_in)
+    if y is None:
+        y = torch.empty_like(k)
+    if state_out is True:
+        state_out = torch.empty((3, B, C), device=k.device, dtype=torch.float32)
+    st = load_library().wkv_forward_typed(B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt),
+                                          _ptr(v, dt), _ptr(r, dt), _ptr(y, dt),
+                                          _ptr(state_in), _ptr(state_out), _plan(plan),
+                                          _stream(stream))
+    _check("wkv_forward_typed", st)
+    return y, state_out
+
+
 def wkv_forward_plan_auto(B: int, T: int, C: int):
     p = ForwardPlan()
     _check("wkv_forward_plan_auto", load_library().wkv_forward_plan_auto(B, T, C, ctypes.byref(p)))
@@ -211,6 +246,25 @@ def wkv_step_gated(w, u, k, v, r, state_in, state_out=None, y=None, stream=None)
     st = load_library().wkv_step_gated(L, B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
                                        _ptr(y), _ptr(state_in), _ptr(state_out), _stream(stream))
     _check("wkv_step_gated", st)
+    return y, state_out
+
+
+def wkv_step_typed(w, u, k, v, state_in, r=None, state_out=None, y=None, stream=None):
+    """``wkv_step`` with k, v (r) and y in k's dtype; w, u, state float32."""
+    if k.dim() != 3:
+        raise ValueError("k must be [L][B][C]")
+    if k.dtype not in _DTYPES:
+        raise TypeError(f"unsupported element type {k.dtype}")
+    dt = k.dtype
+    L, B, C = (int(x) for x in k.shape)
+    if y is None:
+        y = torch.empty_like(k)
+    if state_out is None:
+        state_out = state_in
+    st = load_library().wkv_step_typed(L, B, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt),
+                                       _ptr(v, dt), _ptr(r, dt), _ptr(y, dt), _ptr(state_in),
+                                       _ptr(state_out), _stream(stream))
+    _check("wkv_step_typed", st)
     return y, state_out
 
 

@@ -165,6 +165,36 @@ def test_gated_calls_reject_invalid_arguments(lib):
     assert sg(-2, 2, 4, *base, vp(P + 0x500000), vp(P + 0x300000), si, so, None) == W.WKV_ERR_DIM
 
 
+def test_typed_calls_reject_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    w, u, k, v = vp(P), vp(P + 0x1000), vp(P + 0x100000), vp(P + 0x10000000)
+    y = vp(P + 0x20000000)
+    f = lib.wkv_forward_typed
+    assert f(2, 8, 16, 7, w, u, k, v, None, y, None, None, None, None) == W.WKV_ERR_UNSUPPORTED
+    assert f(2, 8, 16, W.WKV_DTYPE_BF16, w, u, None, v, None, y, None, None, None,
+             None) == W.WKV_ERR_NULL
+    # 2 x 8 x 16 bf16 elements are 512 bytes: y 300 bytes into k overlaps it
+    assert f(2, 8, 16, W.WKV_DTYPE_BF16, w, u, k, v, None, vp(P + 0x100000 + 300), None, None,
+             None, None) == W.WKV_ERR_ALIAS
+    # 16-bit formats: only the variants the automatic choice uses are compiled
+    for plan in ((W.WKV_KERNEL_SEGMENTED, 16, 8, 64), (W.WKV_KERNEL_SEGMENTED, 16, 16, 32),
+                 (W.WKV_KERNEL_LOOKBACK, 8, 8, 64), (W.WKV_KERNEL_LOOKBACK, 4, 16, 128)):
+        p = W.ForwardPlan(*plan)
+        for dt in (W.WKV_DTYPE_F16, W.WKV_DTYPE_BF16):
+            assert f(2, 8, 16, dt, w, u, k, v, None, y, None, None, ctypes.byref(p),
+                     None) == W.WKV_ERR_UNSUPPORTED, (plan, dt)
+    p = W.ForwardPlan(W.WKV_KERNEL_LOOKBACK, 4, 32, 64)     # no gated 4x32 variant
+    assert f(2, 8, 16, W.WKV_DTYPE_F16, w, u, k, v, vp(P + 0x30000000), y, None, None,
+             ctypes.byref(p), None) == W.WKV_ERR_UNSUPPORTED
+    si, so = vp(P + 0x400000), vp(P + 0x400000)
+    base = [vp(P), vp(P + 0x1000), vp(P + 0x100000), vp(P + 0x200000)]
+    sf = lib.wkv_step_typed
+    assert sf(2, 2, 4, 5, *base, None, vp(P + 0x300000), si, so, None) == W.WKV_ERR_UNSUPPORTED
+    assert sf(2, 2, 4, W.WKV_DTYPE_F16, *base, None, vp(P + 0x100000 + 8), si, so,
+              None) == W.WKV_ERR_ALIAS
+
+
 def test_token_shift_rejects_invalid_arguments(lib):
     from linear_recurrent_attention_amd import wkv as W
     vp = ctypes.c_void_p
