@@ -18,6 +18,7 @@ Other workloads print their own line in the same format; they are parity
 workloads with extra measurements, not the headline:
     stream, decode, stability_fwd, stability_bwd   the other operator shapes
     gpt_gated, decode_gated   the same with the output gate sigmoid(r) fused in
+    gpt_bf16, gpt_f16         the GPT forward with 16-bit activations (state fp32)
     token_shift               the token shift at the GPT shape (3 mixes)
     copy                      a 1 GiB device copy, the bandwidth reference
 """
@@ -140,9 +141,12 @@ def cpu_baseline_gpt(torch, synth, inputs_fn, budget_s: float):
                       f"float64 O(T) {what} on {cores} threads ({elapsed:.1f} s)"}
 
 
-def bench_gpt(args, torch, wkv, synth, gated: bool = False):
+def bench_gpt(args, torch, wkv, synth, gated: bool = False, io: str = "f32"):
     """GPT-mode forward of 24 seeded layers; gated: with the time-mixing output
-    gate y = sigmoid(r) * wkv fused in (r read beside k and v)."""
+    gate y = sigmoid(r) * wkv fused in (r read beside k and v); io: element
+    format of k, v, r and y ("f32", "f16" or "bf16"; the state is float32)."""
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[io]
+    esz = 4 if io == "f32" else 2
     sh = synth.SHAPES[synth.GPT]
     B, T, C, NL = sh["B"], sh["T"], sh["C"], sh["layers"]
     dev = torch.device("cuda")
@@ -151,10 +155,12 @@ def bench_gpt(args, torch, wkv, synth, gated: bool = False):
     layers = []
     for l in range(NL):
         d = synth.make(synth.GPT, index=l, device=dev)
+        if io != "f32":
+            d["k"], d["v"] = d["k"].to(tdt), d["v"].to(tdt)
         d["y"] = torch.empty_like(d["k"])
         d["s"] = torch.empty((3, B, C), device=dev)
         if gated:
-            d["r"] = synth.receptance(synth.GPT, l, (B, T, C), device=dev)
+            d["r"] = synth.receptance(synth.GPT, l, (B, T, C), device=dev).to(tdt)
         layers.append(d)
     plan = tuple(args.plan) if args.plan else None
     chosen = plan or wkv.wkv_forward_plan_auto(B, T, C)
@@ -162,7 +168,10 @@ def bench_gpt(args, torch, wkv, synth, gated: bool = False):
         chosen = gated_auto_plan(chosen)
 
     def call(d):
-        if gated:
+        if io != "f32":
+            wkv.wkv_forward_typed(d["w"], d["u"], d["k"], d["v"], d.get("r"), y=d["y"],
+                                  state_out=d["s"], stream=stream, plan=plan)
+        elif gated:
             wkv.wkv_forward_gated(d["w"], d["u"], d["k"], d["v"], d["r"], y=d["y"],
                                   state_out=d["s"], stream=stream, plan=plan)
         else:
@@ -198,13 +207,16 @@ def bench_gpt(args, torch, wkv, synth, gated: bool = False):
     ms_launch = ms / launches
     lane_tok = B * T * C
     # k, v (and r) in, y out; w, u; state out
-    algo_bytes = (16 if gated else 12) * lane_tok + 8 * C + 12 * B * C
+    algo_bytes = (4 if gated else 3) * esz * lane_tok + 8 * C + 12 * B * C
     achieved = algo_bytes / (ms_launch * 1e-3) / 1e9
-    kname = kernel_name(chosen, wkv, gated)
-    wl = "gpt_gated" if gated else "gpt"
+    kname = kernel_name(chosen, wkv, gated, io)
+    wl = ("gpt_gated" if gated else "gpt") + ("" if io == "f32" else "_" + io)
     traffic = measured_traffic(kname, wl)
+    metric = METRIC_GATED if gated else METRIC
+    if io != "f32":
+        metric = metric.replace("fp32", f"{io} activations, fp32 state")
     out = {
-        "metric": METRIC_GATED if gated else METRIC,
+        "metric": metric,
         "value": lane_tok * launches / (ms * 1e-3),
         "unit": "tok·ch/s",
         "n_gpus": 1,
@@ -214,11 +226,11 @@ def bench_gpt(args, torch, wkv, synth, gated: bool = False):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": io,
         "data": "synthetic (seeded; k, v ~ N(0,1) with k x2, decay ~ U(-5,1), u ~ N(0,0.5)"
                 + (", r ~ N(0,2))" if gated else ")"),
-        "config": {"workload": "gpt_gated_forward" if gated else "gpt_forward", "B": B, "T": T,
-                   "C": C, "layers": NL,
+        "config": {"workload": ("gpt_gated_forward" if gated else "gpt_forward") +
+                   ("" if io == "f32" else "_" + io), "B": B, "T": T, "C": C, "layers": NL,
                    "kernel": kname, "plan": list(chosen),
                    "mean_over_layers_of_median_ms": sum(per_layer) / len(per_layer),
                    "hbm_gbs": achieved, "pct_peak_hbm": 100 * achieved / PEAK_HBM_GBS,
@@ -236,17 +248,21 @@ def bench_gpt(args, torch, wkv, synth, gated: bool = False):
     return out
 
 
-def kernel_name(plan, wkv, gated: bool = False) -> str:
+IO_NAMES = {"f32": "wkv::IoF32", "f16": "wkv::IoF16", "bf16": "wkv::IoBF16"}
+
+
+def kernel_name(plan, wkv, gated: bool = False, io: str = "f32") -> str:
     """Kernel symbol (template arguments as in the profiler's kernel names)."""
     kernel, nw, ls = plan[:3]
     cw = plan[3] if len(plan) > 3 and plan[3] else 64
     g = "true" if gated else "false"
+    t = IO_NAMES[io]
     if kernel == wkv.WKV_KERNEL_LANE:
-        return f"fwd_lane_kernel<{g}>"
+        return f"fwd_lane_kernel<{g}, {t}>"
     if kernel == wkv.WKV_KERNEL_SEGMENTED:
-        return f"fwd_seg_kernel<{nw * cw // 64}, {ls}, {cw}, {g}>"
+        return f"fwd_seg_kernel<{nw * cw // 64}, {ls}, {cw}, {g}, {t}>"
     if kernel == wkv.WKV_KERNEL_LOOKBACK:
-        return f"fwd_lookback_kernel<{cw // 64}, {nw}, {ls}, {g}>"
+        return f"fwd_lookback_kernel<{cw // 64}, {nw}, {ls}, {g}, {t}>"
     return f"kernel{kernel}<{nw}, {ls}>"
 
 
@@ -372,7 +388,7 @@ def bench_decode(args, torch, wkv, synth, gated: bool = False):
     per = ms / nsteps
     lanes = L * B * C
     algo = (40 if gated else 36) * lanes + 8 * L * C
-    kname = f"step_kernel<4, {'true' if gated else 'false'}>"
+    kname = f"step_kernel<4, {'true' if gated else 'false'}, wkv::IoF32>"
     wl = "decode_gated" if gated else "decode"
     cpu = None
     if not args.no_cpu_baseline:
@@ -590,8 +606,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt",
-                    choices=["gpt", "gpt_gated", "stream", "decode", "decode_gated",
-                             "stability_fwd", "stability_bwd", "token_shift", "copy"])
+                    choices=["gpt", "gpt_gated", "gpt_bf16", "gpt_f16", "stream", "decode",
+                             "decode_gated", "stability_fwd", "stability_bwd", "token_shift",
+                             "copy"])
     ap.add_argument("--plan", type=int, nargs="+", default=None,
                     metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
                     "(wkv_forward_ex plan)")
@@ -611,6 +628,8 @@ def main():
     wkv.load_library()
     fn = {"gpt": bench_gpt, "stream": bench_stream, "decode": bench_decode, "copy": bench_copy,
           "gpt_gated": lambda a, t, w, s: bench_gpt(a, t, w, s, True),
+          "gpt_bf16": lambda a, t, w, s: bench_gpt(a, t, w, s, False, "bf16"),
+          "gpt_f16": lambda a, t, w, s: bench_gpt(a, t, w, s, False, "f16"),
           "decode_gated": lambda a, t, w, s: bench_decode(a, t, w, s, True),
           "token_shift": bench_shift,
           "stability_fwd": lambda a, t, w, s: bench_stability(a, t, w, s, False),
