@@ -48,9 +48,11 @@ def _load():
         lib.wkvo_backward_scan.argtypes = [i64, i64, i64, D, D, D, D, D, D, D, D, D,
                                            ctypes.c_int]
         lib.wkvo_gate.argtypes = [i64, D, D, D]
+        lib.wkvo_backward_state.argtypes = [i64, i64, i64] + [D] * 13
         lib.wkvo_token_shift.argtypes = [i64, i64, i64, i64, D, D, D, D, D]
         for f in (lib.wkvo_forward_brute, lib.wkvo_forward_scan, lib.wkvo_backward_brute,
-                  lib.wkvo_backward_scan, lib.wkvo_gate, lib.wkvo_token_shift):
+                  lib.wkvo_backward_scan, lib.wkvo_gate, lib.wkvo_token_shift,
+                  lib.wkvo_backward_state):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -132,6 +134,32 @@ def backward_scan(w, u, k, v, dy, nthreads: int = 1):
     if rc:
         raise RuntimeError(f"wkvo_backward_scan failed ({rc})")
     return dk, dv, dw, du
+
+
+def backward_state(w, u, k, v, dy, state_in=None, state_out=None, d_state_out=None):
+    """O(T^2) backward with a carried state.  state_in [3][B][C] (None: empty);
+    d_state_out [3][B][C] the upstream gradient in the coordinates of state_out
+    [3][B][C] (the state the forward returned), or None.  Returns
+    (dk, dv, dw, du, d_state_in [3][B][C])."""
+    B, T, C = _shapes(k, w)
+    w, u, k, v, dy = _f64(w), _f64(u), _f64(k), _f64(v), _f64(dy)
+    si = None if state_in is None else _f64(state_in)
+    so = None if state_out is None else _f64(state_out)
+    ds = None if d_state_out is None else _f64(d_state_out)
+    for a in (si, so, ds):
+        if a is not None and a.shape != (3, B, C):
+            raise ValueError("states must be [3][B][C]")
+    if ds is not None and so is None:
+        raise ValueError("d_state_out needs state_out")
+    dk, dv = np.empty((B, T, C)), np.empty((B, T, C))
+    dw, du = np.empty(C), np.empty(C)
+    dsi = np.empty((3, B, C))
+    rc = _load().wkvo_backward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                                     _ptr(si), _ptr(so), _ptr(ds), _ptr(dk), _ptr(dv), _ptr(dw),
+                                     _ptr(du), _ptr(dsi))
+    if rc:
+        raise RuntimeError(f"wkvo_backward_state failed ({rc})")
+    return dk, dv, dw, du, dsi
 
 
 def gate(y, r):

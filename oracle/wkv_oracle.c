@@ -43,6 +43,9 @@
  *   wkvo_forward_scan      pinned (brute force, chunking identity)
  *   wkvo_backward_brute    pinned (central finite differences, invariants)
  *   wkvo_backward_scan     pinned (brute-force backward, finite differences)
+ *   wkvo_backward_state    pinned (central finite differences of a loss that
+ *                          includes the carried states, reduction to
+ *                          wkvo_backward_brute, chunking identity)
  *   wkvo_gate              pinned (library logistic function, limits, r = 0)
  *   wkvo_token_shift       pinned (hand-computed fixture, mu = 0 and mu = 1
  *                          limits, chunking identity)
@@ -486,5 +489,132 @@ int wkvo_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const double *m
                     last = x_prev ? x_prev[b * C + c] : 0.0;
                 x_prev_out[b * C + c] = last;
             }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward with a carried state ([QuickStart]: RNN mode over chunks), O(T^2) */
+/* ------------------------------------------------------------------------ */
+/*
+ * Derivatives of the closed form of [Core] extended by the state term (as in
+ * forward_brute_lane), for the loss
+ *     L = sum_t g_t y_t + gA A_T + gB B_T,
+ * where A_T, B_T are the true sums after the last token and (gA, gB) their
+ * upstream gradient.  The upstream gradient arrives in the coordinates of the
+ * state the forward handed on, (a_T, b_T, o_T): since a consumer sees only
+ * A_T = a_T e^{o_T} and B_T = b_T e^{o_T}, gA = g_aT e^{-o_T} and
+ * gB = g_bT e^{-o_T} (the o-plane of the gradient is then g_aT a_T + g_bT b_T
+ * and carries nothing more; it is not read).
+ * With E_{t,i} the weight of token i in output t (e^{k_i-(t-1-i)w}, or
+ * e^{u+k_t} for i = t), the state's weight e^{-t w} (numerator A0, denominator
+ * B0), D_t the denominator and p = E / D:
+ *   dv_i = sum_{t>=i} g_t p_{t,i}             + gA e^{k_i-(T-1-i)w}
+ *   dk_i = sum_{t>=i} g_t p_{t,i} (v_i - y_t) + e^{k_i-(T-1-i)w} (gA v_i + gB)
+ *   du   = sum_t g_t p_{t,t} (v_t - y_t)
+ *   dw   = -sum_t sum_{i<t} (t-1-i) g_t p_{t,i} (v_i - y_t)
+ *          -sum_t t g_t e^{-t w} (A0 - y_t B0) / D_t
+ *          -sum_{i<T} (T-1-i) e^{k_i-(T-1-i)w} (gA v_i + gB) - T e^{-T w} (gA A0 + gB B0)
+ *   dA0  = sum_t g_t e^{-t w} / D_t + gA e^{-T w}
+ *   dB0  = -sum_t g_t y_t e^{-t w} / D_t + gB e^{-T w}
+ * and in state coordinates (a0, b0, o0): d_a0 = dA0 e^{o0}, d_b0 = dB0 e^{o0},
+ * d_o0 = dA0 A0 + dB0 B0.  Every exponential is formed with its shift applied
+ * inside the exponent.  state_in NULL is the empty state; d_state_out NULL is
+ * no upstream gradient (state_out is then not read).  dw, du are summed over
+ * the batch.
+ */
+int wkvo_backward_state(int64_t B, int64_t T, int64_t C, const double *w, const double *u,
+                        const double *k, const double *v, const double *dy,
+                        const double *state_in, const double *state_out,
+                        const double *d_state_out, double *dk, double *dv, double *dw,
+                        double *du, double *d_state_in) {
+    if (B < 0 || T < 0 || C < 0) return 1;
+    if (d_state_out && !state_out) return 1;
+    double *x = (double *)malloc(sizeof(double) * (size_t)(T + 2));
+    for (int64_t c = 0; c < C; ++c) {
+        dw[c] = 0.0;
+        du[c] = 0.0;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c) {
+            const double *kk = k + IDX(b, 0, c), *vv = v + IDX(b, 0, c), *gg = dy + IDX(b, 0, c);
+            double *dkk = dk + IDX(b, 0, c), *dvv = dv + IDX(b, 0, c);
+            const double wc = w[c];
+            double a0 = 0.0, b0 = 0.0, o0 = -INFINITY;
+            if (state_in) {
+                a0 = state_in[SIDX(0, b, c)];
+                b0 = state_in[SIDX(1, b, c)];
+                o0 = state_in[SIDX(2, b, c)];
+            }
+            const int has_state = b0 > 0.0;
+            /* upstream gradient: gA = gaT e^{-oT}, kept as (gaT, gbT, -oT) */
+            double gaT = 0.0, gbT = 0.0, moT = 0.0;
+            if (d_state_out) {
+                gaT = d_state_out[SIDX(0, b, c)];
+                gbT = d_state_out[SIDX(1, b, c)];
+                moT = -state_out[SIDX(2, b, c)];
+            }
+            double dA0s = 0.0, dB0s = 0.0;  /* dA0, dB0 times e^{o0} */
+            for (int64_t i = 0; i < T; ++i) {
+                dkk[i * C] = 0.0;
+                dvv[i * C] = 0.0;
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                for (int64_t i = 0; i < t; ++i) x[i] = kk[i * C] - (double)(t - 1 - i) * wc;
+                x[t] = u[c] + kk[t * C];
+                double m = x[t];
+                for (int64_t i = 0; i < t; ++i) m = dmax(m, x[i]);
+                const double xs = has_state ? o0 - (double)t * wc : -INFINITY;
+                if (has_state) m = dmax(m, xs);
+                double den = 0.0, num = 0.0;
+                for (int64_t i = 0; i <= t; ++i) {
+                    const double e = exp(x[i] - m);
+                    den += e;
+                    num += e * vv[i * C];
+                }
+                if (has_state) {
+                    const double e = exp(xs - m);
+                    den += e * b0;
+                    num += e * a0;
+                }
+                const double yt = num / den, g = gg[t * C];
+                for (int64_t i = 0; i <= t; ++i) {
+                    const double p = exp(x[i] - m) / den;
+                    dvv[i * C] += g * p;
+                    dkk[i * C] += g * p * (vv[i * C] - yt);
+                    if (i == t)
+                        du[c] += g * p * (vv[i * C] - yt);
+                    else
+                        dw[c] -= (double)(t - 1 - i) * g * p * (vv[i * C] - yt);
+                }
+                if (has_state) {
+                    /* e^{-t w} e^{o0} / D_t */
+                    const double ps = exp(xs - m) / den;
+                    dA0s += g * ps;
+                    dB0s -= g * yt * ps;
+                    dw[c] -= (double)t * g * ps * (a0 - yt * b0);
+                }
+            }
+            if (d_state_out) {
+                for (int64_t i = 0; i < T; ++i) {
+                    const double e = exp(kk[i * C] - (double)(T - 1 - i) * wc + moT);
+                    const double h = gaT * vv[i * C] + gbT;
+                    dvv[i * C] += gaT * e;
+                    dkk[i * C] += e * h;
+                    dw[c] -= (double)(T - 1 - i) * e * h;
+                }
+                if (has_state) {
+                    const double e = exp(o0 - (double)T * wc + moT);  /* e^{-Tw} e^{o0} e^{-oT} */
+                    dA0s += gaT * e;
+                    dB0s += gbT * e;
+                    dw[c] -= (double)T * e * (gaT * a0 + gbT * b0);
+                }
+            }
+            if (d_state_in) {
+                d_state_in[SIDX(0, b, c)] = dA0s;
+                d_state_in[SIDX(1, b, c)] = dB0s;
+                d_state_in[SIDX(2, b, c)] = dA0s * a0 + dB0s * b0;
+            }
+        }
+    free(x);
     return 0;
 }

@@ -462,3 +462,94 @@ def test_token_shift_chunking(oracle, cuts):
     o, p2 = oracle.token_shift(mu, x[:, :0], p)       # empty call keeps the state
     assert o.shape == (3, 3, 0, 4)
     np.testing.assert_array_equal(p2, p)
+
+
+# ------------------------------------------------ backward with the state ---
+# Quick start (RNN mode carries the state between calls): training over chunks
+# needs the gradient with respect to the state a chunk starts from, and takes
+# the gradient with respect to the state it hands on.
+
+def _state_loss(oracle, w, u, k, v, dy, s_in, gA, gB):
+    """L = sum dy*y + gA*A_T + gB*B_T with A_T, B_T the true sums after the
+    last token (smooth in every input, unlike the (a, b, o) planes)."""
+    y, s = oracle.forward_brute(w, u, k, v, s_in)
+    A = s[0] * np.exp(s[2])
+    Bt = s[1] * np.exp(s[2])
+    return float((y * dy).sum() + (gA * A).sum() + (gB * Bt).sum())
+
+
+@pytest.mark.parametrize("recipe", [synth.GPT, synth.STABILITY])
+def test_backward_state_matches_finite_differences(oracle, recipe):
+    B, T, C = 2, 24, 3
+    d = synth.make(recipe, index=7, B=B, T=T, C=C, with_dy=True)
+    d = {n: t.double().numpy() for n, t in d.items()}
+    w, u, k, v, dy = d["w"], d["u"], d["k"], d["v"], d["dy"]
+    s_in = rand_state(oracle, 30, B, C)
+    _, s_out = oracle.forward_brute(w, u, k, v, s_in)
+    rng = np.random.default_rng(8)
+    g_state = rng.normal(size=(3, B, C))               # upstream (a, b, o) gradient
+    gA = g_state[0] * np.exp(-s_out[2])                # -> true-sum gradient
+    gB = g_state[1] * np.exp(-s_out[2])
+    dk, dv, dw, du, dsi = oracle.backward_state(w, u, k, v, dy, s_in, s_out, g_state)
+
+    def fd(arr, idx):
+        x0 = arr[idx]
+        h = 1e-6 * max(1.0, abs(x0))
+        arr[idx] = x0 + h
+        lp = _state_loss(oracle, w, u, k, v, dy, s_in, gA, gB)
+        arr[idx] = x0 - h
+        lm = _state_loss(oracle, w, u, k, v, dy, s_in, gA, gB)
+        arr[idx] = x0
+        return (lp - lm) / (2 * h)
+
+    def check(grad, arr, idx):
+        ref = fd(arr, idx)
+        scale = max(1e-3, np.abs(grad).max())
+        assert abs(grad[idx] - ref) <= 2e-6 * scale, (idx, grad[idx], ref)
+
+    for idx in [(b, t, c) for b in range(B) for t in (0, 1, 11, T - 2, T - 1) for c in range(C)]:
+        check(dk, k, idx)
+        check(dv, v, idx)
+    for c in range(C):
+        check(dw, w, (c,))
+        check(du, u, (c,))
+    for p in range(3):                                 # a0, b0, o0 of every lane
+        for b in range(B):
+            for c in range(C):
+                check(dsi, s_in, (p, b, c))
+
+
+def test_backward_state_reduces_to_the_stateless_backward(oracle):
+    d = rand_case(31, B=2, T=40, C=4)
+    dy = synth.make(synth.TINY, index=31, B=2, T=40, C=4, with_dy=True)["dy"].double().numpy()
+    ref = oracle.backward_brute(d["w"], d["u"], d["k"], d["v"], dy)
+    got = oracle.backward_state(d["w"], d["u"], d["k"], d["v"], dy)
+    for x, r in zip(got[:4], ref):
+        np.testing.assert_allclose(x, r, rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(got[4], 0.0)        # nothing flows into an empty state
+
+
+@pytest.mark.parametrize("cut", [1, 17, 39])
+def test_backward_state_chains_over_chunks(oracle, cut):
+    """Backward over [0, T) equals the backward of the second chunk, whose
+    state gradient is handed to the backward of the first (state coordinates
+    exactly as the forward handed them on)."""
+    B, T, C = 2, 40, 4
+    d = rand_case(32, B=B, T=T, C=C)
+    w, u, k, v = d["w"], d["u"], d["k"], d["v"]
+    dy = synth.make(synth.TINY, index=32, B=B, T=T, C=C, with_dy=True)["dy"].double().numpy()
+    s0 = rand_state(oracle, 33, B, C)
+    _, s_end = oracle.forward_brute(w, u, k, v, s0)
+    g_end = np.random.default_rng(9).normal(size=(3, B, C))
+    full = oracle.backward_state(w, u, k, v, dy, s0, s_end, g_end)
+    _, s_mid = oracle.forward_brute(w, u, k[:, :cut], v[:, :cut], s0)
+    _, s_end2 = oracle.forward_brute(w, u, k[:, cut:], v[:, cut:], s_mid)
+    second = oracle.backward_state(w, u, k[:, cut:], v[:, cut:], dy[:, cut:], s_mid, s_end2, g_end)
+    first = oracle.backward_state(w, u, k[:, :cut], v[:, :cut], dy[:, :cut], s0, s_mid, second[4])
+    np.testing.assert_allclose(np.concatenate([first[0], second[0]], axis=1), full[0],
+                               rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate([first[1], second[1]], axis=1), full[1],
+                               rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(first[2] + second[2], full[2], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(first[3] + second[3], full[3], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(first[4], full[4], rtol=1e-9, atol=1e-12)
