@@ -158,6 +158,47 @@ WKV_API wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, const float *w,
                                 float *dv, float *dw, float *du, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * wkv_backward for a chunk that starts from a carried state and hands one on:
+ * the gradients of L = sum dy * y + (the upstream loss through the state the
+ * forward returned).  This is the backward of RNN mode over chunks (skill
+ * page, "Quick start"; section "Duality"): chaining it from the last chunk to
+ * the first, each chunk's d_state_in as the previous chunk's d_state_out, gives
+ * the gradients of one call over the whole sequence.  The pages state no
+ * backward; the carried state enters every output as a token before t = 0
+ * whose weights are its sums A0 = a0 e^{o0}, B0 = b0 e^{o0}, at decay distance
+ * t, and the state handed on is A_T = e^{-T w} A0 + sum_i e^{k_i-(T-1-i)w} v_i,
+ * B_T likewise.
+ *
+ *   w, u, k, v, dy, dk, dv, dw, du, workspace: as for wkv_backward (the
+ *                 workspace size is wkv_backward_workspace_size)
+ *   state_in      [3][B][C] the state the forward started from, or NULL (empty)
+ *   state_out     [3][B][C] the state the forward returned (read only when
+ *                 d_state_out is given: the upstream gradient is in its
+ *                 coordinates)
+ *   d_state_out   [3][B][C] gradient of the upstream loss with respect to
+ *                 state_out's planes (a, b, o), or NULL for none.  A consumer
+ *                 sees only A_T and B_T, so the gradient flows through
+ *                 dL/dA_T = d_a e^{-o_T} and dL/dB_T = d_b e^{-o_T}; the o-plane
+ *                 (then d_a a_T + d_b b_T) is not read
+ *   d_state_in    [3][B][C] output: the gradient with respect to state_in's
+ *                 planes, d_a0 = dL/dA0 e^{o0}, d_b0 = dL/dB0 e^{o0},
+ *                 d_o0 = d_a0 a0 + d_b0 b0 (zero for the empty state), or NULL.
+ *                 May equal d_state_out exactly (updated in place)
+ * dw includes the state's share (d/dw of its decay e^{-t w}).  With state_in,
+ * d_state_out and d_state_in all NULL this is wkv_backward.  T == 0 passes the
+ * upstream gradient through to d_state_in.  Outputs must not overlap the
+ * inputs or each other (except d_state_in == d_state_out).  Errors as for
+ * wkv_backward; d_state_out without state_out is WKV_ERR_NULL.
+ */
+WKV_API wkv_status wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w,
+                                      const float *u, const float *k, const float *v,
+                                      const float *dy, const float *state_in,
+                                      const float *state_out, const float *d_state_out,
+                                      float *dk, float *dv, float *dw, float *du,
+                                      float *d_state_in, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 WKV_API const char *wkv_status_string(wkv_status s);
 

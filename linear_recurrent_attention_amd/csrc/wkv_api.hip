@@ -291,6 +291,48 @@ wkv_status step_impl(int64_t L, int64_t B, int64_t C, const float *w, const floa
     return from_hip(wkv::launch_step(a, stream));
 }
 
+// wkv_backward and wkv_backward_state (the former with no states).
+wkv_status backward_impl(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                         const float *k, const float *v, const float *dy, const float *s_in,
+                         const float *s_out, const float *ds_out, float *dk, float *dv,
+                         float *dw, float *du, float *ds_in, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(B, T, C);
+    const int64_t ch = bytes_of(1, 1, C);
+    const int64_t st = bytes_of(3, B, C);
+    if (seq < 0 || ch < 0 || st < 0) return WKV_ERR_OVERFLOW;
+    if (C == 0) return WKV_OK;
+    if (!dw || !du) return WKV_ERR_NULL;
+    if (seq > 0 && (!w || !u || !k || !v || !dy || !dk || !dv)) return WKV_ERR_NULL;
+    if (ds_out && !s_out && B > 0) return WKV_ERR_NULL;
+    const size_t need = wkv::backward_workspace_bytes(B, T, C);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return WKV_ERR_WORKSPACE;
+    const Range rw = rng(w, seq > 0 ? ch : 0), ru = rng(u, seq > 0 ? ch : 0);
+    const Range rk = rng(k, seq), rv = rng(v, seq), rg = rng(dy, seq);
+    const Range rsi = rng(s_in, st), rso = rng(ds_out ? s_out : nullptr, st),
+                rdso = rng(ds_out, st);
+    const Range rdk = rng(dk, seq), rdv = rng(dv, seq), rdw = rng(dw, ch), rdu = rng(du, ch);
+    const Range rdsi = rng(ds_in, st);
+    const Range rws = rng(workspace, (int64_t)need);
+    const Range outs[] = {rdk, rdv, rdw, rdu, rws, rdsi};
+    for (int i = 0; i < 6; ++i) {
+        for (Range r : {rw, ru, rk, rv, rg, rsi, rso})
+            if (overlap(outs[i], r)) return WKV_ERR_ALIAS;
+        // d_state_in may replace d_state_out exactly (read before it is written)
+        if (overlap(outs[i], rdso) && !(i == 5 && (const float *)ds_in == ds_out))
+            return WKV_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j])) return WKV_ERR_ALIAS;
+    }
+    BwdArgs a{B, T, C, w, u, k, v, dy, dk, dv, dw, du, workspace};
+    a.s_in = s_in;
+    a.s_out = s_out;
+    a.ds_out = ds_out;
+    a.ds_in = ds_in;
+    return from_hip(wkv::launch_backward(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -406,28 +448,19 @@ WKV_API wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, const float *w,
                                 const float *k, const float *v, const float *dy, float *dk,
                                 float *dv, float *dw, float *du, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-    if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
-    const int64_t seq = bytes_of(B, T, C);
-    const int64_t ch = bytes_of(1, 1, C);
-    if (seq < 0 || ch < 0) return WKV_ERR_OVERFLOW;
-    if (C == 0) return WKV_OK;
-    if (!dw || !du) return WKV_ERR_NULL;
-    if (seq > 0 && (!w || !u || !k || !v || !dy || !dk || !dv)) return WKV_ERR_NULL;
-    const size_t need = wkv::backward_workspace_bytes(B, T, C);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return WKV_ERR_WORKSPACE;
-    const Range rw = rng(w, seq > 0 ? ch : 0), ru = rng(u, seq > 0 ? ch : 0);
-    const Range rk = rng(k, seq), rv = rng(v, seq), rg = rng(dy, seq);
-    const Range rdk = rng(dk, seq), rdv = rng(dv, seq), rdw = rng(dw, ch), rdu = rng(du, ch);
-    const Range rws = rng(workspace, (int64_t)need);
-    const Range outs[] = {rdk, rdv, rdw, rdu, rws};
-    for (int i = 0; i < 5; ++i) {
-        for (Range r : {rw, ru, rk, rv, rg})
-            if (overlap(outs[i], r)) return WKV_ERR_ALIAS;
-        for (int j = i + 1; j < 5; ++j)
-            if (overlap(outs[i], outs[j])) return WKV_ERR_ALIAS;
-    }
-    const BwdArgs a{B, T, C, w, u, k, v, dy, dk, dv, dw, du, workspace};
-    return from_hip(wkv::launch_backward(a, stream));
+    return backward_impl(B, T, C, w, u, k, v, dy, nullptr, nullptr, nullptr, dk, dv, dw, du,
+                         nullptr, workspace, workspace_bytes, stream);
+}
+
+WKV_API wkv_status wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w,
+                                      const float *u, const float *k, const float *v,
+                                      const float *dy, const float *state_in,
+                                      const float *state_out, const float *d_state_out,
+                                      float *dk, float *dv, float *dw, float *du,
+                                      float *d_state_in, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    return backward_impl(B, T, C, w, u, k, v, dy, state_in, state_out, d_state_out, dk, dv, dw,
+                         du, d_state_in, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,8 +1,10 @@
 // wkv_backward.hip -- gradients dk, dv, dw, du of the GPT-mode WKV forward (gfx950).
 //
 // The pages give no backward; this differentiates the closed form (RWKV
-// architecture deep dive, youngju.dev, "WKV mechanism: core computation") with
-// the empty initial state.  With g_t = dy_t, D_t the denominator of output t,
+// architecture deep dive, youngju.dev, "WKV mechanism: core computation"),
+// starting from a carried state or the empty one (RNN mode over chunks,
+// rwkv-architecture skill page, "Quick start").  With g_t = dy_t, D_t the
+// denominator of output t,
 // lambda_t = log2 D_t, and for token i the sums over later outputs
 //   R_i  = sum_{t>i} g_t 2^{-(t-1-i)W - lambda_t}          S_i  = same with g_t y_t
 //   R'_i = sum_{t>i} (t-1-i) g_t 2^{-(t-1-i)W - lambda_t}  S'_i = same with g_t y_t
@@ -31,6 +33,19 @@
 //            emitting dk, dv and accumulating dw, du.
 // dw and du: per-thread float sums, combined across waves and then across the
 // batch in double precision in a fixed order (deterministic; no atomics).
+//
+// Carried states.  The state a chunk starts from enters every output like a
+// token before t = 0 whose weights are its true sums A0, B0 (numerator,
+// denominator) at decay distance t; so, with R_{-1}, S_{-1}, R'_{-1}, S'_{-1}
+// the sums after the reverse sweep has passed token 0,
+//   dL/dA0 = R_{-1},  dL/dB0 = -S_{-1},  dw -= A0 R'_{-1} - B0 S'_{-1},
+// returned in the state's own coordinates (a0, b0, o0): d_a0 = dL/dA0 e^{o0},
+// d_b0 = dL/dB0 e^{o0}, d_o0 = d_a0 a0 + d_b0 b0.  An upstream gradient of the
+// state handed on, (g_a, g_b) in the coordinates (a_T, b_T, o_T) of that
+// state, is an output after the last token with R_{T-1} = g_a e^{-o_T},
+// S_{T-1} = -g_b e^{-o_T}: the wave that holds token T-1 starts both its
+// segment summary and its re-sweep from it (every later segment of that tile
+// is empty, so nothing else sees a position past the end).
 #include "wkv_device.hpp"
 #include "wkv_internal.hpp"
 
@@ -108,6 +123,7 @@ struct BwdShared {
     float f[2][4][NW][64];
     float r[2][6][NW][64];
     double red[2][NW][64];
+    float seed[3][64];  // upstream state gradient: R, S and frame of R_{T-1}
 };
 
 template <int NW>
@@ -195,7 +211,9 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                                          bool active, const Chan &ch, const float *kseq,
                                          const float *vseq, const float *gseq, float *dkseq,
                                          float *dvseq, uint32_t voff, float *__restrict__ ck,
-                                         double *__restrict__ part, BwdShared<NW> &sh) {
+                                         double *__restrict__ part, const float *s_in,
+                                         const float *s_out, const float *ds_out, float *ds_in,
+                                         BwdShared<NW> &sh) {
     constexpr int TT = NW * LS;
     const int lane = threadIdx.x & 63;
     const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -205,7 +223,11 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
 
     // ---------------- phase 1: starting state of every segment ----------------
     {
+        // the carried state: every wave folds it into its segments' starting states
         Lane carry = lane_empty();
+        if (s_in && active)
+            carry = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
+                            o_in(s_in[(2 * B + bb) * C + c]));
         float Kc[LS], Vc[LS];
         load_seg<LS>(Kc, rows(kseq, (int64_t)s * LS), (int64_t)s * LS, T);
         load_seg<LS>(Vc, rows(vseq, (int64_t)s * LS), (int64_t)s * LS, T);
@@ -253,6 +275,31 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
     // ---------------- phase 2: tiles in reverse ----------------
     float dw_acc = 0.0f, du_acc = 0.0f;
     Rev carry = rev_empty();
+    // the upstream state gradient as R_{T-1}, S_{T-1} (frame -o_T), staged in
+    // LDS so that nothing stays live across the tile loop
+    if (ds_out) {
+        if (s == 0) {
+            float ga = 0.0f, gb = 0.0f, r0 = kEmpty2;
+            if (active) {
+                // (a zero gradient keeps the empty frame: zero sums in a large
+                // frame would rescale the real sums toward underflow)
+                const float o2T = o_in(s_out[(2 * B + bb) * C + c]);
+                const float a_ = ds_out[(0 * B + bb) * C + c], b_ = ds_out[(1 * B + bb) * C + c];
+                if (o2T > kEmpty2 && (a_ != 0.0f || b_ != 0.0f)) {
+                    ga = a_;
+                    gb = b_;
+                    r0 = -o2T;
+                }
+            }
+            sh.seed[0][lane] = ga;
+            sh.seed[1][lane] = -gb;
+            sh.seed[2][lane] = r0;
+        }
+        __syncthreads();
+    }
+    auto seed_of = [&]() {
+        return Rev{sh.seed[0][lane], sh.seed[1][lane], 0.0f, 0.0f, sh.seed[2][lane], 0.0f};
+    };
     float Kc[LS], Vc[LS], Gc[LS];
     {
         const int64_t t0 = (ntiles - 1) * TT + (int64_t)s * LS;
@@ -281,8 +328,11 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 if (t0 + j < T) fwd_token<SAFE>(L, Kc[j] * kLog2e, Vc[j], ch, Y[j], LAM[j], PII[j]);
             }
         }
+        // the wave holding token T-1 (last tile) starts from the upstream seed
+        const bool seeded = ds_out && tile == ntiles - 1 && t0 <= T - 1 && T - 1 < t0 + LS;
         // local backward summary of this segment
         Rev z = rev_empty();
+        if (seeded) z = seed_of();
 #pragma unroll
         for (int j = LS - 1; j >= 0; --j)
             if (t0 + j < T) rev_absorb(z, Gc[j], Y[j], LAM[j], ch.W);
@@ -301,6 +351,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         if (s + 1 < NW) suf = rev_get(sh, buf, s + 1, lane);
         const Rev agg = rev_get(sh, buf, 0, lane);
         rev_compose(suf, carry, ch.W, (float)((NW - 1 - s) * LS));
+        if (seeded) suf = seed_of();  // (later segments and the carry are empty here)
         {
             Rev nc = agg;
             rev_compose(nc, carry, ch.W, (float)TT);
@@ -325,12 +376,44 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 rev_absorb(suf, g, y, LAM[j], ch.W);
             }
         }
+        // wave 0 has swept past token 0: suf holds R_{-1}, S_{-1}, R'_{-1}, S'_{-1}.
+        // Park them, with their frame, in tile 0's checkpoint slots of segments 0
+        // and 1 (every wave read its checkpoint before the scan's barriers) and
+        // finish after the loop, where few registers are live.
+        if (tile == 0 && s == 0 && active && (s_in || ds_in)) {
+            float *q = ck + lane;
+            q[0] = suf.R;
+            q[64] = suf.S;
+            q[128] = suf.R1;
+            q[192] = suf.S1;
+            q[256] = fmaf(-suf.m, ch.W, suf.r0);
+        }
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
             Kc[j] = Kn[j];
             Vc[j] = Vn[j];
             Gc[j] = Gn[j];
         }
+    }
+
+    // the carried state as a token before t = 0: its gradient, and its share of dw
+    if (s == 0 && active && (s_in || ds_in)) {
+        const float *q = ck + lane;
+        float a0 = 0.0f, b0 = 0.0f, o20 = kEmpty2;
+        if (s_in) {
+            a0 = s_in[(0 * B + bb) * C + c];
+            b0 = s_in[(1 * B + bb) * C + c];
+            o20 = o_in(s_in[(2 * B + bb) * C + c]);
+        }
+        // 2^{frame + o0}: bounded, since e^{o0 - t w} b0 <= D_t for every output
+        const float sc = ex2(q[256] + o20);
+        const float da = q[0] * sc, db = -q[64] * sc;
+        if (ds_in) {
+            ds_in[(0 * B + bb) * C + c] = da;
+            ds_in[(1 * B + bb) * C + c] = db;
+            ds_in[(2 * B + bb) * C + c] = fmaf(da, a0, db * b0);
+        }
+        dw_acc = fmaf(-sc, fmaf(a0, q[128], -b0 * q[192]), dw_acc);
     }
 
     // dw, du of this lane: sum over the waves in a fixed order
@@ -358,7 +441,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, 
                                                           float *__restrict__ dk,
                                                           float *__restrict__ dv,
                                                           float *__restrict__ ckpt,
-                                                          double *__restrict__ part) {
+                                                          double *__restrict__ part,
+                                                          const float *s_in, const float *s_out,
+                                                          const float *ds_out, float *ds_in) {
     __shared__ BwdShared<NW> sh;
     constexpr int TT = NW * LS;
     const int64_t ngroups = (C + 63) / 64;
@@ -376,10 +461,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, 
     float *ck = ckpt + (int64_t)blockIdx.x * ntiles * NW * 4 * 64;
     if (fast)
         bwd_body<NW, LS, false>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
-                                dk + base, dv + base, voff, ck, part, sh);
+                                dk + base, dv + base, voff, ck, part, s_in, s_out, ds_out, ds_in,
+                                sh);
     else
         bwd_body<NW, LS, true>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
-                               dk + base, dv + base, voff, ck, part, sh);
+                               dk + base, dv + base, voff, ck, part, s_in, s_out, ds_out, ds_in,
+                               sh);
 }
 
 // dw[c], du[c] = sums over the batch of the per-lane parts, in order b = 0..B-1.
@@ -407,6 +494,25 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(int64_t C, float *__restr
     du[c] = 0.0f;
 }
 
+// T == 0: the state passes through unchanged, so its gradient is the upstream
+// one moved into the coordinates of state_in (e^{o0 - o_T} rescales), or zero.
+__global__ __launch_bounds__(256) void bwd_state_pass_kernel(int64_t n, const float *s_in,
+                                                             const float *s_out,
+                                                             const float *ds_out, float *ds_in) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float da = 0.0f, db = 0.0f, dov = 0.0f;
+    if (s_in && ds_out && s_in[n + i] > 0.0f) {
+        const float sc = ex2((s_in[2 * n + i] - s_out[2 * n + i]) * kLog2e);
+        da = ds_out[i] * sc;
+        db = ds_out[n + i] * sc;
+        dov = fmaf(da, s_in[i], db * s_in[n + i]);
+    }
+    ds_in[i] = da;
+    ds_in[n + i] = db;
+    ds_in[2 * n + i] = dov;
+}
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -428,6 +534,11 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t st) {
         if (C == 0) return hipSuccess;
         hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,
                            C, a.dw, a.du);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !a.ds_in || a.B == 0) return e;
+        const int64_t n = a.B * C;
+        hipLaunchKernelGGL(bwd_state_pass_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
+                           0, st, n, a.s_in, a.s_out, a.ds_out, a.ds_in);
         return hipGetLastError();
     }
     constexpr int64_t TT = kBwdNW * kBwdLS;
@@ -440,7 +551,8 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t st) {
     const int64_t grid = a.B * ngroups;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS>), dim3((unsigned)grid), dim3(kBwdNW * 64),
-                       0, st, a.B, a.T, C, a.w, a.u, a.k, a.v, a.dy, a.dk, a.dv, ck, part);
+                       0, st, a.B, a.T, C, a.w, a.u, a.k, a.v, a.dy, a.dk, a.dv, ck, part,
+                       a.s_in, a.s_out, a.ds_out, a.ds_in);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,

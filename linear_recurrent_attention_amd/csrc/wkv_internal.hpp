@@ -42,11 +42,16 @@ struct ShiftArgs {
     float *out, *x_prev_out;
 };
 
+// s_in: state before the first token (NULL: empty); s_out, ds_out: the state
+// the forward handed on and the upstream gradient in its coordinates (NULL:
+// none); ds_in: gradient with respect to s_in (NULL: not wanted).
 struct BwdArgs {
     int64_t B, T, C;
     const float *w, *u, *k, *v, *dy;
     float *dk, *dv, *dw, *du;
     void *ws;
+    const float *s_in, *s_out, *ds_out;
+    float *ds_in;
 };
 
 // forward (wkv_forward.hip)

@@ -42,7 +42,7 @@ WKV_KERNEL_LOOKBACK = 3
 EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backward",
             "wkv_status_string", "wkv_forward_ex", "wkv_forward_plan_auto",
             "wkv_forward_gated", "wkv_step_gated", "wkv_token_shift", "wkv_forward_typed",
-            "wkv_step_typed")
+            "wkv_step_typed", "wkv_backward_state")
 
 # wkv_dtype values
 WKV_DTYPE_F32 = 0
@@ -102,6 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_forward_typed.restype = ctypes.c_int
     lib.wkv_step_typed.argtypes = [i64, i64, i64, ctypes.c_int] + [vp] * 8 + [vp]
     lib.wkv_step_typed.restype = ctypes.c_int
+    lib.wkv_backward_state.argtypes = [i64, i64, i64] + [vp] * 13 + [vp, sz, vp]
+    lib.wkv_backward_state.restype = ctypes.c_int
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -314,3 +316,32 @@ def wkv_backward(w, u, k, v, dy, dk=None, dv=None, dw=None, du=None, workspace=N
                                      workspace.numel(), _stream(stream))
     _check("wkv_backward", st)
     return dk, dv, dw, du
+
+
+def wkv_backward_state(w, u, k, v, dy, state_in=None, state_out=None, d_state_out=None,
+                       dk=None, dv=None, dw=None, du=None, d_state_in=None, workspace=None,
+                       stream=None):
+    """Backward of a chunk with carried states.  ``d_state_out`` is the upstream
+    gradient in the coordinates of ``state_out`` (the state the forward
+    returned); ``d_state_in=True`` allocates the gradient of ``state_in``.
+    Returns (dk, dv, dw, du, d_state_in)."""
+    B, T, C = _bundle_shape(k, None)
+    dev = k.device
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    dw = torch.empty(C, device=dev, dtype=torch.float32) if dw is None else dw
+    du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
+    if d_state_in is True:
+        d_state_in = torch.empty((3, B, C), device=dev, dtype=torch.float32)
+    need = wkv_backward_workspace_size(B, T, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
+    st = load_library().wkv_backward_state(
+        B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy), _ptr(state_in), _ptr(state_out),
+        _ptr(d_state_out), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), _ptr(d_state_in), ws_ptr,
+        workspace.numel(), _stream(stream))
+    _check("wkv_backward_state", st)
+    return dk, dv, dw, du, d_state_in

@@ -125,6 +125,25 @@ def test_backward_workspace_and_checks(lib):
     assert lib.wkv_backward(2, 64, 32, *ins[:4], None, *outs, ws, n, None) == W.WKV_ERR_NULL
 
 
+def test_backward_state_checks(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    ins = [vp(P + i * 0x10000000) for i in range(5)]           # w u k v dy
+    si, so, dso = (vp(P + (20 + i) * 0x10000000) for i in range(3))
+    outs = [vp(P + (8 + i) * 0x10000000) for i in range(4)]    # dk dv dw du
+    dsi = vp(P + 24 * 0x10000000)
+    ws = vp(P + 16 * 0x10000000)
+    n = lib.wkv_backward_workspace_size(2, 64, 32)
+    f = lib.wkv_backward_state
+    assert f(2, 64, 32, *ins, si, None, dso, *outs, dsi, ws, n, None) == W.WKV_ERR_NULL
+    assert f(2, 64, 32, *ins, si, so, dso, *outs, si, ws, n, None) == W.WKV_ERR_ALIAS
+    assert f(2, 64, 32, *ins, si, so, dso, *outs, vp(P + 22 * 0x10000000 + 8), ws, n,
+             None) == W.WKV_ERR_ALIAS                           # partly over d_state_out
+    assert f(2, 64, 32, *ins, si, so, dso, *outs, outs[0], ws, n, None) == W.WKV_ERR_ALIAS
+    assert f(2, 64, 32, *ins, si, so, dso, *outs, dsi, ws, n - 1, None) == W.WKV_ERR_WORKSPACE
+    assert f(-1, 64, 32, *ins, si, so, dso, *outs, dsi, ws, n, None) == W.WKV_ERR_DIM
+
+
 def test_forward_ex_rejects_unknown_plans(lib):
     from linear_recurrent_attention_amd import wkv as W
     vp = ctypes.c_void_p
