@@ -17,6 +17,7 @@ stream it runs on), and the float64 CPU oracle timed on this host as a baseline.
 Other workloads print their own line in the same format; they are parity
 workloads with extra measurements, not the headline:
     stream, decode, stability_fwd, stability_bwd   the other operator shapes
+    stability_bwd_state       the backward of a chunk with carried states
     gpt_gated, decode_gated   the same with the output gate sigmoid(r) fused in
     gpt_bf16, gpt_f16         the GPT forward with 16-bit activations (state fp32)
     token_shift               the token shift at the GPT shape (3 mixes)
@@ -293,12 +294,14 @@ def bench_stream(args, torch, wkv, synth):
     st = torch.empty((3, 1, C), device=dev)
     plan = tuple(args.plan) if args.plan else None
 
+    # the 1024 calls' arguments are marshalled once (as a C caller would hold
+    # them), so the loop measures the launches, not Python's per-call checks
+    calls = [wkv.bind_forward(w, u, k[j], v[j], y[j], state_in=None if j == 0 else st,
+                              state_out=st, stream=stream, plan=plan) for j in range(NCH)]
+
     def run_all():
-        wkv.wkv_forward(w, u, k[0], v[0], y=y[0], state_in=None, state_out=st, stream=stream,
-                        plan=plan)
-        for j in range(1, NCH):
-            wkv.wkv_forward(w, u, k[j], v[j], y=y[j], state_in=st, state_out=st, stream=stream,
-                            plan=plan)
+        for c in calls:
+            c()
 
     for _ in range(args.warmup):
         run_all()
@@ -432,7 +435,10 @@ def bench_decode(args, torch, wkv, synth, gated: bool = False):
             "cpu_baseline": cpu}
 
 
-def bench_stability(args, torch, wkv, synth, backward: bool):
+def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = False):
+    """B=8 T=4096 C=2048 with wide exponents; backward: the gradients; carried:
+    the backward of a chunk that starts from a carried state and hands one on
+    (wkv_backward_state, with the state gradient in and out)."""
     sh = synth.SHAPES[synth.STABILITY]
     B, T, C = sh["B"], sh["T"], sh["C"]
     dev = torch.device("cuda")
@@ -444,13 +450,37 @@ def bench_stability(args, torch, wkv, synth, backward: bool):
         outs = [tuple(torch.empty_like(s["k"]) for _ in range(2)) for s in sets]
         dwu = torch.empty((2, C), device=dev)
 
+        if carried:
+            for i, st_ in enumerate(sets):
+                # a state from 64 earlier tokens, the state handed on, and an
+                # upstream gradient in its coordinates
+                kk, vv = synth.sequence(synth.STABILITY, 200 + i, (B, 64, C), device=dev)
+                _, st_["s_in"] = wkv.wkv_forward(st_["w"], st_["u"], kk, vv, state_out=True)
+                _, st_["s_out"] = wkv.wkv_forward(st_["w"], st_["u"], st_["k"], st_["v"],
+                                                  state_in=st_["s_in"], state_out=True)
+                st_["g"] = synth.normal((3, B, C), 1.0, synth.seed_of(synth.STABILITY, 300 + i, 0),
+                                        device=dev)
+            dsi = torch.empty((3, B, C), device=dev)
+
         def call(i):
             s = sets[i]
-            wkv.wkv_backward(s["w"], s["u"], s["k"], s["v"], s["dy"], dk=outs[i][0],
-                             dv=outs[i][1], dw=dwu[0], du=dwu[1], workspace=ws, stream=stream)
-        algo = 20 * lane_tok + 16 * C
+            if carried:
+                wkv.wkv_backward_state(s["w"], s["u"], s["k"], s["v"], s["dy"],
+                                       state_in=s["s_in"], state_out=s["s_out"],
+                                       d_state_out=s["g"], dk=outs[i][0], dv=outs[i][1],
+                                       dw=dwu[0], du=dwu[1], d_state_in=dsi, workspace=ws,
+                                       stream=stream)
+            else:
+                wkv.wkv_backward(s["w"], s["u"], s["k"], s["v"], s["dy"], dk=outs[i][0],
+                                 dv=outs[i][1], dw=dwu[0], du=dwu[1], workspace=ws,
+                                 stream=stream)
+        # k, v, dy in, dk, dv out; w, u in, dw, du out; with carried states also
+        # state_in, state_out's o-plane and the upstream gradient in, d_state_in out
+        algo = 20 * lane_tok + 16 * C + (40 * B * C if carried else 0)
         name, kname = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32", \
             "bwd_seg_kernel<16, 8>"
+        if carried:
+            name = name.replace("backward", "backward with carried states")
     else:
         ys = [torch.empty_like(s["k"]) for s in sets]
 
@@ -470,7 +500,7 @@ def bench_stability(args, torch, wkv, synth, backward: bool):
         call(i % 4)
     ms = tm.stop_ms()
     per = ms / n
-    wl = "stability_bwd" if backward else "stability_fwd"
+    wl = ("stability_bwd_state" if carried else "stability_bwd") if backward else "stability_fwd"
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -482,6 +512,21 @@ def bench_stability(args, torch, wkv, synth, backward: bool):
             st_ = sets[0]
             a = [st_[n].double().cpu().numpy() for n in ("w", "u")]
             kk, vv = (st_[n][i:i + 1].double().cpu().numpy() for n in ("k", "v"))
+            if carried:
+                # the oracle's stateful backward is the O(T^2) closed form: time one
+                # 256-token piece of the sequence, counted as such
+                cut = 256
+                sub = lambda t, lo, hi: t[i:i + 1, lo:hi].double().cpu().numpy()
+                # the carried states are the oracle's own: from tokens 256..319 of
+                # the sequence, then over the timed piece
+                _, s_in = oracle.forward_scan(a[0], a[1], sub(st_["k"], cut, cut + 64),
+                                              sub(st_["v"], cut, cut + 64))
+                kp, vp, gp = (sub(st_[n], 0, cut) for n in ("k", "v", "dy"))
+                _, s_out = oracle.forward_scan(a[0], a[1], kp, vp, s_in)
+                t0 = time.perf_counter()
+                oracle.backward_state(a[0], a[1], kp, vp, gp, s_in, s_out,
+                                      st_["g"][:, i:i + 1].double().cpu().numpy())
+                return cut * C, time.perf_counter() - t0
             t0 = time.perf_counter()
             if backward:
                 oracle.backward_scan(a[0], a[1], kk, vv, st_["dy"][i:i + 1].double().cpu().numpy(),
@@ -495,6 +540,11 @@ def bench_stability(args, torch, wkv, synth, backward: bool):
                "sample": f"{calls} of the 8 sequences (T=4096 C=2048 each), float64 O(T) "
                          f"{'reverse scan' if backward else 'recurrence'} on {cores} threads "
                          f"({secs:.1f} s)"}
+        if carried:
+            cpu["cores"] = 1
+            cpu["sample"] = (f"the first 256 tokens of {calls} of the 8 sequences (C=2048), "
+                             f"float64 O(T^2) closed-form backward with carried states on one "
+                             f"thread ({secs:.1f} s)")
     return {"metric": name, "value": lane_tok / (per * 1e-3), "unit": "tok·ch/s",
             "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": per,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -607,8 +657,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt",
                     choices=["gpt", "gpt_gated", "gpt_bf16", "gpt_f16", "stream", "decode",
-                             "decode_gated", "stability_fwd", "stability_bwd", "token_shift",
-                             "copy"])
+                             "decode_gated", "stability_fwd", "stability_bwd",
+                             "stability_bwd_state", "token_shift", "copy"])
     ap.add_argument("--plan", type=int, nargs="+", default=None,
                     metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
                     "(wkv_forward_ex plan)")
@@ -633,7 +683,9 @@ def main():
           "decode_gated": lambda a, t, w, s: bench_decode(a, t, w, s, True),
           "token_shift": bench_shift,
           "stability_fwd": lambda a, t, w, s: bench_stability(a, t, w, s, False),
-          "stability_bwd": lambda a, t, w, s: bench_stability(a, t, w, s, True)}[args.workload]
+          "stability_bwd": lambda a, t, w, s: bench_stability(a, t, w, s, True),
+          "stability_bwd_state": lambda a, t, w, s: bench_stability(a, t, w, s, True, True)
+          }[args.workload]
     torch.cuda.synchronize()
     out = fn(args, torch, wkv, synth)
     print(json.dumps(out), flush=True)

@@ -214,6 +214,28 @@ def wkv_forward_typed(w, u, k, v, r=None, y=None, state_in=None, state_out=None,
     return y, state_out
 
 
+def bind_forward(w, u, k, v, y, state_in=None, state_out=None, stream=None, plan=None):
+    """Marshal the arguments of one ``wkv_forward_ex`` call once and return a
+    callable that re-issues exactly that call (same tensors, whose contents
+    may change between calls).  For loops bound by the launch rate, such as
+    RNN mode over many short chunks, where re-checking every tensor in Python
+    on each call would cost as much as the kernel."""
+    B, T, C = _bundle_shape(k, state_in)
+    lib = load_library()
+    p = None if plan is None else (ForwardPlan(*plan) if len(plan) == 4 else ForwardPlan(*plan, 0))
+    args = (B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(state_in),
+            _ptr(state_out), None if p is None else ctypes.byref(p), _stream(stream))
+    fn = lib.wkv_forward_ex
+    keep = (w, u, k, v, y, state_in, state_out, p)  # the call's tensors stay alive with it
+
+    def call():
+        st = fn(*args)
+        if st != WKV_OK:
+            raise WkvError("wkv_forward_ex", st)
+    call.keep = keep
+    return call
+
+
 def wkv_forward_plan_auto(B: int, T: int, C: int):
     p = ForwardPlan()
     _check("wkv_forward_plan_auto", load_library().wkv_forward_plan_auto(B, T, C, ctypes.byref(p)))

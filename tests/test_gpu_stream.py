@@ -57,6 +57,34 @@ def test_small_stream_all_lanes(oracle):
     assert_state_close(f64(su), sr)
 
 
+@pytest.mark.parametrize("plan", [None, (wkv.WKV_KERNEL_SEGMENTED, 16, 16),
+                                  (wkv.WKV_KERNEL_LOOKBACK, 4, 16)])
+def test_bound_calls_replay_the_stream(oracle, plan):
+    """bind_forward: calls marshalled once and re-issued over the chunks (the
+    state updated in place, the chunk inputs rewritten between replays) match
+    the oracle over the whole sequence on every replay."""
+    C, TC, NCH = 200, 96, 6
+    dev = torch.device("cuda")
+    w, u = synth.channel_params(synth.STREAM, 1, C, device=dev)
+    k = torch.empty((NCH, 1, TC, C), device=dev)
+    v = torch.empty_like(k)
+    y = torch.empty_like(k)
+    st = torch.empty((3, 1, C), device=dev)
+    calls = [wkv.bind_forward(w, u, k[j], v[j], y[j], state_in=None if j == 0 else st,
+                              state_out=st, plan=plan) for j in range(NCH)]
+    for rep in range(2):
+        for j in range(NCH):
+            k[j], v[j] = synth.sequence(synth.STREAM, 100 * rep + j, (1, TC, C), device=dev)
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        note(f"bound stream plan={plan} replay {rep}")
+        kk, vv = (x.reshape(1, NCH * TC, C) for x in (k, v))
+        yr, sr = oracle.forward_scan(f64(w), f64(u), f64(kk), f64(vv))
+        assert_y_close(f64(y.reshape(1, NCH * TC, C)), yr)
+        assert_state_close(f64(st), sr)
+
+
 def test_stream_workload_full_size(oracle):
     sh = synth.SHAPES[synth.STREAM]
     C, TC, NCH = sh["C"], sh["T"], sh["chunks"]
