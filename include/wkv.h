@@ -24,8 +24,9 @@
  *
  * Memory and ownership
  *   - Every tensor argument is a device pointer to float32 (IEEE binary32),
- *     allocated and owned by the caller; the library never frees them and
- *     never keeps them after the call returns.
+ *     except k, v, r and y of the *_typed entry points, which may be 16-bit
+ *     (wkv_dtype).  Tensors are allocated and owned by the caller; the library
+ *     never frees them and never keeps them after the call returns.
  *   - Layouts are dense row-major with the channel index fastest:
  *       k, v, y, dy, dk, dv : [B][T][C]
  *       w, u, dw, du        : [C]             (wkv_step: w, u are [L][C])
