@@ -70,3 +70,74 @@ def test_forced_lookback_is_refused_under_capture():
         with torch.cuda.graph(g, stream=side):
             wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=y, stream=side,
                             plan=(wkv.WKV_KERNEL_LOOKBACK, 4, 16))
+
+
+def _capture(fn, side):
+    with torch.cuda.stream(side):
+        fn()                       # warm-up on the capture stream
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        fn()
+    return g
+
+
+def test_captured_time_mixing_calls_replay_exactly():
+    """Token shift, gated step, typed (bf16) forward and the backward with
+    carried states, captured together: each replay reproduces the eager bits
+    (none of these uses state shared across launches; the forward under
+    capture is the segmented kernel, bitwise reproducible)."""
+    dev = torch.device("cuda")
+    B, T, C, L = 2, 300, 128, 3
+    side = torch.cuda.Stream()
+    mu, x, xp = (t.to(dev) for t in synth.shift_inputs(synth.GPT, 90, B, T, C, 3))
+    d = synth.make(synth.STABILITY, index=91, B=B, T=T, C=C, device=dev, with_dy=True)
+    r16 = synth.receptance(synth.GPT, 91, (B, T, C), device=dev).to(torch.bfloat16)
+    k16, v16 = d["k"].to(torch.bfloat16), d["v"].to(torch.bfloat16)
+    wl = torch.stack([d["w"]] * L)
+    ul = torch.stack([d["u"]] * L)
+    ks, vs = synth.sequence(synth.DECODE, 92, (L, B, C), device=dev)
+    rs = synth.receptance(synth.DECODE, 92, (L, B, C), device=dev)
+    st0 = torch.zeros((L, 3, B, C), device=dev)
+    st0[:, 2] = -1e38
+    s_in = torch.zeros((3, B, C), device=dev)
+    s_in[1] = 1.0
+    s_in[2] = 0.5
+    s_out = torch.zeros((3, B, C), device=dev)
+    s_out[1] = 2.0
+    s_out[2] = 3.0
+    g_out = synth.normal((3, B, C), 1.0, synth.seed_of(synth.GPT, 93, 0), device=dev)
+    ws = torch.empty(wkv.wkv_backward_workspace_size(B, T, C), device=dev, dtype=torch.uint8)
+    outs = dict(sh=torch.empty((3, B, T, C), device=dev), xl=torch.empty((B, C), device=dev),
+                ys=torch.empty((L, B, C), device=dev), st=torch.empty_like(st0),
+                y16=torch.empty_like(k16), dk=torch.empty_like(d["k"]),
+                dv=torch.empty_like(d["k"]), dw=torch.empty(C, device=dev),
+                du=torch.empty(C, device=dev), dsi=torch.empty((3, B, C), device=dev))
+
+    def work(stream):
+        wkv.wkv_token_shift(mu, x, xp, out=outs["sh"], x_prev_out=outs["xl"], stream=stream)
+        wkv.wkv_step_gated(wl, ul, ks, vs, rs, st0, state_out=outs["st"], y=outs["ys"],
+                           stream=stream)
+        wkv.wkv_forward_typed(d["w"], d["u"], k16, v16, r16, y=outs["y16"], stream=stream,
+                              plan=(wkv.WKV_KERNEL_SEGMENTED, 16, 16))
+        wkv.wkv_backward_state(d["w"], d["u"], d["k"], d["v"], d["dy"], state_in=s_in,
+                               state_out=s_out, d_state_out=g_out, dk=outs["dk"], dv=outs["dv"],
+                               dw=outs["dw"], du=outs["du"], d_state_in=outs["dsi"],
+                               workspace=ws, stream=stream)
+
+    work(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in outs.items()}
+    g = _capture(lambda: work(side), side)
+    for rep in range(4):
+        for t in outs.values():
+            t.fill_(float("nan")) if t.is_floating_point() else t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        work(torch.cuda.current_stream())       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in outs.items():
+            assert torch.equal(t, ref[n]), f"replay {rep}: {n} differs from the eager result"
