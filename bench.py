@@ -100,6 +100,17 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def timed_oracle(fn, budget_s: float):
     """Calls fn(i) for i = 0, 1, ... until budget_s seconds of oracle time
     have been spent (at least one call).  fn returns (lane-tokens, seconds of
@@ -137,9 +148,18 @@ def cpu_baseline_gpt(torch, synth, inputs_fn, budget_s: float):
         done += d["k"].numel()
         layer += 1
     what = "recurrence and gate (the gate single-threaded)" if gated else "recurrence"
+    # the same on one thread, on the first layer
+    d = inputs_fn(0)
+    a = [d[n].double().cpu().numpy() for n in ("w", "u", "k", "v")]
+    t0 = time.perf_counter()
+    oracle.forward_scan(*a, nthreads=1)
+    one = d["k"].numel() / (time.perf_counter() - t0)
+    per_tok = 12.0 if not gated else 16.0   # algorithmic fp32 bytes per lane-token
     return {"value": done / elapsed, "unit": "tok·ch/s", "cores": cores, "kind": "oracle",
             "sample": f"{layer} of the 24 seeded B=8 T=1024 C=2048 layers, whole, "
-                      f"float64 O(T) {what} on {cores} threads ({elapsed:.1f} s)"}
+                      f"float64 O(T) {what} on {cores} threads ({elapsed:.1f} s)",
+            "value_1_thread": one, "effective_gbs": done / elapsed * per_tok / 1e9,
+            "cpu_model": cpu_model()}
 
 
 def bench_gpt(args, torch, wkv, synth, gated: bool = False, io: str = "f32"):
