@@ -243,3 +243,27 @@ def test_binding_fails_loudly_without_library(tmp_path):
             wkv.load_library(str(tmp_path / "libwkv.so"))
         finally:
             wkv._lib = wkv._lib_saved
+
+
+def test_auto_plan_follows_its_thresholds(lib):
+    """The automatic kernel choice is host arithmetic (with 256 CUs when no
+    device answers): lane kernel for T <= 16 or for >= 131072 lanes with
+    T <= 128; segmented for >= 262144 lanes; otherwise the look-back kernel
+    with 32-token segments when there are >= 8 blocks per CU, else 16."""
+    from linear_recurrent_attention_amd import wkv as W
+    L, S, K = W.WKV_KERNEL_LANE, W.WKV_KERNEL_SEGMENTED, W.WKV_KERNEL_LOOKBACK
+    cases = {
+        (8, 1024, 2048): (K, 4, 32, 64),      # gpt: 256 groups x 8 blocks = 2048 blocks
+        (8, 4096, 2048): (K, 4, 32, 64),
+        (1, 1024, 5120): (K, 4, 16, 64),      # stream: 80 groups x 8 blocks < 2048
+        (1, 16, 8): (L, 0, 0, 0),
+        (1, 17, 8): (K, 4, 16, 64),
+        (1024, 1, 4096): (L, 0, 0, 0),        # decode-like
+        (32, 128, 4096): (L, 0, 0, 0),        # 131072 lanes, T = 128
+        (32, 129, 4096): (K, 4, 32, 64),      # 2048 groups x 2 blocks
+        (64, 1024, 4096): (S, 16, 16, 64),    # 262144 lanes
+    }
+    for shape, want in cases.items():
+        assert W.wkv_forward_plan_auto(*shape) == want, shape
+    with pytest.raises(W.WkvError):
+        W.wkv_forward_plan_auto(-1, 4, 4)
