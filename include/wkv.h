@@ -323,6 +323,24 @@ WKV_API wkv_status wkv_step_typed(int64_t L, int64_t B, int64_t C, wkv_dtype dty
                                   const void *r, void *y, const float *state_in,
                                   float *state_out, hipStream_t stream);
 
+/*
+ * wkv_backward_state with 16-bit (or 32-bit) activation gradients: k, v, dy,
+ * dk and dv hold `dtype` elements (wkv_dtype); w, u, dw, du, the states and
+ * their gradients are float32, and all arithmetic is float32.  Inputs widen
+ * exactly; dk and dv are rounded once to `dtype` (nearest, ties to even).  The
+ * pages train the model in bfloat16 (skill page, "Workflow 3: Fine-tuning
+ * RWKV").  Arguments, semantics and errors as for wkv_backward_state, with
+ * byte sizes at the element size of dtype; an unknown dtype returns
+ * WKV_ERR_UNSUPPORTED.  The workspace size is wkv_backward_workspace_size.
+ */
+WKV_API wkv_status wkv_backward_typed(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                      const float *w, const float *u, const void *k,
+                                      const void *v, const void *dy, const float *state_in,
+                                      const float *state_out, const float *d_state_out,
+                                      void *dk, void *dv, float *dw, float *du,
+                                      float *d_state_in, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* Largest number of mixes wkv_token_shift takes in one call. */
 #define WKV_TOKEN_SHIFT_MAX_MIXES 8
 

@@ -291,14 +291,17 @@ wkv_status step_impl(int64_t L, int64_t B, int64_t C, const float *w, const floa
     return from_hip(wkv::launch_step(a, stream));
 }
 
-// wkv_backward and wkv_backward_state (the former with no states).
-wkv_status backward_impl(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
-                         const float *k, const float *v, const float *dy, const float *s_in,
-                         const float *s_out, const float *ds_out, float *dk, float *dv,
+// wkv_backward, wkv_backward_state and wkv_backward_typed (the first with no
+// states); io is the wkv_dtype of k, v, dy, dk and dv.
+wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w, const float *u,
+                         const void *k, const void *v, const void *dy, const float *s_in,
+                         const float *s_out, const float *ds_out, void *dk, void *dv,
                          float *dw, float *du, float *ds_in, void *workspace,
                          size_t workspace_bytes, hipStream_t stream) {
+    const int64_t esize = elem_bytes(io);
+    if (esize == 0) return WKV_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
-    const int64_t seq = bytes_of(B, T, C);
+    const int64_t seq = bytes_of(B, T, C, esize);
     const int64_t ch = bytes_of(1, 1, C);
     const int64_t st = bytes_of(3, B, C);
     if (seq < 0 || ch < 0 || st < 0) return WKV_ERR_OVERFLOW;
@@ -326,6 +329,7 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, const float *w, const 
             if (overlap(outs[i], outs[j])) return WKV_ERR_ALIAS;
     }
     BwdArgs a{B, T, C, w, u, k, v, dy, dk, dv, dw, du, workspace};
+    a.io = io;
     a.s_in = s_in;
     a.s_out = s_out;
     a.ds_out = ds_out;
@@ -448,8 +452,8 @@ WKV_API wkv_status wkv_backward(int64_t B, int64_t T, int64_t C, const float *w,
                                 const float *k, const float *v, const float *dy, float *dk,
                                 float *dv, float *dw, float *du, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-    return backward_impl(B, T, C, w, u, k, v, dy, nullptr, nullptr, nullptr, dk, dv, dw, du,
-                         nullptr, workspace, workspace_bytes, stream);
+    return backward_impl(B, T, C, WKV_DTYPE_F32, w, u, k, v, dy, nullptr, nullptr, nullptr, dk,
+                         dv, dw, du, nullptr, workspace, workspace_bytes, stream);
 }
 
 WKV_API wkv_status wkv_backward_state(int64_t B, int64_t T, int64_t C, const float *w,
@@ -459,8 +463,20 @@ WKV_API wkv_status wkv_backward_state(int64_t B, int64_t T, int64_t C, const flo
                                       float *dk, float *dv, float *dw, float *du,
                                       float *d_state_in, void *workspace,
                                       size_t workspace_bytes, hipStream_t stream) {
-    return backward_impl(B, T, C, w, u, k, v, dy, state_in, state_out, d_state_out, dk, dv, dw,
-                         du, d_state_in, workspace, workspace_bytes, stream);
+    return backward_impl(B, T, C, WKV_DTYPE_F32, w, u, k, v, dy, state_in, state_out,
+                         d_state_out, dk, dv, dw, du, d_state_in, workspace, workspace_bytes,
+                         stream);
+}
+
+WKV_API wkv_status wkv_backward_typed(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                      const float *w, const float *u, const void *k,
+                                      const void *v, const void *dy, const float *state_in,
+                                      const float *state_out, const float *d_state_out,
+                                      void *dk, void *dv, float *dw, float *du,
+                                      float *d_state_in, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    return backward_impl(B, T, C, (int)dtype, w, u, k, v, dy, state_in, state_out, d_state_out,
+                         dk, dv, dw, du, d_state_in, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -158,8 +158,8 @@ __device__ __forceinline__ Rev rev_get(const BwdShared<NW> &sh, int buf, int s, 
 
 // LS rows t0.. of one tensor through a wave-uniform descriptor (rows past the
 // end of the sequence are not read and hold 0).
-template <int LS>
-__device__ __forceinline__ void load_seg(float (&X)[LS], const TileRows &r, int64_t t0, int64_t T) {
+template <int LS, class TR>
+__device__ __forceinline__ void load_seg(float (&X)[LS], const TR &r, int64_t t0, int64_t T) {
     if (t0 + LS <= T) {
 #pragma unroll
         for (int j = 0; j < LS; ++j) X[j] = r.ld(j);
@@ -206,19 +206,25 @@ __device__ __forceinline__ void fwd_token(Lane &L, float K, float v, const Chan 
     L.n = pos ? 0.0f : n1;
 }
 
-template <int NW, int LS, bool SAFE>
+// IO: element format of k, v, dy, dk and dv (the states, w, u, dw, du and all
+// arithmetic are float32).
+template <int NW, int LS, bool SAFE, class IO>
 __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_t bb, int64_t c,
-                                         bool active, const Chan &ch, const float *kseq,
-                                         const float *vseq, const float *gseq, float *dkseq,
-                                         float *dvseq, uint32_t voff, float *__restrict__ ck,
+                                         bool active, const Chan &ch,
+                                         const typename IO::T *kseq, const typename IO::T *vseq,
+                                         const typename IO::T *gseq, typename IO::T *dkseq,
+                                         typename IO::T *dvseq, uint32_t voff,
+                                         float *__restrict__ ck,
                                          double *__restrict__ part, const float *s_in,
                                          const float *s_out, const float *ds_out, float *ds_in,
                                          BwdShared<NW> &sh) {
     constexpr int TT = NW * LS;
     const int lane = threadIdx.x & 63;
     const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t rowb = (uint32_t)(C * 4);
-    auto rows = [&](const float *seq, int64_t t0) { return TileRows(seq + t0 * C, voff, rowb); };
+    const uint32_t rowb = (uint32_t)(C * IO::kBytes);
+    auto rows = [&](const typename IO::T *seq, int64_t t0) {
+        return TileRowsT<IO>(seq + t0 * C, voff, rowb);
+    };
     const int64_t ntiles = (T + TT - 1) / TT;
 
     // ---------------- phase 1: starting state of every segment ----------------
@@ -358,7 +364,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             carry = nc;
         }
         // re-sweep backward from the suffix state, emitting gradients
-        const TileRows dkr = rows(dkseq, t0), dvr = rows(dvseq, t0);
+        const TileRowsT<IO> dkr = rows(dkseq, t0), dvr = rows(dvseq, t0);
 #pragma unroll
         for (int j = LS - 1; j >= 0; --j) {
             if (t0 + j < T) {
@@ -431,15 +437,15 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
     }
 }
 
-template <int NW, int LS>
+template <int NW, int LS, class IO>
 __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, int64_t C,
                                                           const float *__restrict__ w,
                                                           const float *__restrict__ u,
-                                                          const float *__restrict__ k,
-                                                          const float *__restrict__ v,
-                                                          const float *__restrict__ dy,
-                                                          float *__restrict__ dk,
-                                                          float *__restrict__ dv,
+                                                          const typename IO::T *__restrict__ k,
+                                                          const typename IO::T *__restrict__ v,
+                                                          const typename IO::T *__restrict__ dy,
+                                                          typename IO::T *__restrict__ dk,
+                                                          typename IO::T *__restrict__ dv,
                                                           float *__restrict__ ckpt,
                                                           double *__restrict__ part,
                                                           const float *s_in, const float *s_out,
@@ -457,16 +463,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, 
     // wave-uniform base of this (sequence, channel group); inactive lanes read
     // the group's first channel and never store
     const int64_t base = bb * T * C + g * 64;
-    const uint32_t voff = active ? (uint32_t)(threadIdx.x & 63) * 4u : 0u;
+    const uint32_t voff = active ? (uint32_t)((threadIdx.x & 63) * IO::kBytes) : 0u;
     float *ck = ckpt + (int64_t)blockIdx.x * ntiles * NW * 4 * 64;
     if (fast)
-        bwd_body<NW, LS, false>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
-                                dk + base, dv + base, voff, ck, part, s_in, s_out, ds_out, ds_in,
-                                sh);
+        bwd_body<NW, LS, false, IO>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
+                                    dk + base, dv + base, voff, ck, part, s_in, s_out, ds_out,
+                                    ds_in, sh);
     else
-        bwd_body<NW, LS, true>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
-                               dk + base, dv + base, voff, ck, part, s_in, s_out, ds_out, ds_in,
-                               sh);
+        bwd_body<NW, LS, true, IO>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
+                                   dk + base, dv + base, voff, ck, part, s_in, s_out, ds_out,
+                                   ds_in, sh);
 }
 
 // dw[c], du[c] = sums over the batch of the per-lane parts, in order b = 0..B-1.
@@ -516,6 +522,15 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(int64_t n, const fl
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+template <class IO>
+void launch_bwd_seg(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
+    using T = typename IO::T;
+    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS, IO>), dim3((unsigned)grid),
+                       dim3(kBwdNW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, (const T *)a.k,
+                       (const T *)a.v, (const T *)a.dy, (T *)a.dk, (T *)a.dv, ck, part, a.s_in,
+                       a.s_out, a.ds_out, a.ds_in);
+}
+
 }  // namespace
 
 size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C) {
@@ -550,9 +565,12 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t st) {
                                        sizeof(float)));
     const int64_t grid = a.B * ngroups;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS>), dim3((unsigned)grid), dim3(kBwdNW * 64),
-                       0, st, a.B, a.T, C, a.w, a.u, a.k, a.v, a.dy, a.dk, a.dv, ck, part,
-                       a.s_in, a.s_out, a.ds_out, a.ds_in);
+    switch (a.io) {
+        case kIoF32: launch_bwd_seg<IoF32>(a, grid, ck, part, st); break;
+        case kIoF16: launch_bwd_seg<IoF16>(a, grid, ck, part, st); break;
+        case kIoBF16: launch_bwd_seg<IoBF16>(a, grid, ck, part, st); break;
+        default: return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, st,

@@ -250,8 +250,8 @@ struct IoF16 {
     }
 };
 
-// bfloat16 is the upper half of a float32: widening is a shift; narrowing
-// rounds the dropped half to nearest, ties to even, and keeps NaN a NaN.
+// bfloat16 is the upper half of a float32: widening is a shift; narrowing is
+// gfx950's v_cvt_pk_bf16_f32 (round to nearest even, NaN stays NaN).
 struct IoBF16 {
     using T = unsigned short;
     static constexpr int kBytes = 2;
@@ -259,9 +259,7 @@ struct IoBF16 {
         return __builtin_bit_cast(float, (uint32_t)x << 16);
     }
     __device__ __forceinline__ static T from_f(float x) {
-        const uint32_t u = __builtin_bit_cast(uint32_t, x);
-        if ((u & 0x7fffffffu) > 0x7f800000u) return (T)((u >> 16) | 0x40u);
-        return (T)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+        return __builtin_bit_cast(unsigned short, (__bf16)x);
     }
     __device__ __forceinline__ static float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                uint32_t soff) {

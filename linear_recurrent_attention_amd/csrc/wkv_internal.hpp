@@ -45,13 +45,17 @@ struct ShiftArgs {
 // s_in: state before the first token (NULL: empty); s_out, ds_out: the state
 // the forward handed on and the upstream gradient in its coordinates (NULL:
 // none); ds_in: gradient with respect to s_in (NULL: not wanted).
+// k, v, dy, dk, dv hold elements of format `io`.
 struct BwdArgs {
     int64_t B, T, C;
-    const float *w, *u, *k, *v, *dy;
-    float *dk, *dv, *dw, *du;
+    const float *w, *u;
+    const void *k, *v, *dy;
+    void *dk, *dv;
+    float *dw, *du;
     void *ws;
     const float *s_in, *s_out, *ds_out;
     float *ds_in;
+    int io;
 };
 
 // forward (wkv_forward.hip)

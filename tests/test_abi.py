@@ -144,6 +144,25 @@ def test_backward_state_checks(lib):
     assert f(-1, 64, 32, *ins, si, so, dso, *outs, dsi, ws, n, None) == W.WKV_ERR_DIM
 
 
+def test_backward_typed_checks(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    ins = [vp(P + i * 0x10000000) for i in range(5)]           # w u k v dy
+    outs = [vp(P + (8 + i) * 0x10000000) for i in range(4)]    # dk dv dw du
+    ws = vp(P + 16 * 0x10000000)
+    n = lib.wkv_backward_workspace_size(2, 64, 32)
+    f = lib.wkv_backward_typed
+    assert f(2, 64, 32, 9, *ins, None, None, None, *outs, None, ws, n, None) == \
+        W.WKV_ERR_UNSUPPORTED
+    # 2 x 64 x 32 bf16 elements are 8 KiB: dk 6 KiB into k overlaps it
+    bad = list(outs)
+    bad[0] = vp(P + 2 * 0x10000000 + 6144)
+    assert f(2, 64, 32, W.WKV_DTYPE_BF16, *ins, None, None, None, *bad, None, ws, n,
+             None) == W.WKV_ERR_ALIAS
+    assert f(2, 64, 32, W.WKV_DTYPE_F16, *ins[:4], None, None, None, None, *outs, None, ws, n,
+             None) == W.WKV_ERR_NULL
+
+
 def test_forward_ex_rejects_unknown_plans(lib):
     from linear_recurrent_attention_amd import wkv as W
     vp = ctypes.c_void_p

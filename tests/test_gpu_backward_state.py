@@ -189,3 +189,52 @@ def test_stability_workload_full_size_sampled(oracle):
     assert_grad_close(f64(got[3])[cs], ref[3], "du", fs)
     for pl in range(3):
         assert_grad_close(f64(got[4])[pl][:, cs], ref[4][pl], f"d_state_in[{pl}]", fs)
+
+
+
+# ---------------------------------------------------- 16-bit activations ---
+# k, v, dy in fp16 / bf16 (widened exactly), dk and dv rounded once to the
+# format: their bound gains the relative half-unit h of the format's last
+# place (2^-11 fp16, 2^-8 bf16); dw, du and the state gradient are float32.
+
+HALF_ULP = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 5), (2, 300, 100), (1, 513, 130), (2, 129, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("states", [False, True])
+def test_typed_backward_matches_oracle(oracle, dt, shape, states):
+    from parity import G_FLOOR, G_RTOL
+    B, T, C = shape
+    d = synth.make(synth.STABILITY, index=80, B=B, T=T, C=C, with_dy=True)
+    d = {n: (t.to(dt) if n in ("k", "v", "dy") else t) for n, t in d.items()}
+    a = {n: f64(d[n]) for n in ("w", "u", "k", "v", "dy")}
+    s_in = s_out = g_out = None
+    if states:
+        p = synth.make(synth.TINY, index=81, B=B, T=11, C=C)
+        s_in = oracle_state(oracle, a["w"], a["u"], f64(p["k"]), f64(p["v"]))
+        s_out = oracle_state(oracle, a["w"], a["u"], a["k"], a["v"], s_in)
+        g_out = upstream(B, C, 5)
+    dev = torch.device("cuda")
+    t = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+    note(f"typed bwd {dt} B={B} T={T} C={C} states={states}")
+    got = wkv.wkv_backward_typed(*(d[n].to(dev) for n in ("w", "u", "k", "v", "dy")),
+                                 state_in=t(s_in), state_out=t(s_out), d_state_out=t(g_out),
+                                 d_state_in=True)
+    torch.cuda.synchronize()
+    assert got[0].dtype == dt and got[1].dtype == dt
+    ref = oracle.backward_state(a["w"], a["u"], a["k"], a["v"], a["dy"], s_in, s_out, g_out)
+    f = roundoff_floor(a["dy"], a["v"])
+    fs = roundoff_floor(a["dy"], a["v"], summed=True)
+    for name, x, r in (("dk", got[0], ref[0]), ("dv", got[1], ref[1])):
+        x = f64(x)
+        assert np.all(np.isfinite(x)), name
+        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+        bound = (G_RTOL + HALF_ULP[dt]) * np.abs(r) + G_FLOOR * rms + f + 1e-300
+        e = float(np.max(np.abs(x - r) / bound)) if r.size else 0.0
+        assert e <= 1.0, f"{name}: {e:.3g}x the tolerance"
+    assert_grad_close(f64(got[2]), ref[2], "dw", fs)
+    assert_grad_close(f64(got[3]), ref[3], "du", fs)
+    for pl in range(3):
+        assert_grad_close(f64(got[4])[pl], ref[4][pl], f"d_state_in[{pl}]", fs)
