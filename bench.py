@@ -18,6 +18,7 @@ Other workloads print their own line in the same format; they are parity
 workloads with extra measurements, not the headline:
     stream, decode, stability_fwd, stability_bwd   the other operator shapes
     stability_bwd_state       the backward of a chunk with carried states
+    stability_bwd_bf16        the backward with bf16 activations and gradients
     gpt_gated, decode_gated   the same with the output gate sigmoid(r) fused in
     gpt_bf16, gpt_f16         the GPT forward with 16-bit activations (state fp32)
     token_shift               the token shift at the GPT shape (3 mixes)
@@ -455,7 +456,8 @@ def bench_decode(args, torch, wkv, synth, gated: bool = False):
             "cpu_baseline": cpu}
 
 
-def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = False):
+def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = False,
+                    io: str = "f32"):
     """B=8 T=4096 C=2048 with wide exponents; backward: the gradients; carried:
     the backward of a chunk that starts from a carried state and hands one on
     (wkv_backward_state, with the state gradient in and out)."""
@@ -464,6 +466,11 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
     dev = torch.device("cuda")
     stream = torch.cuda.current_stream()
     sets = [synth.make(synth.STABILITY, index=i, device=dev, with_dy=backward) for i in range(4)]
+    if io != "f32":   # backward with 16-bit k, v, dy, dk, dv (state and dw, du float32)
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[io]
+        for st_ in sets:
+            for n in ("k", "v", "dy"):
+                st_[n] = st_[n].to(tdt)
     lane_tok = B * T * C
     if backward:
         ws = torch.empty(wkv.wkv_backward_workspace_size(B, T, C), device=dev, dtype=torch.uint8)
@@ -484,7 +491,11 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
 
         def call(i):
             s = sets[i]
-            if carried:
+            if io != "f32":
+                wkv.wkv_backward_typed(s["w"], s["u"], s["k"], s["v"], s["dy"], dk=outs[i][0],
+                                       dv=outs[i][1], dw=dwu[0], du=dwu[1], workspace=ws,
+                                       stream=stream)
+            elif carried:
                 wkv.wkv_backward_state(s["w"], s["u"], s["k"], s["v"], s["dy"],
                                        state_in=s["s_in"], state_out=s["s_out"],
                                        d_state_out=s["g"], dk=outs[i][0], dv=outs[i][1],
@@ -496,9 +507,12 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
                                  stream=stream)
         # k, v, dy in, dk, dv out; w, u in, dw, du out; with carried states also
         # state_in, state_out's o-plane and the upstream gradient in, d_state_in out
-        algo = 20 * lane_tok + 16 * C + (40 * B * C if carried else 0)
-        name, kname = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32", \
-            "bwd_seg_kernel<16, 8>"
+        esz = 4 if io == "f32" else 2
+        algo = 5 * esz * lane_tok + 16 * C + (40 * B * C if carried else 0)
+        name = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32"
+        kname = f"bwd_seg_kernel<16, 8, {IO_NAMES[io]}>"
+        if io != "f32":
+            name = name.replace("fp32", f"{io} activations, fp32 state")
         if carried:
             name = name.replace("backward", "backward with carried states")
     else:
@@ -521,6 +535,8 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
     ms = tm.stop_ms()
     per = ms / n
     wl = ("stability_bwd_state" if carried else "stability_bwd") if backward else "stability_fwd"
+    if io != "f32":
+        wl += "_" + io
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -567,7 +583,7 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
                              f"thread ({secs:.1f} s)")
     return {"metric": name, "value": lane_tok / (per * 1e-3), "unit": "tok·ch/s",
             "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": per,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": io,
             "data": "synthetic", "config": {"workload": wl, "B": B, "T": T, "C": C,
                                             "kernel": kname},
             "roofline": {"bound": "hbm", "achieved": algo / (per * 1e-3) / 1e9,
@@ -678,7 +694,8 @@ def main():
     ap.add_argument("--workload", default="gpt",
                     choices=["gpt", "gpt_gated", "gpt_bf16", "gpt_f16", "stream", "decode",
                              "decode_gated", "stability_fwd", "stability_bwd",
-                             "stability_bwd_state", "token_shift", "copy"])
+                             "stability_bwd_state", "stability_bwd_bf16", "token_shift",
+                             "copy"])
     ap.add_argument("--plan", type=int, nargs="+", default=None,
                     metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
                     "(wkv_forward_ex plan)")
@@ -704,7 +721,9 @@ def main():
           "token_shift": bench_shift,
           "stability_fwd": lambda a, t, w, s: bench_stability(a, t, w, s, False),
           "stability_bwd": lambda a, t, w, s: bench_stability(a, t, w, s, True),
-          "stability_bwd_state": lambda a, t, w, s: bench_stability(a, t, w, s, True, True)
+          "stability_bwd_state": lambda a, t, w, s: bench_stability(a, t, w, s, True, True),
+          "stability_bwd_bf16": lambda a, t, w, s: bench_stability(a, t, w, s, True, False,
+                                                                   "bf16"),
           }[args.workload]
     torch.cuda.synchronize()
     out = fn(args, torch, wkv, synth)
