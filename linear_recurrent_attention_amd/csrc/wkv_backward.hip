@@ -207,8 +207,9 @@ __device__ __forceinline__ void fwd_token(Lane &L, float K, float v, const Chan 
 }
 
 // IO: element format of k, v, dy, dk and dv (the states, w, u, dw, du and all
-// arithmetic are float32).
-template <int NW, int LS, bool SAFE, class IO>
+// arithmetic are float32).  FULL: T is a whole number of tiles, so no token
+// needs a bounds test.
+template <int NW, int LS, bool SAFE, bool FULL, class IO>
 __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_t bb, int64_t c,
                                          bool active, const Chan &ch,
                                          const typename IO::T *kseq, const typename IO::T *vseq,
@@ -247,7 +248,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             Lane S = lane_empty();
 #pragma unroll
             for (int j = 0; j < LS; ++j)
-                if (t0 + j < T) absorb(S, Kc[j] * kLog2e, Vc[j], ch);
+                if (FULL || t0 + j < T) absorb(S, Kc[j] * kLog2e, Vc[j], ch);
             int buf = 0;
 #pragma unroll
             for (int d = 1; d < NW; d <<= 1) {
@@ -331,7 +332,8 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 Y[j] = 0.0f;
                 LAM[j] = 0.0f;
                 PII[j] = 0.0f;
-                if (t0 + j < T) fwd_token<SAFE>(L, Kc[j] * kLog2e, Vc[j], ch, Y[j], LAM[j], PII[j]);
+                if (FULL || t0 + j < T)
+                    fwd_token<SAFE>(L, Kc[j] * kLog2e, Vc[j], ch, Y[j], LAM[j], PII[j]);
             }
         }
         // the wave holding token T-1 (last tile) starts from the upstream seed
@@ -341,7 +343,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         if (seeded) z = seed_of();
 #pragma unroll
         for (int j = LS - 1; j >= 0; --j)
-            if (t0 + j < T) rev_absorb(z, Gc[j], Y[j], LAM[j], ch.W);
+            if (FULL || t0 + j < T) rev_absorb(z, Gc[j], Y[j], LAM[j], ch.W);
         // inclusive scan from the last segment backward (Hillis-Steele)
         int buf = 0;
 #pragma unroll
@@ -367,7 +369,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         const TileRowsT<IO> dkr = rows(dkseq, t0), dvr = rows(dvseq, t0);
 #pragma unroll
         for (int j = LS - 1; j >= 0; --j) {
-            if (t0 + j < T) {
+            if (FULL || t0 + j < T) {
                 const float K = Kc[j] * kLog2e;
                 const float v = Vc[j], g = Gc[j], y = Y[j];
                 const float ek = ex2(fmaf(-suf.m, ch.W, K + suf.r0));
@@ -437,7 +439,8 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
     }
 }
 
-template <int NW, int LS, class IO>
+// FULL: T is a whole number of tiles (chosen on the host).
+template <int NW, int LS, bool FULL, class IO>
 __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, int64_t C,
                                                           const float *__restrict__ w,
                                                           const float *__restrict__ u,
@@ -466,13 +469,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, 
     const uint32_t voff = active ? (uint32_t)((threadIdx.x & 63) * IO::kBytes) : 0u;
     float *ck = ckpt + (int64_t)blockIdx.x * ntiles * NW * 4 * 64;
     if (fast)
-        bwd_body<NW, LS, false, IO>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
-                                    dk + base, dv + base, voff, ck, part, s_in, s_out, ds_out,
-                                    ds_in, sh);
+        bwd_body<NW, LS, false, FULL, IO>(B, T, C, bb, c, active, ch, k + base, v + base,
+                                          dy + base, dk + base, dv + base, voff, ck, part, s_in,
+                                          s_out, ds_out, ds_in, sh);
     else
-        bwd_body<NW, LS, true, IO>(B, T, C, bb, c, active, ch, k + base, v + base, dy + base,
-                                   dk + base, dv + base, voff, ck, part, s_in, s_out, ds_out,
-                                   ds_in, sh);
+        bwd_body<NW, LS, true, FULL, IO>(B, T, C, bb, c, active, ch, k + base, v + base,
+                                         dy + base, dk + base, dv + base, voff, ck, part, s_in,
+                                         s_out, ds_out, ds_in, sh);
 }
 
 // dw[c], du[c] = sums over the batch of the per-lane parts, in order b = 0..B-1.
@@ -522,13 +525,21 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(int64_t n, const fl
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-template <class IO>
-void launch_bwd_seg(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
+template <bool FULL, class IO>
+void launch_bwd_seg_k(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
     using T = typename IO::T;
-    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS, IO>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS, FULL, IO>), dim3((unsigned)grid),
                        dim3(kBwdNW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, (const T *)a.k,
                        (const T *)a.v, (const T *)a.dy, (T *)a.dk, (T *)a.dv, ck, part, a.s_in,
                        a.s_out, a.ds_out, a.ds_in);
+}
+
+template <class IO>
+void launch_bwd_seg(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
+    if (a.T % (kBwdNW * kBwdLS) == 0)
+        launch_bwd_seg_k<true, IO>(a, grid, ck, part, st);
+    else
+        launch_bwd_seg_k<false, IO>(a, grid, ck, part, st);
 }
 
 }  // namespace
