@@ -510,7 +510,8 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
         esz = 4 if io == "f32" else 2
         algo = 5 * esz * lane_tok + 16 * C + (40 * B * C if carried else 0)
         name = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32"
-        kname = f"bwd_seg_kernel<16, 8, {IO_NAMES[io]}>"
+        # (the whole-tile variant when T is a multiple of its 128-token tile)
+        kname = f"bwd_seg_kernel<16, 8, {'true' if T % 128 == 0 else 'false'}, {IO_NAMES[io]}>"
         if io != "f32":
             name = name.replace("fp32", f"{io} activations, fp32 state")
         if carried:
