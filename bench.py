@@ -19,6 +19,8 @@ workloads with extra measurements, not the headline:
     stream, decode, stability_fwd, stability_bwd   the other operator shapes
     stability_bwd_state       the backward of a chunk with carried states
     stability_bwd_bf16        the backward with bf16 activations and gradients
+    stability_fwd_ckpt        the forward that also writes 128-token checkpoints
+    stability_bwd_ckpt[_bf16] the backward that starts from those checkpoints
     gpt_gated, decode_gated   the same with the output gate sigmoid(r) fused in
     gpt_bf16, gpt_f16         the GPT forward with 16-bit activations (state fp32)
     token_shift               the token shift at the GPT shape (3 mixes)
@@ -457,10 +459,13 @@ def bench_decode(args, torch, wkv, synth, gated: bool = False):
 
 
 def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = False,
-                    io: str = "f32"):
+                    io: str = "f32", ckpt: bool = False):
     """B=8 T=4096 C=2048 with wide exponents; backward: the gradients; carried:
     the backward of a chunk that starts from a carried state and hands one on
-    (wkv_backward_state, with the state gradient in and out)."""
+    (wkv_backward_state, with the state gradient in and out); ckpt: the forward
+    that also writes its 128-token checkpoints, or the backward that starts
+    from them (wkv_forward_checkpointed / wkv_backward_checkpointed; the
+    checkpoints are written by the forward before the timed region)."""
     sh = synth.SHAPES[synth.STABILITY]
     B, T, C = sh["B"], sh["T"], sh["C"]
     dev = torch.device("cuda")
@@ -472,6 +477,10 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
             for n in ("k", "v", "dy"):
                 st_[n] = st_[n].to(tdt)
     lane_tok = B * T * C
+    nck = wkv.checkpoint_count(T)
+    if ckpt:
+        for st_ in sets:
+            _, _, st_["ck"] = wkv.wkv_forward_checkpointed(st_["w"], st_["u"], st_["k"], st_["v"])
     if backward:
         ws = torch.empty(wkv.wkv_backward_workspace_size(B, T, C), device=dev, dtype=torch.uint8)
         outs = [tuple(torch.empty_like(s["k"]) for _ in range(2)) for s in sets]
@@ -491,7 +500,11 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
 
         def call(i):
             s = sets[i]
-            if io != "f32":
+            if ckpt:
+                wkv.wkv_backward_checkpointed(s["w"], s["u"], s["k"], s["v"], s["dy"], s["ck"],
+                                              dk=outs[i][0], dv=outs[i][1], dw=dwu[0],
+                                              du=dwu[1], workspace=ws, stream=stream)
+            elif io != "f32":
                 wkv.wkv_backward_typed(s["w"], s["u"], s["k"], s["v"], s["dy"], dk=outs[i][0],
                                        dv=outs[i][1], dw=dwu[0], du=dwu[1], workspace=ws,
                                        stream=stream)
@@ -508,22 +521,33 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
         # k, v, dy in, dk, dv out; w, u in, dw, du out; with carried states also
         # state_in, state_out's o-plane and the upstream gradient in, d_state_in out
         esz = 4 if io == "f32" else 2
-        algo = 5 * esz * lane_tok + 16 * C + (40 * B * C if carried else 0)
+        # (and the checkpoints in: 12 bytes per lane each)
+        algo = (5 * esz * lane_tok + 16 * C + (40 * B * C if carried else 0) +
+                (12 * B * C * nck if ckpt else 0))
         name = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32"
         # (the whole-tile variant when T is a multiple of its 128-token tile)
-        kname = f"bwd_seg_kernel<16, 8, {'true' if T % 128 == 0 else 'false'}, {IO_NAMES[io]}>"
+        kname = (f"bwd_seg_kernel<16, 8, {'true' if T % 128 == 0 else 'false'}, "
+                 f"{'true' if ckpt else 'false'}, {IO_NAMES[io]}>")
         if io != "f32":
             name = name.replace("fp32", f"{io} activations, fp32 state")
         if carried:
             name = name.replace("backward", "backward with carried states")
+        if ckpt:
+            name = name.replace("backward", "backward from the forward's checkpoints")
     else:
         ys = [torch.empty_like(s["k"]) for s in sets]
 
         def call(i):
             s = sets[i]
-            wkv.wkv_forward(s["w"], s["u"], s["k"], s["v"], y=ys[i], stream=stream)
-        algo = 12 * lane_tok + 8 * C
+            if ckpt:
+                wkv.wkv_forward_checkpointed(s["w"], s["u"], s["k"], s["v"], y=ys[i],
+                                             checkpoints=s["ck"], stream=stream)
+            else:
+                wkv.wkv_forward(s["w"], s["u"], s["k"], s["v"], y=ys[i], stream=stream)
+        algo = 12 * lane_tok + 8 * C + (12 * B * C * nck if ckpt else 0)
         name = "WKV fwd tokens·channels/sec, B=8 T=4096 C=2048 fp32 (wide exponents)"
+        if ckpt:
+            name = name.replace("fwd", "fwd with 128-token checkpoints")
         kname = kernel_name(wkv.wkv_forward_plan_auto(B, T, C), wkv)
     for i in range(args.warmup):
         call(i % 4)
@@ -536,6 +560,8 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
     ms = tm.stop_ms()
     per = ms / n
     wl = ("stability_bwd_state" if carried else "stability_bwd") if backward else "stability_fwd"
+    if ckpt:
+        wl += "_ckpt"
     if io != "f32":
         wl += "_" + io
     cpu = None
@@ -695,7 +721,8 @@ def main():
     ap.add_argument("--workload", default="gpt",
                     choices=["gpt", "gpt_gated", "gpt_bf16", "gpt_f16", "stream", "decode",
                              "decode_gated", "stability_fwd", "stability_bwd",
-                             "stability_bwd_state", "stability_bwd_bf16", "token_shift",
+                             "stability_bwd_state", "stability_bwd_bf16", "stability_fwd_ckpt",
+                             "stability_bwd_ckpt", "stability_bwd_ckpt_bf16", "token_shift",
                              "copy"])
     ap.add_argument("--plan", type=int, nargs="+", default=None,
                     metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
@@ -725,6 +752,11 @@ def main():
           "stability_bwd_state": lambda a, t, w, s: bench_stability(a, t, w, s, True, True),
           "stability_bwd_bf16": lambda a, t, w, s: bench_stability(a, t, w, s, True, False,
                                                                    "bf16"),
+          "stability_fwd_ckpt": lambda a, t, w, s: bench_stability(a, t, w, s, False,
+                                                                   ckpt=True),
+          "stability_bwd_ckpt": lambda a, t, w, s: bench_stability(a, t, w, s, True, ckpt=True),
+          "stability_bwd_ckpt_bf16": lambda a, t, w, s: bench_stability(a, t, w, s, True, False,
+                                                                        "bf16", ckpt=True),
           }[args.workload]
     torch.cuda.synchronize()
     out = fn(args, torch, wkv, synth)

@@ -341,6 +341,67 @@ WKV_API wkv_status wkv_backward_typed(int64_t B, int64_t T, int64_t C, wkv_dtype
                                       float *d_state_in, void *workspace,
                                       size_t workspace_bytes, hipStream_t stream);
 
+/* Tokens between two checkpoints of the forward state. */
+#define WKV_CHECKPOINT_TOKENS 128
+/* Checkpoints of a sequence of T tokens: one before every multiple of
+ * WKV_CHECKPOINT_TOKENS that lies strictly inside it. */
+#define WKV_CHECKPOINT_COUNT(T) ((T) > 0 ? ((T) - 1) / WKV_CHECKPOINT_TOKENS : 0)
+
+/*
+ * wkv_forward_typed that also saves the state every WKV_CHECKPOINT_TOKENS
+ * tokens, for a backward that starts from them.  Checkpoint i is the RNN-mode
+ * state (a, b, o) after the first (i + 1) * WKV_CHECKPOINT_TOKENS tokens,
+ * exactly the state_out of a call over that prefix (rwkv-architecture skill
+ * page, "Quick start": the state carried between calls; RWKV architecture
+ * deep dive, "Duality": the parallel and recurrent forms agree).  Training
+ * keeps them from the forward to the backward (skill page, "Workflow 3:
+ * Fine-tuning RWKV").
+ *
+ *   checkpoints  [WKV_CHECKPOINT_COUNT(T)][3][B][C] float32 output, fully
+ *                overwritten; each entry has the layout of state_out, so
+ *                checkpoints + i*3*B*C can serve as a later call's state_in.
+ *                Required when that count times B*C is positive, else ignored
+ *                (may be NULL).  Must not overlap any other argument.
+ * Every other argument, the plan, the result and the errors are those of
+ * wkv_forward_typed; y and state_out are bitwise those of wkv_forward_typed
+ * with the same plan (the look-back kernel excepted, which is not bitwise
+ * reproducible from call to call).  Writing the checkpoints adds
+ * 12 bytes per lane per WKV_CHECKPOINT_TOKENS tokens to the traffic.
+ */
+WKV_API wkv_status wkv_forward_checkpointed(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                            const float *w, const float *u, const void *k,
+                                            const void *v, const void *r, void *y,
+                                            const float *state_in, float *state_out,
+                                            float *checkpoints, const wkv_forward_plan *plan,
+                                            hipStream_t stream);
+
+/*
+ * wkv_backward_typed given the checkpoints that wkv_forward_checkpointed wrote
+ * for the same inputs and state_in.  The gradients are the same functions of
+ * the inputs; the forward states they need are rebuilt from the checkpoints,
+ * tile by tile, instead of by a first pass over k and v, which saves reading
+ * k and v twice (8 of the 28 bytes per lane-token that wkv_backward_typed
+ * moves in float32).  The pages state no backward; see wkv_backward.
+ *
+ *   checkpoints  [WKV_CHECKPOINT_COUNT(T)][3][B][C] as written by
+ *                wkv_forward_checkpointed for these w, u, k, v and state_in;
+ *                read only; required when that count times B*C is positive.
+ *                No output may overlap it
+ * Every other argument, the workspace size (wkv_backward_workspace_size) and
+ * the errors are those of wkv_backward_typed.  Results agree with
+ * wkv_backward_typed to rounding (the states pass through the checkpoints'
+ * float32 a, b, o once per tile); dw and du stay bitwise reproducible from
+ * run to run.
+ */
+WKV_API wkv_status wkv_backward_checkpointed(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                             const float *w, const float *u, const void *k,
+                                             const void *v, const void *dy,
+                                             const float *state_in, const float *checkpoints,
+                                             const float *state_out, const float *d_state_out,
+                                             void *dk, void *dv, float *dw, float *du,
+                                             float *d_state_in, void *workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
+
 /* Largest number of mixes wkv_token_shift takes in one call. */
 #define WKV_TOKEN_SHIFT_MAX_MIXES 8
 

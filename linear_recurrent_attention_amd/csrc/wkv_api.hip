@@ -188,16 +188,36 @@ wkv_status check_forward(int64_t B, int64_t T, int64_t C, const float *w, const 
 
 wkv_status from_hip(hipError_t e) { return e == hipSuccess ? WKV_OK : WKV_ERR_HIP; }
 
-// wkv_forward_ex, wkv_forward_gated and wkv_forward_typed: r is NULL for the
-// plain forward; io is the wkv_dtype of k, v, r and y.
+// Checkpoints of a sequence of T tokens: the states before tokens 128, 256, ...
+// that lie inside it.
+int64_t ckpt_count(int64_t T) { return T > 0 ? (T - 1) / wkv::kCkptTokens : 0; }
+
+// wkv_forward_ex, wkv_forward_gated, wkv_forward_typed and
+// wkv_forward_checkpointed: r is NULL for the plain forward; io is the
+// wkv_dtype of k, v, r and y; with_ck: the call writes checkpoints to ck.
 wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
                         const void *k, const void *v, const void *r, void *y,
                         const float *state_in, float *state_out, const wkv_forward_plan *plan,
-                        bool gated, int io, hipStream_t stream) {
+                        bool gated, int io, hipStream_t stream, bool with_ck = false,
+                        float *ck = nullptr) {
     const int64_t esize = elem_bytes(io);
     if (esize == 0) return WKV_ERR_UNSUPPORTED;
     wkv_status st = check_forward(B, T, C, w, u, k, v, y, state_in, state_out, r, gated, esize);
     if (st != WKV_OK) return st;
+    if (with_ck) {
+        const int64_t ckb = bytes_of(3 * ckpt_count(T), B, C);
+        if (ckb < 0) return WKV_ERR_OVERFLOW;
+        if (ckb > 0 && !ck) return WKV_ERR_NULL;
+        const int64_t seq = bytes_of(B, T, C, esize), sts = bytes_of(3, B, C),
+                      chs = bytes_of(1, 1, C);
+        const Range rc = rng(ck, ckb);
+        for (Range x : {rng(w, chs), rng(u, chs), rng(k, seq), rng(v, seq), rng(y, seq),
+                        rng(r, gated ? seq : 0), rng(state_in, sts), rng(state_out, sts)})
+            if (overlap(rc, x)) return WKV_ERR_ALIAS;
+        if (ckb == 0) ck = nullptr;
+    } else {
+        ck = nullptr;
+    }
     wkv_forward_plan p{WKV_KERNEL_AUTO, 0, 0, 0};
     if (plan) p = *plan;
     switch (p.kernel) {
@@ -246,7 +266,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
     } else if (capturing && p.kernel == WKV_KERNEL_LOOKBACK) {
         return WKV_ERR_UNSUPPORTED;
     }
-    const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr, io};
+    const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr, io, ck};
     if (p.kernel == WKV_KERNEL_LANE) {
         if ((lanes + 255) / 256 > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
         return from_hip(wkv::launch_forward_lane(a, stream));
@@ -291,13 +311,16 @@ wkv_status step_impl(int64_t L, int64_t B, int64_t C, const float *w, const floa
     return from_hip(wkv::launch_step(a, stream));
 }
 
-// wkv_backward, wkv_backward_state and wkv_backward_typed (the first with no
-// states); io is the wkv_dtype of k, v, dy, dk and dv.
+// wkv_backward, wkv_backward_state, wkv_backward_typed and
+// wkv_backward_checkpointed (the first with no states); io is the wkv_dtype of
+// k, v, dy, dk and dv; from_ck: the forward states come from the checkpoints
+// cks.
 wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w, const float *u,
                          const void *k, const void *v, const void *dy, const float *s_in,
                          const float *s_out, const float *ds_out, void *dk, void *dv,
                          float *dw, float *du, float *ds_in, void *workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+                         size_t workspace_bytes, hipStream_t stream, bool from_ck = false,
+                         const float *cks = nullptr) {
     const int64_t esize = elem_bytes(io);
     if (esize == 0) return WKV_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
@@ -309,18 +332,21 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w
     if (!dw || !du) return WKV_ERR_NULL;
     if (seq > 0 && (!w || !u || !k || !v || !dy || !dk || !dv)) return WKV_ERR_NULL;
     if (ds_out && !s_out && B > 0) return WKV_ERR_NULL;
+    const int64_t ckb = from_ck ? bytes_of(3 * ckpt_count(T), B, C) : 0;
+    if (ckb < 0) return WKV_ERR_OVERFLOW;
+    if (ckb > 0 && !cks) return WKV_ERR_NULL;
     const size_t need = wkv::backward_workspace_bytes(B, T, C);
     if (need > 0 && (!workspace || workspace_bytes < need)) return WKV_ERR_WORKSPACE;
     const Range rw = rng(w, seq > 0 ? ch : 0), ru = rng(u, seq > 0 ? ch : 0);
     const Range rk = rng(k, seq), rv = rng(v, seq), rg = rng(dy, seq);
     const Range rsi = rng(s_in, st), rso = rng(ds_out ? s_out : nullptr, st),
-                rdso = rng(ds_out, st);
+                rdso = rng(ds_out, st), rck = rng(cks, ckb);
     const Range rdk = rng(dk, seq), rdv = rng(dv, seq), rdw = rng(dw, ch), rdu = rng(du, ch);
     const Range rdsi = rng(ds_in, st);
     const Range rws = rng(workspace, (int64_t)need);
     const Range outs[] = {rdk, rdv, rdw, rdu, rws, rdsi};
     for (int i = 0; i < 6; ++i) {
-        for (Range r : {rw, ru, rk, rv, rg, rsi, rso})
+        for (Range r : {rw, ru, rk, rv, rg, rsi, rso, rck})
             if (overlap(outs[i], r)) return WKV_ERR_ALIAS;
         // d_state_in may replace d_state_out exactly (read before it is written)
         if (overlap(outs[i], rdso) && !(i == 5 && (const float *)ds_in == ds_out))
@@ -334,6 +360,8 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w
     a.s_out = s_out;
     a.ds_out = ds_out;
     a.ds_in = ds_in;
+    a.from_ck = from_ck;
+    a.ck = ckb > 0 ? cks : nullptr;
     return from_hip(wkv::launch_backward(a, stream));
 }
 
@@ -477,6 +505,29 @@ WKV_API wkv_status wkv_backward_typed(int64_t B, int64_t T, int64_t C, wkv_dtype
                                       size_t workspace_bytes, hipStream_t stream) {
     return backward_impl(B, T, C, (int)dtype, w, u, k, v, dy, state_in, state_out, d_state_out,
                          dk, dv, dw, du, d_state_in, workspace, workspace_bytes, stream);
+}
+
+WKV_API wkv_status wkv_forward_checkpointed(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                            const float *w, const float *u, const void *k,
+                                            const void *v, const void *r, void *y,
+                                            const float *state_in, float *state_out,
+                                            float *checkpoints, const wkv_forward_plan *plan,
+                                            hipStream_t stream) {
+    return forward_impl(B, T, C, w, u, k, v, r, y, state_in, state_out, plan, r != nullptr,
+                        (int)dtype, stream, true, checkpoints);
+}
+
+WKV_API wkv_status wkv_backward_checkpointed(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                             const float *w, const float *u, const void *k,
+                                             const void *v, const void *dy,
+                                             const float *state_in, const float *checkpoints,
+                                             const float *state_out, const float *d_state_out,
+                                             void *dk, void *dv, float *dw, float *du,
+                                             float *d_state_in, void *workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+    return backward_impl(B, T, C, (int)dtype, w, u, k, v, dy, state_in, state_out, d_state_out,
+                         dk, dv, dw, du, d_state_in, workspace, workspace_bytes, stream, true,
+                         checkpoints);
 }
 
 }  // extern "C"

@@ -208,8 +208,11 @@ __device__ __forceinline__ void fwd_token(Lane &L, float K, float v, const Chan 
 
 // IO: element format of k, v, dy, dk and dv (the states, w, u, dw, du and all
 // arithmetic are float32).  FULL: T is a whole number of tiles, so no token
-// needs a bounds test.
-template <int NW, int LS, bool SAFE, bool FULL, class IO>
+// needs a bounds test.  CK: the forward's checkpoints `cks` hold the state at
+// the start of every tile but the first; there is no phase 1, and each tile's
+// segment starting states are rebuilt in phase 2 by the same scan, from the
+// tile's checkpoint (or state_in).
+template <int NW, int LS, bool SAFE, bool FULL, bool CK, class IO>
 __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_t bb, int64_t c,
                                          bool active, const Chan &ch,
                                          const typename IO::T *kseq, const typename IO::T *vseq,
@@ -218,8 +221,9 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                                          float *__restrict__ ck,
                                          double *__restrict__ part, const float *s_in,
                                          const float *s_out, const float *ds_out, float *ds_in,
-                                         BwdShared<NW> &sh) {
+                                         const float *cks, BwdShared<NW> &sh) {
     constexpr int TT = NW * LS;
+    static_assert(!CK || TT == kCkptTokens, "one checkpoint per tile");
     const int lane = threadIdx.x & 63;
     const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t rowb = (uint32_t)(C * IO::kBytes);
@@ -229,7 +233,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
     const int64_t ntiles = (T + TT - 1) / TT;
 
     // ---------------- phase 1: starting state of every segment ----------------
-    {
+    if constexpr (!CK) {
         // the carried state: every wave folds it into its segments' starting states
         Lane carry = lane_empty();
         if (s_in && active)
@@ -322,11 +326,45 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             load_seg<LS>(Vn, rows(vseq, t0 - TT), t0 - TT, T);
             load_seg<LS>(Gn, rows(gseq, t0 - TT), t0 - TT, T);
         }
-        // forward recompute of y, lambda, p_ii from the stored starting state
+        // forward recompute of y, lambda, p_ii from the segment's starting state
         float Y[LS], LAM[LS], PII[LS];
         {
-            const float *q = ck + ((tile * NW + s) * 4) * 64 + lane;
-            Lane L{q[0], q[64], q[128], q[192]};
+            Lane L;
+            if constexpr (CK) {
+                // the tile's starting state: state_in for the first tile, else
+                // the checkpoint before it
+                const float *src = tile == 0 ? s_in : cks + (tile - 1) * 3 * B * C;
+                float a0 = 0.0f, b0 = 0.0f, o0 = kEmpty2;
+                if (src && active) {
+                    a0 = src[(0 * B + bb) * C + c];
+                    b0 = src[(1 * B + bb) * C + c];
+                    o0 = o_in(src[(2 * B + bb) * C + c]);
+                }
+                // this segment's summary, scanned over the tile's segments
+                Lane S = lane_empty();
+#pragma unroll
+                for (int j = 0; j < LS; ++j)
+                    if (FULL || t0 + j < T) absorb(S, Kc[j] * kLog2e, Vc[j], ch);
+                int fb = 0;
+#pragma unroll
+                for (int d = 1; d < NW; d <<= 1) {
+                    fwd_put(sh, fb, s, lane, S);
+                    __syncthreads();
+                    if (s >= d) {
+                        Lane X = fwd_get(sh, fb, s - d, lane);
+                        compose(X, S, ch.W, (float)(d * LS));
+                        S = X;
+                    }
+                    fb ^= 1;
+                }
+                fwd_put(sh, fb, s, lane, S);
+                __syncthreads();
+                L = lane_at(a0, b0, o0);
+                if (s > 0) compose(L, fwd_get(sh, fb, s - 1, lane), ch.W, (float)(s * LS));
+            } else {
+                const float *q = ck + ((tile * NW + s) * 4) * 64 + lane;
+                L = Lane{q[0], q[64], q[128], q[192]};
+            }
 #pragma unroll
             for (int j = 0; j < LS; ++j) {
                 Y[j] = 0.0f;
@@ -439,8 +477,9 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
     }
 }
 
-// FULL: T is a whole number of tiles (chosen on the host).
-template <int NW, int LS, bool FULL, class IO>
+// FULL: T is a whole number of tiles (chosen on the host).  CK: start every
+// tile from the forward's checkpoints `cks` instead of a first pass.
+template <int NW, int LS, bool FULL, bool CK, class IO>
 __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, int64_t C,
                                                           const float *__restrict__ w,
                                                           const float *__restrict__ u,
@@ -452,7 +491,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, 
                                                           float *__restrict__ ckpt,
                                                           double *__restrict__ part,
                                                           const float *s_in, const float *s_out,
-                                                          const float *ds_out, float *ds_in) {
+                                                          const float *ds_out, float *ds_in,
+                                                          const float *cks) {
     __shared__ BwdShared<NW> sh;
     constexpr int TT = NW * LS;
     const int64_t ngroups = (C + 63) / 64;
@@ -469,13 +509,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, 
     const uint32_t voff = active ? (uint32_t)((threadIdx.x & 63) * IO::kBytes) : 0u;
     float *ck = ckpt + (int64_t)blockIdx.x * ntiles * NW * 4 * 64;
     if (fast)
-        bwd_body<NW, LS, false, FULL, IO>(B, T, C, bb, c, active, ch, k + base, v + base,
-                                          dy + base, dk + base, dv + base, voff, ck, part, s_in,
-                                          s_out, ds_out, ds_in, sh);
+        bwd_body<NW, LS, false, FULL, CK, IO>(B, T, C, bb, c, active, ch, k + base, v + base,
+                                              dy + base, dk + base, dv + base, voff, ck, part,
+                                              s_in, s_out, ds_out, ds_in, cks, sh);
     else
-        bwd_body<NW, LS, true, FULL, IO>(B, T, C, bb, c, active, ch, k + base, v + base,
-                                         dy + base, dk + base, dv + base, voff, ck, part, s_in,
-                                         s_out, ds_out, ds_in, sh);
+        bwd_body<NW, LS, true, FULL, CK, IO>(B, T, C, bb, c, active, ch, k + base, v + base,
+                                             dy + base, dk + base, dv + base, voff, ck, part,
+                                             s_in, s_out, ds_out, ds_in, cks, sh);
 }
 
 // dw[c], du[c] = sums over the batch of the per-lane parts, in order b = 0..B-1.
@@ -525,21 +565,29 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(int64_t n, const fl
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-template <bool FULL, class IO>
+template <bool FULL, bool CK, class IO>
 void launch_bwd_seg_k(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
     using T = typename IO::T;
-    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS, FULL, IO>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS, FULL, CK, IO>), dim3((unsigned)grid),
                        dim3(kBwdNW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, (const T *)a.k,
                        (const T *)a.v, (const T *)a.dy, (T *)a.dk, (T *)a.dv, ck, part, a.s_in,
-                       a.s_out, a.ds_out, a.ds_in);
+                       a.s_out, a.ds_out, a.ds_in, a.ck);
+}
+
+template <bool CK, class IO>
+void launch_bwd_seg_ck(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
+    if (a.T % (kBwdNW * kBwdLS) == 0)
+        launch_bwd_seg_k<true, CK, IO>(a, grid, ck, part, st);
+    else
+        launch_bwd_seg_k<false, CK, IO>(a, grid, ck, part, st);
 }
 
 template <class IO>
 void launch_bwd_seg(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
-    if (a.T % (kBwdNW * kBwdLS) == 0)
-        launch_bwd_seg_k<true, IO>(a, grid, ck, part, st);
+    if (a.from_ck)
+        launch_bwd_seg_ck<true, IO>(a, grid, ck, part, st);
     else
-        launch_bwd_seg_k<false, IO>(a, grid, ck, part, st);
+        launch_bwd_seg_ck<false, IO>(a, grid, ck, part, st);
 }
 
 }  // namespace

@@ -306,4 +306,13 @@ __device__ __forceinline__ float gate_of(float r) { return rcp(1.0f + ex2(-r * k
 __device__ __forceinline__ float o_in(float o_nat) { return fmaxf(o_nat * kLog2e, kEmpty2); }
 __device__ __forceinline__ float o_out(float o2) { return o2 * kLn2; }
 
+// Stores state L of lane i in the public layout [3][n] (a, b, o with o in
+// natural-log units), each plane n floats apart.
+__device__ __forceinline__ void store_state(float *dst, int64_t n, int64_t i, const Lane &L,
+                                            float W, float poison) {
+    dst[i] = L.a + poison;
+    dst[n + i] = L.b + poison;
+    dst[2 * n + i] = o_out(lane_o(L, W)) + poison;
+}
+
 }  // namespace wkv

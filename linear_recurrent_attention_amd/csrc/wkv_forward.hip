@@ -33,16 +33,24 @@ namespace wkv {
 // One thread per lane.
 // ---------------------------------------------------------------------------
 // GATE: y = sigmoid(r) * wkv with r read beside k and v.  IO: element format.
+// ck: NULL, or where the state before every token t = i * kCkptTokens (i >= 1)
+// goes, as checkpoint i - 1 of lane `li` among n lanes.
 template <bool SAFE, bool GATE, class IO>
 __device__ __forceinline__ void lane_sweep(int64_t T, int64_t C,
                                            const typename IO::T *__restrict__ kp,
                                            const typename IO::T *__restrict__ vp,
                                            const typename IO::T *__restrict__ rp,
                                            typename IO::T *__restrict__ yp, Lane &L,
-                                           const Chan &ch) {
+                                           const Chan &ch, float *ck, int64_t n, int64_t li) {
     int64_t t = 0;
     constexpr int U8 = 8;
+    static_assert(kCkptTokens % U8 == 0, "checkpoints fall on whole groups of tokens");
+    auto checkpoint = [&]() {
+        if (ck && t > 0 && t % kCkptTokens == 0)
+            store_state(ck + (t / kCkptTokens - 1) * 3 * n, n, li, L, ch.W, 0.0f);
+    };
     for (; t + U8 <= T; t += U8) {
+        checkpoint();
         float K[U8], V[U8], R[U8];
 #pragma unroll
         for (int j = 0; j < U8; ++j) {
@@ -58,6 +66,7 @@ __device__ __forceinline__ void lane_sweep(int64_t T, int64_t C,
         }
     }
     for (; t < T; ++t) {
+        checkpoint();
         float yv = step<SAFE>(L, IO::to_f(kp[t * C]) * kLog2e, IO::to_f(vp[t * C]), ch);
         if constexpr (GATE) yv *= gate_of(IO::to_f(rp[t * C]));
         yp[t * C] = IO::from_f(yv);
@@ -73,7 +82,8 @@ __global__ __launch_bounds__(256) void fwd_lane_kernel(int64_t B, int64_t T, int
                                                        const typename IO::T *__restrict__ r,
                                                        typename IO::T *__restrict__ y,
                                                        const float *__restrict__ s_in,
-                                                       float *__restrict__ s_out) {
+                                                       float *__restrict__ s_out,
+                                                       float *__restrict__ ck) {
     const int64_t lane = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const bool active = lane < B * C;
     const int64_t bb = active ? lane / C : 0;
@@ -89,9 +99,11 @@ __global__ __launch_bounds__(256) void fwd_lane_kernel(int64_t B, int64_t T, int
     const int64_t base = bb * T * C + c;
     const typename IO::T *rp = GATE ? r + base : nullptr;
     if (wave_fast)
-        lane_sweep<false, GATE, IO>(T, C, k + base, v + base, rp, y + base, L, ch);
+        lane_sweep<false, GATE, IO>(T, C, k + base, v + base, rp, y + base, L, ch, ck, B * C,
+                                    lane);
     else
-        lane_sweep<true, GATE, IO>(T, C, k + base, v + base, rp, y + base, L, ch);
+        lane_sweep<true, GATE, IO>(T, C, k + base, v + base, rp, y + base, L, ch, ck, B * C,
+                                   lane);
     if (s_out) {
         s_out[(0 * B + bb) * C + c] = L.a;
         s_out[(1 * B + bb) * C + c] = L.b;
@@ -174,7 +186,8 @@ __device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], con
                                          const float (&Rg)[GATE ? LS : 1], Lane &carry, const SegGeom<NW, LS, CW> &G, int64_t B,
                                          int64_t T, int64_t C, int64_t bb, int64_t c, bool active,
                                          const Chan &ch, typename IO::T *yseq, uint32_t voff,
-                                         float *__restrict__ s_out, SegShared<NW> &sh) {
+                                         float *__restrict__ s_out, float *__restrict__ ck,
+                                         SegShared<NW> &sh) {
     using Geo = SegGeom<NW, LS, CW>;
     const int64_t t0 = tile * Geo::TT + (int64_t)G.seg * LS;
 
@@ -210,6 +223,10 @@ __device__ __forceinline__ void seg_tile(int64_t tile, const float (&K)[LS], con
     if (G.seg > 0) compose(R, sh.get(buf, G.slot - CW), ch.W, (float)(G.seg * LS));
     // carry for the next tile: carry, then the whole tile
     compose(carry, sh.get(buf, (Geo::NSEG - 1) * CW + (G.lane % CW)), ch.W, (float)Geo::TT);
+    // a segment that starts on a checkpoint token stores its starting state
+    static_assert(kCkptTokens % LS == 0, "checkpoints fall on segment starts");
+    if (ck && active && t0 > 0 && t0 < T && t0 % kCkptTokens == 0)
+        store_state(ck + (t0 / kCkptTokens - 1) * 3 * B * C, B * C, bb * C + c, R, ch.W, 0.0f);
 
     // (3) re-sweep from the prefix state, emitting y
     const int64_t tw = tile * Geo::TT + (int64_t)G.wave * Geo::SPW * LS;  // wave's first row
@@ -249,7 +266,7 @@ __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_
                                          const typename IO::T *vseq, const typename IO::T *rseq,
                                          typename IO::T *yseq, uint32_t voff,
                                          const float *__restrict__ s_in, float *__restrict__ s_out,
-                                         SegShared<NW> &sh) {
+                                         float *__restrict__ ck, SegShared<NW> &sh) {
     using Geo = SegGeom<NW, LS, CW>;
     const int64_t ntiles = (T + Geo::TT - 1) / Geo::TT;
     const uint32_t rowb = (uint32_t)(C * IO::kBytes);
@@ -286,16 +303,16 @@ __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_
         load_r(Rc, tile);
         load(KB, VB, tile + 1);
         seg_tile<NW, LS, CW, SAFE, FULL, GATE, IO>(tile, KA, VA, Rc, carry, G, B, T, C, bb, c, active,
-                                               ch, yseq, voff, s_out, sh);
+                                               ch, yseq, voff, s_out, ck, sh);
         load_r(Rc, tile + 1);
         if (tile + 2 < ntiles) load(KA, VA, tile + 2);
         seg_tile<NW, LS, CW, SAFE, FULL, GATE, IO>(tile + 1, KB, VB, Rc, carry, G, B, T, C, bb, c,
-                                               active, ch, yseq, voff, s_out, sh);
+                                               active, ch, yseq, voff, s_out, ck, sh);
     }
     if (tile < ntiles) {
         load_r(Rc, tile);
         seg_tile<NW, LS, CW, SAFE, FULL, GATE, IO>(tile, KA, VA, Rc, carry, G, B, T, C, bb, c, active,
-                                               ch, yseq, voff, s_out, sh);
+                                               ch, yseq, voff, s_out, ck, sh);
     }
 }
 
@@ -308,7 +325,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_seg_kernel(int64_t B, int64_t T, 
                                                           const typename IO::T *__restrict__ r,
                                                           typename IO::T *__restrict__ y,
                                                           const float *__restrict__ s_in,
-                                                          float *__restrict__ s_out) {
+                                                          float *__restrict__ s_out,
+                                                          float *__restrict__ ck) {
     using Geo = SegGeom<NW, LS, CW>;
     __shared__ SegShared<NW> sh;
     const int64_t ngroups = (C + CW - 1) / CW;
@@ -335,16 +353,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_seg_kernel(int64_t B, int64_t T, 
     const typename IO::T *rs = GATE ? r + base : nullptr;
     if (fast && full)
         seg_body<NW, LS, CW, false, true, GATE, IO>(B, T, C, bb, c, active, ch, G, k + base, v + base,
-                                                rs, y + base, voff, s_in, s_out, sh);
+                                                rs, y + base, voff, s_in, s_out, ck, sh);
     else if (fast)
         seg_body<NW, LS, CW, false, false, GATE, IO>(B, T, C, bb, c, active, ch, G, k + base,
-                                                 v + base, rs, y + base, voff, s_in, s_out, sh);
+                                                 v + base, rs, y + base, voff, s_in, s_out, ck, sh);
     else if (full)
         seg_body<NW, LS, CW, true, true, GATE, IO>(B, T, C, bb, c, active, ch, G, k + base, v + base,
-                                               rs, y + base, voff, s_in, s_out, sh);
+                                               rs, y + base, voff, s_in, s_out, ck, sh);
     else
         seg_body<NW, LS, CW, true, false, GATE, IO>(B, T, C, bb, c, active, ch, G, k + base, v + base,
-                                                rs, y + base, voff, s_in, s_out, sh);
+                                                rs, y + base, voff, s_in, s_out, ck, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -371,7 +389,7 @@ static hipError_t launch_lane(const FwdArgs &a, hipStream_t st) {
     const int64_t grid = (a.B * a.C + 255) / 256;
     hipLaunchKernelGGL((fwd_lane_kernel<GATE, IO>), dim3((unsigned)grid), dim3(256), 0, st, a.B,
                        a.T, a.C, a.w, a.u, (const T *)a.k, (const T *)a.v, (const T *)a.r,
-                       (T *)a.y, a.s_in, a.s_out);
+                       (T *)a.y, a.s_in, a.s_out, a.ck);
     return hipGetLastError();
 }
 
@@ -395,7 +413,7 @@ static hipError_t launch_seg(const FwdArgs &a, hipStream_t st) {
     const int64_t grid = a.B * ((a.C + CW - 1) / CW);
     hipLaunchKernelGGL((fwd_seg_kernel<NW, LS, CW, GATE, IO>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, (const T *)a.k,
-                       (const T *)a.v, (const T *)a.r, (T *)a.y, a.s_in, a.s_out);
+                       (const T *)a.v, (const T *)a.r, (T *)a.y, a.s_in, a.s_out, a.ck);
     return hipGetLastError();
 }
 

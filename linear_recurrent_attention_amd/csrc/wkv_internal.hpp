@@ -12,8 +12,13 @@ namespace wkv {
 // state are always float32.
 constexpr int kIoF32 = 0, kIoF16 = 1, kIoBF16 = 2;
 
+// Tokens between two checkpoints of the forward state: the backward's tile.
+constexpr int64_t kCkptTokens = 128;
+
 // r: receptance of the time-mixing gate, same layout as k; NULL: y = wkv,
 // else y = sigmoid(r) * wkv.  k, v, r, y hold elements of format `io`.
+// ck: NULL, or [(T-1)/kCkptTokens][3][B][C]: the state before token
+// (i+1)*kCkptTokens goes to ck[i] (every forward kernel writes them).
 struct FwdArgs {
     int64_t B, T, C;
     const float *w, *u;
@@ -23,6 +28,7 @@ struct FwdArgs {
     float *s_out;
     const void *r;
     int io;
+    float *ck = nullptr;
 };
 
 struct StepArgs {
@@ -56,6 +62,11 @@ struct BwdArgs {
     const float *s_in, *s_out, *ds_out;
     float *ds_in;
     int io;
+    // from_ck: the forward states are rebuilt tile by tile from the forward's
+    // checkpoints ck (layout of FwdArgs::ck; NULL when T <= kCkptTokens, which
+    // has none) instead of by a first pass over k and v
+    const float *ck = nullptr;
+    bool from_ck = false;
 };
 
 // forward (wkv_forward.hip)

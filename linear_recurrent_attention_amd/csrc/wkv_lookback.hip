@@ -121,8 +121,9 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
                                         const LbWave &q, const float (&K)[LS], const float (&V)[LS],
                                         const float (&Rg)[GATE ? LS : 1],
                                         typename IO::T *yseq, const float *__restrict__ s_in,
-                                        float *__restrict__ s_out, Word *aggs, Word *incls,
-                                        uint32_t epoch, LbShared<CG, NS> &sh) {
+                                        float *__restrict__ s_out, float *__restrict__ ck,
+                                        Word *aggs, Word *incls, uint32_t epoch,
+                                        LbShared<CG, NS> &sh) {
     constexpr int TB = NS * LS;
     const int lane = q.lane, g = q.g, s = q.s;
     const int64_t j = q.j;
@@ -237,6 +238,11 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
     Lane R = P;
     for (int w = 0; w < s; ++w) compose(R, lds_lane(sh.s, w, g, lane), ch.W, (float)LS);
     const float poison = failed ? __builtin_nanf("") : 0.0f;
+    // a segment that starts on a checkpoint token stores its starting state
+    static_assert(kCkptTokens % LS == 0, "checkpoints fall on segment starts");
+    if (ck && q.active && q.t0 > 0 && q.t0 < T && q.t0 % kCkptTokens == 0)
+        store_state(ck + (q.t0 / kCkptTokens - 1) * 3 * B * C, B * C, q.bb * C + q.c, R, ch.W,
+                    poison);
     if (q.gok) {
         const TileRowsT<IO> yr(yseq + q.t0 * C, q.voff, q.rowb);
         bool framed = false;
@@ -290,7 +296,7 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
     int64_t B, int64_t T, int64_t C, const float *__restrict__ w, const float *__restrict__ u,
     const typename IO::T *__restrict__ k, const typename IO::T *__restrict__ v,
     const typename IO::T *__restrict__ r, typename IO::T *__restrict__ y, const float *s_in,
-    float *s_out, Word *aggs, Word *incls, uint32_t epoch, uint32_t nsets) {
+    float *s_out, float *ck, Word *aggs, Word *incls, uint32_t epoch, uint32_t nsets) {
     constexpr int TB = NS * LS;
     __shared__ LbShared<CG, NS> sh;
     LbWave q;
@@ -360,17 +366,17 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
     if (fast) {
         if (full)
             lb_body<CG, NS, LS, false, true, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
-                                                   s_out, aggs, incls, epoch, sh);
+                                                   s_out, ck, aggs, incls, epoch, sh);
         else
             lb_body<CG, NS, LS, false, false, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
-                                                    s_out, aggs, incls, epoch, sh);
+                                                    s_out, ck, aggs, incls, epoch, sh);
     } else {
         if (full)
             lb_body<CG, NS, LS, true, true, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
-                                                  s_out, aggs, incls, epoch, sh);
+                                                  s_out, ck, aggs, incls, epoch, sh);
         else
             lb_body<CG, NS, LS, true, false, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
-                                                   s_out, aggs, incls, epoch, sh);
+                                                   s_out, ck, aggs, incls, epoch, sh);
     }
 }
 
@@ -413,7 +419,7 @@ hipError_t launch_lb(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st
     hipLaunchKernelGGL((fwd_lookback_kernel<CG, NS, LS, GATE, IO>),
                        dim3((unsigned)(nsets * a.B * nblocks)), dim3(CG * NS * 64), 0, st, a.B,
                        a.T, a.C, a.w, a.u, (const T *)a.k, (const T *)a.v, (const T *)a.r,
-                       (T *)a.y, a.s_in, a.s_out, aggs, incls, sc.epoch, (uint32_t)nsets);
+                       (T *)a.y, a.s_in, a.s_out, a.ck, aggs, incls, sc.epoch, (uint32_t)nsets);
     return hipGetLastError();
 }
 

@@ -42,7 +42,8 @@ WKV_KERNEL_LOOKBACK = 3
 EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backward",
             "wkv_status_string", "wkv_forward_ex", "wkv_forward_plan_auto",
             "wkv_forward_gated", "wkv_step_gated", "wkv_token_shift", "wkv_forward_typed",
-            "wkv_step_typed", "wkv_backward_state", "wkv_backward_typed")
+            "wkv_step_typed", "wkv_backward_state", "wkv_backward_typed",
+            "wkv_forward_checkpointed", "wkv_backward_checkpointed")
 
 # wkv_dtype values
 WKV_DTYPE_F32 = 0
@@ -52,6 +53,12 @@ _DTYPES = {torch.float32: WKV_DTYPE_F32, torch.float16: WKV_DTYPE_F16,
            torch.bfloat16: WKV_DTYPE_BF16}
 
 WKV_TOKEN_SHIFT_MAX_MIXES = 8
+WKV_CHECKPOINT_TOKENS = 128
+
+
+def checkpoint_count(T: int) -> int:
+    """Checkpoints of a sequence of T tokens (WKV_CHECKPOINT_COUNT)."""
+    return (T - 1) // WKV_CHECKPOINT_TOKENS if T > 0 else 0
 
 
 class WkvError(RuntimeError):
@@ -107,6 +114,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_backward_typed.argtypes = ([i64, i64, i64, ctypes.c_int] + [vp] * 13 +
                                        [vp, sz, vp])
     lib.wkv_backward_typed.restype = ctypes.c_int
+    lib.wkv_forward_checkpointed.argtypes = ([i64, i64, i64, ctypes.c_int] + [vp] * 9 +
+                                             [ctypes.POINTER(ForwardPlan), vp])
+    lib.wkv_forward_checkpointed.restype = ctypes.c_int
+    lib.wkv_backward_checkpointed.argtypes = ([i64, i64, i64, ctypes.c_int] + [vp] * 14 +
+                                              [vp, sz, vp])
+    lib.wkv_backward_checkpointed.restype = ctypes.c_int
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -215,6 +228,31 @@ def wkv_forward_typed(w, u, k, v, r=None, y=None, state_in=None, state_out=None,
                                           _stream(stream))
     _check("wkv_forward_typed", st)
     return y, state_out
+
+
+def wkv_forward_checkpointed(w, u, k, v, r=None, y=None, state_in=None, state_out=None,
+                             checkpoints=None, stream=None, plan=None):
+    """``wkv_forward_typed`` that also writes the state before every multiple of
+    WKV_CHECKPOINT_TOKENS tokens inside the sequence into ``checkpoints``
+    ([checkpoint_count(T)][3][B][C] float32, allocated when None).  Returns
+    (y, state_out, checkpoints)."""
+    if k.dtype not in _DTYPES:
+        raise TypeError(f"unsupported element type {k.dtype}")
+    dt = k.dtype
+    B, T, C = _bundle_shape(k, state_in)
+    if y is None:
+        y = torch.empty_like(k)
+    if state_out is True:
+        state_out = torch.empty((3, B, C), device=k.device, dtype=torch.float32)
+    if checkpoints is None:
+        checkpoints = torch.empty((checkpoint_count(T), 3, B, C), device=k.device,
+                                  dtype=torch.float32)
+    st = load_library().wkv_forward_checkpointed(
+        B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt), _ptr(v, dt), _ptr(r, dt),
+        _ptr(y, dt), _ptr(state_in), _ptr(state_out), _ptr(checkpoints), _plan(plan),
+        _stream(stream))
+    _check("wkv_forward_checkpointed", st)
+    return y, state_out, checkpoints
 
 
 def bind_forward(w, u, k, v, y, state_in=None, state_out=None, stream=None, plan=None):
@@ -399,4 +437,36 @@ def wkv_backward_typed(w, u, k, v, dy, state_in=None, state_out=None, d_state_ou
         _ptr(state_in), _ptr(state_out), _ptr(d_state_out), _ptr(dk, dt), _ptr(dv, dt), _ptr(dw),
         _ptr(du), _ptr(d_state_in), ws_ptr, workspace.numel(), _stream(stream))
     _check("wkv_backward_typed", st)
+    return dk, dv, dw, du, d_state_in
+
+
+def wkv_backward_checkpointed(w, u, k, v, dy, checkpoints, state_in=None, state_out=None,
+                              d_state_out=None, dk=None, dv=None, dw=None, du=None,
+                              d_state_in=None, workspace=None, stream=None):
+    """``wkv_backward_typed`` that rebuilds the forward states from the
+    checkpoints ``wkv_forward_checkpointed`` wrote for the same inputs and
+    state_in, instead of re-reading k and v in a first pass."""
+    if k.dtype not in _DTYPES:
+        raise TypeError(f"unsupported element type {k.dtype}")
+    dt = k.dtype
+    B, T, C = _bundle_shape(k, None)
+    dev = k.device
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    dw = torch.empty(C, device=dev, dtype=torch.float32) if dw is None else dw
+    du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
+    if d_state_in is True:
+        d_state_in = torch.empty((3, B, C), device=dev, dtype=torch.float32)
+    need = wkv_backward_workspace_size(B, T, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
+    st = load_library().wkv_backward_checkpointed(
+        B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt), _ptr(v, dt), _ptr(dy, dt),
+        _ptr(state_in), _ptr(checkpoints), _ptr(state_out), _ptr(d_state_out), _ptr(dk, dt),
+        _ptr(dv, dt), _ptr(dw), _ptr(du), _ptr(d_state_in), ws_ptr, workspace.numel(),
+        _stream(stream))
+    _check("wkv_backward_checkpointed", st)
     return dk, dv, dw, du, d_state_in

@@ -163,6 +163,60 @@ def test_backward_typed_checks(lib):
              None) == W.WKV_ERR_NULL
 
 
+def test_checkpoint_count_matches_the_header():
+    from linear_recurrent_attention_amd import wkv as W
+    src = open(HEADER).read()
+    m = re.search(r"#define WKV_CHECKPOINT_TOKENS (\d+)", src)
+    assert m and int(m.group(1)) == W.WKV_CHECKPOINT_TOKENS == 128
+    # one checkpoint before every multiple of 128 strictly inside the sequence
+    for T, n in ((0, 0), (1, 0), (127, 0), (128, 0), (129, 1), (256, 1), (257, 2), (4096, 31),
+                 (1024, 7)):
+        assert W.checkpoint_count(T) == n, T
+
+
+def test_checkpointed_calls_reject_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    w, u, k, v = vp(P), vp(P + 0x1000), vp(P + 0x100000), vp(P + 0x10000000)
+    y, ck = vp(P + 0x20000000), vp(P + 0x40000000)
+    f = lib.wkv_forward_checkpointed
+    # B=2 T=300 C=16: two checkpoints, 2 x 3 x 2 x 16 floats = 768 bytes
+    assert f(2, 300, 16, W.WKV_DTYPE_F32, w, u, k, v, None, y, None, None, None, None,
+             None) == W.WKV_ERR_NULL
+    assert f(2, 300, 16, 5, w, u, k, v, None, y, None, None, ck, None, None) == \
+        W.WKV_ERR_UNSUPPORTED
+    assert f(-2, 300, 16, W.WKV_DTYPE_F32, w, u, k, v, None, y, None, None, ck, None,
+             None) == W.WKV_ERR_DIM
+    assert f(2, 300, 16, W.WKV_DTYPE_F32, w, u, k, v, None, y, None, None,
+             vp(P + 0x20000000 + 4), None, None) == W.WKV_ERR_ALIAS      # on y
+    assert f(2, 300, 16, W.WKV_DTYPE_F32, w, u, k, v, None, y, None, vp(P + 0x40000000 + 764),
+             ck, None, None) == W.WKV_ERR_ALIAS                           # state_out on its end
+    assert f(2, 300, 16, W.WKV_DTYPE_BF16, w, u, k, v, vp(P + 0x30000000), y, None, None,
+             vp(P + 0x30000000 + 8), None, None) == W.WKV_ERR_ALIAS      # on r
+    p = W.ForwardPlan(W.WKV_KERNEL_SEGMENTED, 3, 16, 0)
+    assert f(2, 300, 16, W.WKV_DTYPE_F32, w, u, k, v, None, y, None, None, ck, ctypes.byref(p),
+             None) == W.WKV_ERR_UNSUPPORTED
+    ins = [vp(P + i * 0x10000000) for i in range(5)]           # w u k v dy
+    outs = [vp(P + (8 + i) * 0x10000000) for i in range(4)]    # dk dv dw du
+    ws = vp(P + 16 * 0x10000000)
+    n = lib.wkv_backward_workspace_size(2, 300, 16)
+    g = lib.wkv_backward_checkpointed
+    assert g(2, 300, 16, W.WKV_DTYPE_F32, *ins, None, None, None, None, *outs, None, ws, n,
+             None) == W.WKV_ERR_NULL                              # checkpoints missing
+    assert g(2, 300, 16, 9, *ins, None, ck, None, None, *outs, None, ws, n, None) == \
+        W.WKV_ERR_UNSUPPORTED
+    bad = list(outs)
+    bad[1] = vp(P + 0x40000000 + 512)                          # dv over the checkpoints
+    assert g(2, 300, 16, W.WKV_DTYPE_F32, *ins, None, ck, None, None, *bad, None, ws, n,
+             None) == W.WKV_ERR_ALIAS
+    assert g(2, 300, 16, W.WKV_DTYPE_F32, *ins, None, ck, None, None, *outs,
+             vp(P + 0x40000000 + 8), ws, n, None) == W.WKV_ERR_ALIAS    # d_state_in on them
+    assert g(2, 300, 16, W.WKV_DTYPE_F32, *ins, None, ck, None, None, *outs, None, ck, n,
+             None) == W.WKV_ERR_ALIAS                             # workspace on them
+    assert g(2, 300, 16, W.WKV_DTYPE_F32, *ins, None, ck, None, None, *outs, None, ws, n - 1,
+             None) == W.WKV_ERR_WORKSPACE
+
+
 def test_forward_ex_rejects_unknown_plans(lib):
     from linear_recurrent_attention_amd import wkv as W
     vp = ctypes.c_void_p
