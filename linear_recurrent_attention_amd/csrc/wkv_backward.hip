@@ -31,6 +31,10 @@
 //            R = R_early + 2^{-W len} R_late, R' = R'_early + 2^{-W len}(R'_late +
 //            len R_late)); re-sweep backward from each segment's suffix state,
 //            emitting dk, dv and accumulating dw, du.
+// With the forward's checkpoints (the state before every 128th token: one per
+// tile) there is no phase 1: phase 2 folds each segment's tokens from the
+// empty state, scans the summaries across the waves and starts from the
+// tile's checkpoint, which saves reading k and v a second time.
 // dw and du: per-thread float sums, combined across waves and then across the
 // batch in double precision in a fixed order (deterministic; no atomics).
 //

@@ -24,6 +24,10 @@
 //                    current one is processed.  The section "Parallel training
 //                    formulation" says the sequence is computed with a scan;
 //                    this is one.
+// Every forward kernel can also store the state before every 128th token
+// (checkpoints, for a backward that starts from them): in the lane kernel
+// every 128 tokens of the sweep, in the segmented and look-back kernels where
+// a segment's re-sweep starts on such a token.
 #include "wkv_device.hpp"
 #include "wkv_internal.hpp"
 

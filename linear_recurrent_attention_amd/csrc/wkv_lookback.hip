@@ -13,10 +13,12 @@
 // looks back over earlier blocks of each of its groups, folding their
 // published states until it meets one that holds the whole prefix, publishes
 // its own inclusive state, and every wave re-sweeps its tokens from its own
-// starting state, writing y.  Each workgroup reads its k and v once and
-// writes its y once, so HBM traffic is the algorithmic 12 bytes per
-// lane-token; the workgroups are small and short-lived, so many of them per
-// CU keep the memory system busy while others wait.
+// starting state, writing y (a wave whose segment starts on a multiple of 128
+// tokens also stores that state as a checkpoint, when asked to).  Each
+// workgroup reads its k and v once and writes its y once, so HBM traffic is
+// the algorithmic 12 bytes per lane-token; the workgroups are small and
+// short-lived, so many of them per CU keep the memory system busy while
+// others wait.
 //
 // Publishing without fences.  A release fence at device scope writes back the
 // issuing die's whole L2 and costs ~0.1 us per workgroup on MI355X, serialised,
