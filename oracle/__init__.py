@@ -48,11 +48,12 @@ def _load():
         lib.wkvo_backward_scan.argtypes = [i64, i64, i64, D, D, D, D, D, D, D, D, D,
                                            ctypes.c_int]
         lib.wkvo_gate.argtypes = [i64, D, D, D]
+        lib.wkvo_gate_backward.argtypes = [i64, D, D, D, D, D]
         lib.wkvo_backward_state.argtypes = [i64, i64, i64] + [D] * 13
         lib.wkvo_token_shift.argtypes = [i64, i64, i64, i64, D, D, D, D, D]
         for f in (lib.wkvo_forward_brute, lib.wkvo_forward_scan, lib.wkvo_backward_brute,
                   lib.wkvo_backward_scan, lib.wkvo_gate, lib.wkvo_token_shift,
-                  lib.wkvo_backward_state):
+                  lib.wkvo_backward_state, lib.wkvo_gate_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -172,6 +173,21 @@ def gate(y, r):
     if rc:
         raise RuntimeError(f"wkvo_gate failed ({rc})")
     return out
+
+
+def gate_backward(y, r, d):
+    """Backward of the gate out = sigmoid(r) * y for the upstream gradient d of
+    out: returns (g, dr), g = d * sigmoid(r) the gradient reaching y and
+    dr = d * y * sigmoid(r) * (1 - sigmoid(r)).  Elementwise, float64."""
+    y, r, d = _f64(y), _f64(r), _f64(d)
+    if y.shape != r.shape or y.shape != d.shape:
+        raise ValueError("y, r and d must have the same shape")
+    g = np.empty(y.shape)
+    dr = np.empty(y.shape)
+    rc = _load().wkvo_gate_backward(int(y.size), _ptr(y), _ptr(r), _ptr(d), _ptr(g), _ptr(dr))
+    if rc:
+        raise RuntimeError(f"wkvo_gate_backward failed ({rc})")
+    return g, dr
 
 
 def token_shift(mu, x, x_prev=None):

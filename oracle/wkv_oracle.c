@@ -47,6 +47,8 @@
  *                          includes the carried states, reduction to
  *                          wkvo_backward_brute, chunking identity)
  *   wkvo_gate              pinned (library logistic function, limits, r = 0)
+ *   wkvo_gate_backward     pinned (central finite differences of wkvo_gate in
+ *                          y and in r, saturated tails)
  *   wkvo_token_shift       pinned (hand-computed fixture, mu = 0 and mu = 1
  *                          limits, chunking identity)
  */
@@ -447,6 +449,33 @@ int wkvo_gate(int64_t n, const double *y, const double *r, double *out) {
             s = e / (1.0 + e);
         }
         out[i] = s * y[i];
+    }
+    return 0;
+}
+
+/*
+ * Backward of [Block]'s gate, out = s y with s = sigmoid(r): for the upstream
+ * gradient d of out, the gradient reaching the WKV output is g = d s and the
+ * gradient of the receptance is dr = d y s (1 - s), s (1 - s) being the
+ * derivative of the logistic function.  The pages state no backward; this is
+ * the chain rule on wkvo_gate.
+ */
+int wkvo_gate_backward(int64_t n, const double *y, const double *r, const double *d,
+                       double *g, double *dr) {
+    if (n < 0 || (n > 0 && (!y || !r || !d || !g || !dr))) return 1;
+    for (int64_t i = 0; i < n; ++i) {
+        double s, sc; /* sigmoid(r) and 1 - sigmoid(r), each without cancellation */
+        if (r[i] >= 0.0) {
+            const double e = exp(-r[i]);
+            s = 1.0 / (1.0 + e);
+            sc = e / (1.0 + e);
+        } else {
+            const double e = exp(r[i]);
+            s = e / (1.0 + e);
+            sc = 1.0 / (1.0 + e);
+        }
+        g[i] = d[i] * s;
+        dr[i] = d[i] * y[i] * s * sc;
     }
     return 0;
 }

@@ -141,3 +141,43 @@ def test_captured_time_mixing_calls_replay_exactly():
         torch.cuda.synchronize()
         for n, t in outs.items():
             assert torch.equal(t, ref[n]), f"replay {rep}: {n} differs from the eager result"
+
+
+def test_captured_training_path_replays_exactly():
+    """The forward that writes its 128-token checkpoints and the backward that
+    starts from them, captured together: every replay reproduces the eager bits
+    (the segmented forward and the backward are bitwise reproducible)."""
+    dev = torch.device("cuda")
+    B, T, C = 2, 700, 96
+    side = torch.cuda.Stream()
+    d = synth.make(synth.STABILITY, index=94, B=B, T=T, C=C, device=dev, with_dy=True)
+    ws = torch.empty(wkv.wkv_backward_workspace_size(B, T, C), device=dev, dtype=torch.uint8)
+    outs = dict(y=torch.empty_like(d["k"]), so=torch.empty((3, B, C), device=dev),
+                ck=torch.empty((wkv.checkpoint_count(T), 3, B, C), device=dev),
+                dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["k"]),
+                dw=torch.empty(C, device=dev), du=torch.empty(C, device=dev))
+
+    def work(stream):
+        wkv.wkv_forward_checkpointed(d["w"], d["u"], d["k"], d["v"], y=outs["y"],
+                                     state_out=outs["so"], checkpoints=outs["ck"], stream=stream,
+                                     plan=(wkv.WKV_KERNEL_SEGMENTED, 16, 16))
+        wkv.wkv_backward_checkpointed(d["w"], d["u"], d["k"], d["v"], d["dy"], outs["ck"],
+                                      dk=outs["dk"], dv=outs["dv"], dw=outs["dw"], du=outs["du"],
+                                      workspace=ws, stream=stream)
+
+    work(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in outs.items()}
+    g = _capture(lambda: work(side), side)
+    for rep in range(4):
+        for t in outs.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        work(torch.cuda.current_stream())       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in outs.items():
+            assert torch.equal(t, ref[n]), f"replay {rep}: {n} differs from the eager result"

@@ -404,6 +404,44 @@ def test_gate_limits_and_symmetry(oracle):
     np.testing.assert_allclose(oracle.gate(one, r) + oracle.gate(one, -r), one, rtol=1e-15)
 
 
+def test_gate_backward_is_the_derivative_of_the_gate(oracle):
+    """Central differences of sum(d * gate(y, r)) in y and in r.  Each output
+    depends on its own y and r only, so one perturbation of every element at
+    once gives every partial derivative."""
+    rng = np.random.default_rng(12)
+    n = 2000
+    y = rng.normal(0.0, 2.0, n)
+    r = rng.normal(0.0, 4.0, n)
+    d = rng.normal(0.0, 1.0, n)
+    g, dr = oracle.gate_backward(y, r, d)
+    h = 1e-5
+    num_y = d * (oracle.gate(y + h, r) - oracle.gate(y - h, r)) / (2 * h)
+    num_r = d * (oracle.gate(y, r + h) - oracle.gate(y, r - h)) / (2 * h)
+    np.testing.assert_allclose(g, num_y, rtol=1e-8, atol=1e-10)
+    np.testing.assert_allclose(dr, num_r, rtol=1e-6, atol=1e-10)
+
+
+def test_gate_backward_tails_and_zero(oracle):
+    y = np.array([2.0, -3.0, 0.5, 1.0])
+    d = np.array([1.0, 0.5, -2.0, 4.0])
+    # r = 0: g = d / 2, dr = d y / 4
+    g, dr = oracle.gate_backward(y, np.zeros(4), d)
+    np.testing.assert_array_equal(g, d / 2)
+    np.testing.assert_array_equal(dr, d * y / 4)
+    # saturated gate: open passes d through, closed passes nothing; dr vanishes
+    g, dr = oracle.gate_backward(y, np.full(4, 800.0), d)
+    np.testing.assert_array_equal(g, d)
+    assert np.all(dr == 0)
+    g, dr = oracle.gate_backward(y, np.full(4, -800.0), d)
+    assert np.all(g == 0) and np.all(dr == 0)
+    # dr is even in r (s (1 - s) is), g(r) + g(-r) = d
+    r = np.linspace(-20, 20, 4)
+    g1, dr1 = oracle.gate_backward(y, r, d)
+    g2, dr2 = oracle.gate_backward(y, -r, d)
+    np.testing.assert_allclose(dr1, dr2, rtol=1e-14)
+    np.testing.assert_allclose(g1 + g2, d, rtol=1e-14)
+
+
 def _shift_fixture():
     rows = {"x": [], "mu": [], "out": {}, "prev": None, "last": None}
     with open(os.path.join(GOLDEN, "token_shift_worked.txt")) as f:
