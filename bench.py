@@ -21,6 +21,7 @@ workloads with extra measurements, not the headline:
     stability_bwd_bf16        the backward with bf16 activations and gradients
     stability_fwd_ckpt        the forward that also writes 128-token checkpoints
     stability_bwd_ckpt[_bf16] the backward that starts from those checkpoints
+    stability_bwd_gated_ckpt  the same for the gated output (dr written too)
     gpt_gated, decode_gated   the same with the output gate sigmoid(r) fused in
     gpt_bf16, gpt_f16         the GPT forward with 16-bit activations (state fp32)
     token_shift               the token shift at the GPT shape (3 mixes)
@@ -459,13 +460,15 @@ def bench_decode(args, torch, wkv, synth, gated: bool = False):
 
 
 def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = False,
-                    io: str = "f32", ckpt: bool = False):
+                    io: str = "f32", ckpt: bool = False, gated: bool = False):
     """B=8 T=4096 C=2048 with wide exponents; backward: the gradients; carried:
     the backward of a chunk that starts from a carried state and hands one on
     (wkv_backward_state, with the state gradient in and out); ckpt: the forward
     that also writes its 128-token checkpoints, or the backward that starts
     from them (wkv_forward_checkpointed / wkv_backward_checkpointed; the
-    checkpoints are written by the forward before the timed region)."""
+    checkpoints are written by the forward before the timed region); gated: the
+    backward of the gated output sigmoid(r) * wkv from the checkpoints
+    (wkv_backward_gated, dr written as well)."""
     sh = synth.SHAPES[synth.STABILITY]
     B, T, C = sh["B"], sh["T"], sh["C"]
     dev = torch.device("cuda")
@@ -478,9 +481,13 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
                 st_[n] = st_[n].to(tdt)
     lane_tok = B * T * C
     nck = wkv.checkpoint_count(T)
+    if gated:
+        for i, st_ in enumerate(sets):
+            st_["r"] = synth.receptance(synth.STABILITY, i, (B, T, C), device=dev).to(st_["k"].dtype)
     if ckpt:
         for st_ in sets:
-            _, _, st_["ck"] = wkv.wkv_forward_checkpointed(st_["w"], st_["u"], st_["k"], st_["v"])
+            _, _, st_["ck"] = wkv.wkv_forward_checkpointed(st_["w"], st_["u"], st_["k"], st_["v"],
+                                                           r=st_.get("r"))
     if backward:
         ws = torch.empty(wkv.wkv_backward_workspace_size(B, T, C), device=dev, dtype=torch.uint8)
         outs = [tuple(torch.empty_like(s["k"]) for _ in range(2)) for s in sets]
@@ -498,9 +505,17 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
                                         device=dev)
             dsi = torch.empty((3, B, C), device=dev)
 
+        if gated:
+            drs = [torch.empty_like(s["k"]) for s in sets]
+
         def call(i):
             s = sets[i]
-            if ckpt:
+            if gated:
+                wkv.wkv_backward_gated(s["w"], s["u"], s["k"], s["v"], s["r"], s["dy"],
+                                       checkpoints=s["ck"], dk=outs[i][0], dv=outs[i][1],
+                                       dr=drs[i], dw=dwu[0], du=dwu[1], workspace=ws,
+                                       stream=stream)
+            elif ckpt:
                 wkv.wkv_backward_checkpointed(s["w"], s["u"], s["k"], s["v"], s["dy"], s["ck"],
                                               dk=outs[i][0], dv=outs[i][1], dw=dwu[0],
                                               du=dwu[1], workspace=ws, stream=stream)
@@ -522,18 +537,24 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
         # state_in, state_out's o-plane and the upstream gradient in, d_state_in out
         esz = 4 if io == "f32" else 2
         # (and the checkpoints in: 12 bytes per lane each)
-        algo = (5 * esz * lane_tok + 16 * C + (40 * B * C if carried else 0) +
-                (12 * B * C * nck if ckpt else 0))
+        # (and the checkpoints in: 12 bytes per lane each; gated: r in, dr out)
+        algo = ((7 if gated else 5) * esz * lane_tok + 16 * C +
+                (40 * B * C if carried else 0) + (12 * B * C * nck if ckpt else 0))
         name = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32"
         # (the whole-tile variant when T is a multiple of its 128-token tile)
-        kname = (f"bwd_seg_kernel<16, 8, {'true' if T % 128 == 0 else 'false'}, "
-                 f"{'true' if ckpt else 'false'}, {IO_NAMES[io]}>")
+        # (the gated kernel always runs the general variant)
+        full = T % 128 == 0 and not gated
+        kname = (f"bwd_seg_kernel<16, 8, {'true' if full else 'false'}, "
+                 f"{'true' if ckpt else 'false'}, {'true' if gated else 'false'}, "
+                 f"{IO_NAMES[io]}>")
         if io != "f32":
             name = name.replace("fp32", f"{io} activations, fp32 state")
         if carried:
             name = name.replace("backward", "backward with carried states")
         if ckpt:
             name = name.replace("backward", "backward from the forward's checkpoints")
+        if gated:
+            name = name.replace("backward", "gated backward (dr too)")
     else:
         ys = [torch.empty_like(s["k"]) for s in sets]
 
@@ -560,6 +581,8 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
     ms = tm.stop_ms()
     per = ms / n
     wl = ("stability_bwd_state" if carried else "stability_bwd") if backward else "stability_fwd"
+    if gated:
+        wl += "_gated"
     if ckpt:
         wl += "_ckpt"
     if io != "f32":
@@ -590,10 +613,16 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
                 oracle.backward_state(a[0], a[1], kp, vp, gp, s_in, s_out,
                                       st_["g"][:, i:i + 1].double().cpu().numpy())
                 return cut * C, time.perf_counter() - t0
+            dyy = st_["dy"][i:i + 1].double().cpu().numpy() if backward else None
+            rr = st_["r"][i:i + 1].double().cpu().numpy() if gated else None
             t0 = time.perf_counter()
-            if backward:
-                oracle.backward_scan(a[0], a[1], kk, vv, st_["dy"][i:i + 1].double().cpu().numpy(),
-                                     nthreads=cores)
+            if backward and gated:
+                # the oracle's gated backward: wkv, the gate's chain rule, the reverse scan
+                yy, _ = oracle.forward_scan(a[0], a[1], kk, vv, nthreads=cores)
+                gg, _ = oracle.gate_backward(yy, rr, dyy)
+                oracle.backward_scan(a[0], a[1], kk, vv, gg, nthreads=cores)
+            elif backward:
+                oracle.backward_scan(a[0], a[1], kk, vv, dyy, nthreads=cores)
             else:
                 oracle.forward_scan(a[0], a[1], kk, vv, nthreads=cores)
             return T * C, time.perf_counter() - t0
@@ -601,8 +630,8 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
         done, secs, calls = timed_oracle(seq, args.cpu_seconds)
         cpu = {"value": done / secs, "unit": "tok·ch/s", "cores": cores, "kind": "oracle",
                "sample": f"{calls} of the 8 sequences (T=4096 C=2048 each), float64 O(T) "
-                         f"{'reverse scan' if backward else 'recurrence'} on {cores} threads "
-                         f"({secs:.1f} s)"}
+                         f"{'recurrence, gate chain rule and reverse scan' if gated else ('reverse scan' if backward else 'recurrence')} "
+                         f"on {cores} threads ({secs:.1f} s)"}
         if carried:
             cpu["cores"] = 1
             cpu["sample"] = (f"the first 256 tokens of {calls} of the 8 sequences (C=2048), "
@@ -722,7 +751,8 @@ def main():
                     choices=["gpt", "gpt_gated", "gpt_bf16", "gpt_f16", "stream", "decode",
                              "decode_gated", "stability_fwd", "stability_bwd",
                              "stability_bwd_state", "stability_bwd_bf16", "stability_fwd_ckpt",
-                             "stability_bwd_ckpt", "stability_bwd_ckpt_bf16", "token_shift",
+                             "stability_bwd_ckpt", "stability_bwd_ckpt_bf16",
+                             "stability_bwd_gated_ckpt", "token_shift",
                              "copy"])
     ap.add_argument("--plan", type=int, nargs="+", default=None,
                     metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
@@ -757,6 +787,8 @@ def main():
           "stability_bwd_ckpt": lambda a, t, w, s: bench_stability(a, t, w, s, True, ckpt=True),
           "stability_bwd_ckpt_bf16": lambda a, t, w, s: bench_stability(a, t, w, s, True, False,
                                                                         "bf16", ckpt=True),
+          "stability_bwd_gated_ckpt": lambda a, t, w, s: bench_stability(a, t, w, s, True,
+                                                                         ckpt=True, gated=True),
           }[args.workload]
     torch.cuda.synchronize()
     out = fn(args, torch, wkv, synth)

@@ -402,6 +402,34 @@ WKV_API wkv_status wkv_backward_checkpointed(int64_t B, int64_t T, int64_t C, wk
                                              float *d_state_in, void *workspace,
                                              size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Backward of the gated forward (wkv_forward_gated, or a typed or checkpointed
+ * forward given r): dy is the gradient of the gated output
+ * o = sigmoid(r) * wkv (RWKV architecture deep dive, "RWKV architecture
+ * overview", block figure; the pages state no backward).  The recurrence
+ * receives g = dy * sigmoid(r), so dk, dv, dw, du and d_state_in are those of
+ * wkv_backward_typed for that g, and
+ *   dr = dy * wkv * sigmoid(r) * (1 - sigmoid(r))
+ * is written beside them (wkv is recomputed, not read).
+ *
+ *   r            [B][T][C] of `dtype`: the forward's receptance; required when
+ *                B*T*C > 0
+ *   dr           [B][T][C] of `dtype`: output, fully overwritten, rounded once
+ *                to `dtype`; required when B*T*C > 0; overlaps nothing
+ *   checkpoints  NULL: the backward makes its own first pass over k and v;
+ *                else as for wkv_backward_checkpointed
+ * Every other argument, the workspace size and the errors are those of
+ * wkv_backward_typed.
+ */
+WKV_API wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                      const float *w, const float *u, const void *k,
+                                      const void *v, const void *r, const void *dy,
+                                      const float *state_in, const float *checkpoints,
+                                      const float *state_out, const float *d_state_out,
+                                      void *dk, void *dv, void *dr, float *dw, float *du,
+                                      float *d_state_in, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* Largest number of mixes wkv_token_shift takes in one call. */
 #define WKV_TOKEN_SHIFT_MAX_MIXES 8
 

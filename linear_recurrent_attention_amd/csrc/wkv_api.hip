@@ -311,16 +311,18 @@ wkv_status step_impl(int64_t L, int64_t B, int64_t C, const float *w, const floa
     return from_hip(wkv::launch_step(a, stream));
 }
 
-// wkv_backward, wkv_backward_state, wkv_backward_typed and
-// wkv_backward_checkpointed (the first with no states); io is the wkv_dtype of
-// k, v, dy, dk and dv; from_ck: the forward states come from the checkpoints
-// cks.
+// wkv_backward, wkv_backward_state, wkv_backward_typed,
+// wkv_backward_checkpointed and wkv_backward_gated (the first with no states);
+// io is the wkv_dtype of k, v, dy, dk and dv (and r, dr); from_ck: the forward
+// states come from the checkpoints cks; gated: dy is the gradient of
+// sigmoid(r) * wkv, and dr receives the gradient in r.
 wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w, const float *u,
                          const void *k, const void *v, const void *dy, const float *s_in,
                          const float *s_out, const float *ds_out, void *dk, void *dv,
                          float *dw, float *du, float *ds_in, void *workspace,
                          size_t workspace_bytes, hipStream_t stream, bool from_ck = false,
-                         const float *cks = nullptr) {
+                         const float *cks = nullptr, bool gated = false,
+                         const void *r = nullptr, void *dr = nullptr) {
     const int64_t esize = elem_bytes(io);
     if (esize == 0) return WKV_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
@@ -331,6 +333,7 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w
     if (C == 0) return WKV_OK;
     if (!dw || !du) return WKV_ERR_NULL;
     if (seq > 0 && (!w || !u || !k || !v || !dy || !dk || !dv)) return WKV_ERR_NULL;
+    if (gated && seq > 0 && (!r || !dr)) return WKV_ERR_NULL;
     if (ds_out && !s_out && B > 0) return WKV_ERR_NULL;
     const int64_t ckb = from_ck ? bytes_of(3 * ckpt_count(T), B, C) : 0;
     if (ckb < 0) return WKV_ERR_OVERFLOW;
@@ -344,14 +347,16 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w
     const Range rdk = rng(dk, seq), rdv = rng(dv, seq), rdw = rng(dw, ch), rdu = rng(du, ch);
     const Range rdsi = rng(ds_in, st);
     const Range rws = rng(workspace, (int64_t)need);
-    const Range outs[] = {rdk, rdv, rdw, rdu, rws, rdsi};
-    for (int i = 0; i < 6; ++i) {
-        for (Range r : {rw, ru, rk, rv, rg, rsi, rso, rck})
-            if (overlap(outs[i], r)) return WKV_ERR_ALIAS;
+    const Range rr = rng(gated ? r : nullptr, seq), rdr = rng(gated ? dr : nullptr, seq);
+    const Range outs[] = {rdk, rdv, rdw, rdu, rws, rdsi, rdr};
+    constexpr int kOuts = 7;
+    for (int i = 0; i < kOuts; ++i) {
+        for (Range q : {rw, ru, rk, rv, rg, rsi, rso, rck, rr})
+            if (overlap(outs[i], q)) return WKV_ERR_ALIAS;
         // d_state_in may replace d_state_out exactly (read before it is written)
         if (overlap(outs[i], rdso) && !(i == 5 && (const float *)ds_in == ds_out))
             return WKV_ERR_ALIAS;
-        for (int j = i + 1; j < 6; ++j)
+        for (int j = i + 1; j < kOuts; ++j)
             if (overlap(outs[i], outs[j])) return WKV_ERR_ALIAS;
     }
     BwdArgs a{B, T, C, w, u, k, v, dy, dk, dv, dw, du, workspace};
@@ -362,6 +367,8 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w
     a.ds_in = ds_in;
     a.from_ck = from_ck;
     a.ck = ckb > 0 ? cks : nullptr;
+    a.r = gated ? r : nullptr;
+    a.dr = gated ? dr : nullptr;
     return from_hip(wkv::launch_backward(a, stream));
 }
 
@@ -528,6 +535,19 @@ WKV_API wkv_status wkv_backward_checkpointed(int64_t B, int64_t T, int64_t C, wk
     return backward_impl(B, T, C, (int)dtype, w, u, k, v, dy, state_in, state_out, d_state_out,
                          dk, dv, dw, du, d_state_in, workspace, workspace_bytes, stream, true,
                          checkpoints);
+}
+
+WKV_API wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype dtype,
+                                      const float *w, const float *u, const void *k,
+                                      const void *v, const void *r, const void *dy,
+                                      const float *state_in, const float *checkpoints,
+                                      const float *state_out, const float *d_state_out,
+                                      void *dk, void *dv, void *dr, float *dw, float *du,
+                                      float *d_state_in, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    return backward_impl(B, T, C, (int)dtype, w, u, k, v, dy, state_in, state_out, d_state_out,
+                         dk, dv, dw, du, d_state_in, workspace, workspace_bytes, stream,
+                         checkpoints != nullptr, checkpoints, true, r, dr);
 }
 
 }  // extern "C"

@@ -215,13 +215,16 @@ __device__ __forceinline__ void fwd_token(Lane &L, float K, float v, const Chan 
 // needs a bounds test.  CK: the forward's checkpoints `cks` hold the state at
 // the start of every tile but the first; there is no phase 1, and each tile's
 // segment starting states are rebuilt in phase 2 by the same scan, from the
-// tile's checkpoint (or state_in).
-template <int NW, int LS, bool SAFE, bool FULL, bool CK, class IO>
+// tile's checkpoint (or state_in).  GATE: the forward's output was
+// sigmoid(r) * wkv and dy its gradient; the recurrence's upstream gradient is
+// g = dy sigmoid(r), and dr = g wkv (1 - sigmoid(r)) is stored as well.
+template <int NW, int LS, bool SAFE, bool FULL, bool CK, bool GATE, class IO>
 __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_t bb, int64_t c,
                                          bool active, const Chan &ch,
                                          const typename IO::T *kseq, const typename IO::T *vseq,
                                          const typename IO::T *gseq, typename IO::T *dkseq,
-                                         typename IO::T *dvseq, uint32_t voff,
+                                         typename IO::T *dvseq, const typename IO::T *rseq,
+                                         typename IO::T *drseq, uint32_t voff,
                                          float *__restrict__ ck,
                                          double *__restrict__ part, const float *s_in,
                                          const float *s_out, const float *ds_out, float *ds_in,
@@ -330,6 +333,9 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             load_seg<LS>(Vn, rows(vseq, t0 - TT), t0 - TT, T);
             load_seg<LS>(Gn, rows(gseq, t0 - TT), t0 - TT, T);
         }
+        // the receptance of this tile (used once the forward is recomputed)
+        float Rc[GATE ? LS : 1];
+        if constexpr (GATE) load_seg<LS>(Rc, rows(rseq, t0), t0, T);
         // forward recompute of y, lambda, p_ii from the segment's starting state
         float Y[LS], LAM[LS], PII[LS];
         {
@@ -376,6 +382,19 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 PII[j] = 0.0f;
                 if (FULL || t0 + j < T)
                     fwd_token<SAFE>(L, Kc[j] * kLog2e, Vc[j], ch, Y[j], LAM[j], PII[j]);
+            }
+        }
+        if constexpr (GATE) {
+            // g = dy sigmoid(r) replaces dy, and dr = g wkv (1 - sigmoid(r)) is
+            // stored now that wkv is known, so that r is dead before the scans
+            const TileRowsT<IO> drr = rows(drseq, t0);
+#pragma unroll
+            for (int j = 0; j < LS; ++j) {
+                if (FULL || t0 + j < T) {
+                    const float sg = gate_of(Rc[j]);
+                    Gc[j] *= sg;
+                    if (active) drr.st(j, Gc[j] * Y[j] * (1.0f - sg));
+                }
             }
         }
         // the wave holding token T-1 (last tile) starts from the upstream seed
@@ -482,8 +501,9 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
 }
 
 // FULL: T is a whole number of tiles (chosen on the host).  CK: start every
-// tile from the forward's checkpoints `cks` instead of a first pass.
-template <int NW, int LS, bool FULL, bool CK, class IO>
+// tile from the forward's checkpoints `cks` instead of a first pass.  GATE:
+// the gradient of the gated output, with r read and dr written.
+template <int NW, int LS, bool FULL, bool CK, bool GATE, class IO>
 __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, int64_t C,
                                                           const float *__restrict__ w,
                                                           const float *__restrict__ u,
@@ -496,7 +516,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, 
                                                           double *__restrict__ part,
                                                           const float *s_in, const float *s_out,
                                                           const float *ds_out, float *ds_in,
-                                                          const float *cks) {
+                                                          const float *cks,
+                                                          const typename IO::T *__restrict__ r,
+                                                          typename IO::T *__restrict__ dr) {
     __shared__ BwdShared<NW> sh;
     constexpr int TT = NW * LS;
     const int64_t ngroups = (C + 63) / 64;
@@ -513,13 +535,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_seg_kernel(int64_t B, int64_t T, 
     const uint32_t voff = active ? (uint32_t)((threadIdx.x & 63) * IO::kBytes) : 0u;
     float *ck = ckpt + (int64_t)blockIdx.x * ntiles * NW * 4 * 64;
     if (fast)
-        bwd_body<NW, LS, false, FULL, CK, IO>(B, T, C, bb, c, active, ch, k + base, v + base,
-                                              dy + base, dk + base, dv + base, voff, ck, part,
-                                              s_in, s_out, ds_out, ds_in, cks, sh);
+        bwd_body<NW, LS, false, FULL, CK, GATE, IO>(
+            B, T, C, bb, c, active, ch, k + base, v + base, dy + base, dk + base, dv + base,
+            GATE ? r + base : nullptr, GATE ? dr + base : nullptr, voff, ck, part, s_in, s_out,
+            ds_out, ds_in, cks, sh);
     else
-        bwd_body<NW, LS, true, FULL, CK, IO>(B, T, C, bb, c, active, ch, k + base, v + base,
-                                             dy + base, dk + base, dv + base, voff, ck, part,
-                                             s_in, s_out, ds_out, ds_in, cks, sh);
+        bwd_body<NW, LS, true, FULL, CK, GATE, IO>(
+            B, T, C, bb, c, active, ch, k + base, v + base, dy + base, dk + base, dv + base,
+            GATE ? r + base : nullptr, GATE ? dr + base : nullptr, voff, ck, part, s_in, s_out,
+            ds_out, ds_in, cks, sh);
 }
 
 // dw[c], du[c] = sums over the batch of the per-lane parts, in order b = 0..B-1.
@@ -569,26 +593,43 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(int64_t n, const fl
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-template <bool FULL, bool CK, class IO>
+template <bool FULL, bool CK, bool GATE, class IO>
 void launch_bwd_seg_k(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
     using T = typename IO::T;
-    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS, FULL, CK, IO>), dim3((unsigned)grid),
-                       dim3(kBwdNW * 64), 0, st, a.B, a.T, a.C, a.w, a.u, (const T *)a.k,
-                       (const T *)a.v, (const T *)a.dy, (T *)a.dk, (T *)a.dv, ck, part, a.s_in,
-                       a.s_out, a.ds_out, a.ds_in, a.ck);
+    hipLaunchKernelGGL((bwd_seg_kernel<kBwdNW, kBwdLS, FULL, CK, GATE, IO>),
+                       dim3((unsigned)grid), dim3(kBwdNW * 64), 0, st, a.B, a.T, a.C, a.w, a.u,
+                       (const T *)a.k, (const T *)a.v, (const T *)a.dy, (T *)a.dk, (T *)a.dv, ck,
+                       part, a.s_in, a.s_out, a.ds_out, a.ds_in, a.ck, (const T *)a.r,
+                       (T *)a.dr);
 }
 
-template <bool CK, class IO>
-void launch_bwd_seg_ck(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
-    if (a.T % (kBwdNW * kBwdLS) == 0)
-        launch_bwd_seg_k<true, CK, IO>(a, grid, ck, part, st);
+// The whole-tile variant where T allows it, except with the gate: its extra
+// row array makes the whole-tile code spill some 40 registers, against none
+// for the general code.
+template <bool CK, bool GATE, class IO>
+void launch_bwd_seg_full(const BwdArgs &a, int64_t grid, float *ck, double *part,
+                         hipStream_t st) {
+    if constexpr (!GATE) {
+        if (a.T % (kBwdNW * kBwdLS) == 0) {
+            launch_bwd_seg_k<true, CK, GATE, IO>(a, grid, ck, part, st);
+            return;
+        }
+    }
+    launch_bwd_seg_k<false, CK, GATE, IO>(a, grid, ck, part, st);
+}
+
+template <bool GATE, class IO>
+void launch_bwd_seg_ck(const BwdArgs &a, int64_t grid, float *ck, double *part,
+                       hipStream_t st) {
+    if (a.from_ck)
+        launch_bwd_seg_full<true, GATE, IO>(a, grid, ck, part, st);
     else
-        launch_bwd_seg_k<false, CK, IO>(a, grid, ck, part, st);
+        launch_bwd_seg_full<false, GATE, IO>(a, grid, ck, part, st);
 }
 
 template <class IO>
 void launch_bwd_seg(const BwdArgs &a, int64_t grid, float *ck, double *part, hipStream_t st) {
-    if (a.from_ck)
+    if (a.r)
         launch_bwd_seg_ck<true, IO>(a, grid, ck, part, st);
     else
         launch_bwd_seg_ck<false, IO>(a, grid, ck, part, st);

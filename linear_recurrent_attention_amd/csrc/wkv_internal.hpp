@@ -67,6 +67,10 @@ struct BwdArgs {
     // has none) instead of by a first pass over k and v
     const float *ck = nullptr;
     bool from_ck = false;
+    // r: NULL, or the receptance of a gated forward (layout of k): dy is then
+    // the gradient of sigmoid(r) * wkv, and dr receives its gradient in r
+    const void *r = nullptr;
+    void *dr = nullptr;
 };
 
 // forward (wkv_forward.hip)

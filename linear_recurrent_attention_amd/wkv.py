@@ -43,7 +43,7 @@ EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backw
             "wkv_status_string", "wkv_forward_ex", "wkv_forward_plan_auto",
             "wkv_forward_gated", "wkv_step_gated", "wkv_token_shift", "wkv_forward_typed",
             "wkv_step_typed", "wkv_backward_state", "wkv_backward_typed",
-            "wkv_forward_checkpointed", "wkv_backward_checkpointed")
+            "wkv_forward_checkpointed", "wkv_backward_checkpointed", "wkv_backward_gated")
 
 # wkv_dtype values
 WKV_DTYPE_F32 = 0
@@ -120,6 +120,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_backward_checkpointed.argtypes = ([i64, i64, i64, ctypes.c_int] + [vp] * 14 +
                                               [vp, sz, vp])
     lib.wkv_backward_checkpointed.restype = ctypes.c_int
+    lib.wkv_backward_gated.argtypes = [i64, i64, i64, ctypes.c_int] + [vp] * 16 + [vp, sz, vp]
+    lib.wkv_backward_gated.restype = ctypes.c_int
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -470,3 +472,36 @@ def wkv_backward_checkpointed(w, u, k, v, dy, checkpoints, state_in=None, state_
         _stream(stream))
     _check("wkv_backward_checkpointed", st)
     return dk, dv, dw, du, d_state_in
+
+
+def wkv_backward_gated(w, u, k, v, r, dy, checkpoints=None, state_in=None, state_out=None,
+                       d_state_out=None, dk=None, dv=None, dr=None, dw=None, du=None,
+                       d_state_in=None, workspace=None, stream=None):
+    """Backward of the gated forward: dy is the gradient of sigmoid(r) * wkv.
+    Returns (dk, dv, dr, dw, du, d_state_in); checkpoints None makes the
+    backward run its own first pass."""
+    if k.dtype not in _DTYPES:
+        raise TypeError(f"unsupported element type {k.dtype}")
+    dt = k.dtype
+    B, T, C = _bundle_shape(k, None)
+    dev = k.device
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    dr = torch.empty_like(k) if dr is None else dr
+    dw = torch.empty(C, device=dev, dtype=torch.float32) if dw is None else dw
+    du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
+    if d_state_in is True:
+        d_state_in = torch.empty((3, B, C), device=dev, dtype=torch.float32)
+    need = wkv_backward_workspace_size(B, T, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
+    st = load_library().wkv_backward_gated(
+        B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt), _ptr(v, dt), _ptr(r, dt),
+        _ptr(dy, dt), _ptr(state_in), _ptr(checkpoints), _ptr(state_out), _ptr(d_state_out),
+        _ptr(dk, dt), _ptr(dv, dt), _ptr(dr, dt), _ptr(dw), _ptr(du), _ptr(d_state_in), ws_ptr,
+        workspace.numel(), _stream(stream))
+    _check("wkv_backward_gated", st)
+    return dk, dv, dr, dw, du, d_state_in

@@ -217,6 +217,35 @@ def test_checkpointed_calls_reject_invalid_arguments(lib):
              None) == W.WKV_ERR_WORKSPACE
 
 
+def test_gated_backward_rejects_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    w, u, k, v = (vp(P + i * 0x10000000) for i in range(4))
+    dy, r = vp(P + 4 * 0x10000000), vp(P + 5 * 0x10000000)
+    dk, dv, dw, du = (vp(P + (8 + i) * 0x10000000) for i in range(4))
+    dr, ws = vp(P + 12 * 0x10000000), vp(P + 16 * 0x10000000)
+    n = lib.wkv_backward_workspace_size(2, 300, 16)
+    g = lib.wkv_backward_gated
+    ok = [w, u, k, v, r, dy, None, None, None, None, dk, dv, dr, dw, du, None, ws, n, None]
+
+    def call(dtype=W.WKV_DTYPE_F32, **over):
+        args = list(ok)
+        names = ["w", "u", "k", "v", "r", "dy", "si", "ck", "so", "dso", "dk", "dv", "dr", "dw",
+                 "du", "dsi", "ws", "n", "stream"]
+        for key, val in over.items():
+            args[names.index(key)] = val
+        return g(2, 300, 16, dtype, *args)
+
+    assert call(r=None) == W.WKV_ERR_NULL
+    assert call(dr=None) == W.WKV_ERR_NULL
+    assert call(dtype=7) == W.WKV_ERR_UNSUPPORTED
+    assert call(dr=vp(P + 5 * 0x10000000 + 64)) == W.WKV_ERR_ALIAS      # dr over r
+    assert call(dr=vp(P + 8 * 0x10000000 + 64)) == W.WKV_ERR_ALIAS      # dr over dk
+    assert call(dk=vp(P + 5 * 0x10000000 + 4)) == W.WKV_ERR_ALIAS       # dk over r
+    assert call(n=n - 1) == W.WKV_ERR_WORKSPACE
+    assert call(ck=vp(P + 12 * 0x10000000 + 256)) == W.WKV_ERR_ALIAS    # checkpoints under dr
+
+
 def test_forward_ex_rejects_unknown_plans(lib):
     from linear_recurrent_attention_amd import wkv as W
     vp = ctypes.c_void_p
