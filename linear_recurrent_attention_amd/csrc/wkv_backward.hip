@@ -246,9 +246,12 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         if (s_in && active)
             carry = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
                             o_in(s_in[(2 * B + bb) * C + c]));
+        // keys in log2 units, scaled where each prefetched tile is handed over
         float Kc[LS], Vc[LS];
         load_seg<LS>(Kc, rows(kseq, (int64_t)s * LS), (int64_t)s * LS, T);
         load_seg<LS>(Vc, rows(vseq, (int64_t)s * LS), (int64_t)s * LS, T);
+#pragma unroll
+        for (int j = 0; j < LS; ++j) Kc[j] *= kLog2e;
         for (int64_t tile = 0; tile < ntiles; ++tile) {
             const int64_t t0 = tile * TT + (int64_t)s * LS;
             float Kn[LS], Vn[LS];
@@ -259,7 +262,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             Lane S = lane_empty();
 #pragma unroll
             for (int j = 0; j < LS; ++j)
-                if (FULL || t0 + j < T) absorb(S, Kc[j] * kLog2e, Vc[j], ch);
+                if (FULL || t0 + j < T) absorb(S, Kc[j], Vc[j], ch);
             int buf = 0;
 #pragma unroll
             for (int d = 1; d < NW; d <<= 1) {
@@ -284,7 +287,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             q[192] = R.n;
 #pragma unroll
             for (int j = 0; j < LS; ++j) {
-                Kc[j] = Kn[j];
+                Kc[j] = Kn[j] * kLog2e;
                 Vc[j] = Vn[j];
             }
         }
@@ -318,12 +321,16 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
     auto seed_of = [&]() {
         return Rev{sh.seed[0][lane], sh.seed[1][lane], 0.0f, 0.0f, sh.seed[2][lane], 0.0f};
     };
+    // Kc holds the keys in log2 units (k log2 e): the scaling takes the place
+    // of the register copy that hands each prefetched tile over
     float Kc[LS], Vc[LS], Gc[LS];
     {
         const int64_t t0 = (ntiles - 1) * TT + (int64_t)s * LS;
         load_seg<LS>(Kc, rows(kseq, t0), t0, T);
         load_seg<LS>(Vc, rows(vseq, t0), t0, T);
         load_seg<LS>(Gc, rows(gseq, t0), t0, T);
+#pragma unroll
+        for (int j = 0; j < LS; ++j) Kc[j] *= kLog2e;
     }
     for (int64_t tile = ntiles - 1; tile >= 0; --tile) {
         const int64_t t0 = tile * TT + (int64_t)s * LS;
@@ -354,7 +361,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 Lane S = lane_empty();
 #pragma unroll
                 for (int j = 0; j < LS; ++j)
-                    if (FULL || t0 + j < T) absorb(S, Kc[j] * kLog2e, Vc[j], ch);
+                    if (FULL || t0 + j < T) absorb(S, Kc[j], Vc[j], ch);
                 int fb = 0;
 #pragma unroll
                 for (int d = 1; d < NW; d <<= 1) {
@@ -381,7 +388,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 LAM[j] = 0.0f;
                 PII[j] = 0.0f;
                 if (FULL || t0 + j < T)
-                    fwd_token<SAFE>(L, Kc[j] * kLog2e, Vc[j], ch, Y[j], LAM[j], PII[j]);
+                    fwd_token<SAFE>(L, Kc[j], Vc[j], ch, Y[j], LAM[j], PII[j]);
             }
         }
         if constexpr (GATE) {
@@ -431,7 +438,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
 #pragma unroll
         for (int j = LS - 1; j >= 0; --j) {
             if (FULL || t0 + j < T) {
-                const float K = Kc[j] * kLog2e;
+                const float K = Kc[j];
                 const float v = Vc[j], g = Gc[j], y = Y[j];
                 const float ek = ex2(fmaf(-suf.m, ch.W, K + suf.r0));
                 const float own = PII[j] * g;
@@ -459,7 +466,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         }
 #pragma unroll
         for (int j = 0; j < LS; ++j) {
-            Kc[j] = Kn[j];
+            Kc[j] = Kn[j] * kLog2e;
             Vc[j] = Vn[j];
             Gc[j] = Gn[j];
         }
