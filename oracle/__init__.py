@@ -51,9 +51,11 @@ def _load():
         lib.wkvo_gate_backward.argtypes = [i64, D, D, D, D, D]
         lib.wkvo_backward_state.argtypes = [i64, i64, i64] + [D] * 13
         lib.wkvo_token_shift.argtypes = [i64, i64, i64, i64, D, D, D, D, D]
+        lib.wkvo_token_shift_backward.argtypes = [i64, i64, i64, i64] + [D] * 8
         for f in (lib.wkvo_forward_brute, lib.wkvo_forward_scan, lib.wkvo_backward_brute,
                   lib.wkvo_backward_scan, lib.wkvo_gate, lib.wkvo_token_shift,
-                  lib.wkvo_backward_state, lib.wkvo_gate_backward):
+                  lib.wkvo_backward_state, lib.wkvo_gate_backward,
+                  lib.wkvo_token_shift_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -211,6 +213,33 @@ def token_shift(mu, x, x_prev=None):
     if rc:
         raise RuntimeError(f"wkvo_token_shift failed ({rc})")
     return out, xpo
+
+
+def token_shift_backward(mu, x, x_prev, d_out, d_x_prev_out=None):
+    """Backward of ``token_shift``: upstream gradients d_out [M][B][T][C] of the
+    mixes and d_x_prev_out [B][C] of the carried token (None: zero).  Returns
+    (dx [B][T][C], d_x_prev [B][C], dmu [M][C])."""
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("x must be [B][T][C]")
+    B, T, C = x.shape
+    mu = _f64(mu)
+    if mu.ndim != 2 or mu.shape[1] != C:
+        raise ValueError("mu must be [M][C]")
+    M = mu.shape[0]
+    xp = None if x_prev is None else _f64(x_prev)
+    d_out = _f64(d_out)
+    if d_out.shape != (M, B, T, C):
+        raise ValueError("d_out must be [M][B][T][C]")
+    dxpo = None if d_x_prev_out is None else _f64(d_x_prev_out)
+    dx = np.empty((B, T, C))
+    dxp = np.empty((B, C))
+    dmu = np.empty((M, C))
+    rc = _load().wkvo_token_shift_backward(B, T, C, M, _ptr(mu), _ptr(x), _ptr(xp), _ptr(d_out),
+                                           _ptr(dxpo), _ptr(dx), _ptr(dxp), _ptr(dmu))
+    if rc:
+        raise RuntimeError(f"wkvo_token_shift_backward failed ({rc})")
+    return dx, dxp, dmu
 
 
 def canonical_state(state):

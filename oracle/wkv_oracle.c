@@ -51,6 +51,10 @@
  *                          y and in r, saturated tails)
  *   wkvo_token_shift       pinned (hand-computed fixture, mu = 0 and mu = 1
  *                          limits, chunking identity)
+ *   wkvo_token_shift_backward  pinned (central finite differences of
+ *                          wkvo_token_shift, per element on a small case and
+ *                          along random directions on a larger one; mu = 0
+ *                          and mu = 1 limits)
  */
 #include <math.h>
 #include <pthread.h>
@@ -490,6 +494,59 @@ int wkvo_gate_backward(int64_t n, const double *y, const double *r, const double
  * for a fresh sequence (x_prev == NULL).  x_prev_out[b][c] receives the last
  * token of this call, x[b][T-1][c], or x_prev (0 when fresh) when T == 0.
  */
+/*
+ * Backward of the token shift [Shift] with its carried token [States].  For
+ * the upstream gradients d_out [M][B][T][C] of the M mixes and d_xpo [B][C] of
+ * the carried token handed on (NULL: none), the chain rule on wkvo_token_shift
+ * gives, token t feeding mix t with weight mu and mix t + 1 with 1 - mu:
+ *   dx[b][t][c]   = sum_m mu_m[c] d_out[m][b][t][c]
+ *                 + sum_m (1 - mu_m[c]) d_out[m][b][t+1][c]     (t + 1 < T)
+ *                 + d_xpo[b][c]                                (t = T - 1)
+ *   dx_prev[b][c] = sum_m (1 - mu_m[c]) d_out[m][b][0][c]       (T > 0)
+ *                 = d_xpo[b][c]                                (T = 0)
+ *   dmu[m][c]     = sum_{b,t} d_out[m][b][t][c] (x[b][t][c] - x[b][t-1][c])
+ * with x[b][-1] = x_prev (zeros when NULL).  The pages state no backward.
+ * dx_prev may be NULL (not wanted).
+ */
+int wkvo_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M, const double *mu,
+                              const double *x, const double *x_prev, const double *d_out,
+                              const double *d_xpo, double *dx, double *dx_prev, double *dmu) {
+    if (B < 0 || T < 0 || C < 0 || M < 0) return 1;
+    if (B * T * C > 0 && (!x || !dx || (M > 0 && (!mu || !d_out)))) return 1;
+    if (M * C > 0 && !dmu) return 1;
+    const int64_t plane = B * T * C;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < C; ++c) dmu[m * C + c] = 0.0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t c = 0; c < C; ++c) {
+                double g = (t == T - 1 && d_xpo) ? d_xpo[b * C + c] : 0.0;
+                const double prev =
+                    t > 0 ? x[IDX(b, t - 1, c)] : (x_prev ? x_prev[b * C + c] : 0.0);
+                for (int64_t m = 0; m < M; ++m) {
+                    const double mu_ = mu[m * C + c];
+                    const double d = d_out[m * plane + IDX(b, t, c)];
+                    g += mu_ * d;
+                    if (t + 1 < T) g += (1.0 - mu_) * d_out[m * plane + IDX(b, t + 1, c)];
+                    dmu[m * C + c] += d * (x[IDX(b, t, c)] - prev);
+                }
+                dx[IDX(b, t, c)] = g;
+            }
+    if (dx_prev)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t c = 0; c < C; ++c) {
+                double g = 0.0;
+                if (T > 0) {
+                    for (int64_t m = 0; m < M; ++m)
+                        g += (1.0 - mu[m * C + c]) * d_out[m * plane + IDX(b, 0, c)];
+                } else if (d_xpo) {
+                    g = d_xpo[b * C + c];
+                }
+                dx_prev[b * C + c] = g;
+            }
+    return 0;
+}
+
 int wkvo_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const double *mu,
                      const double *x, const double *x_prev, double *out,
                      double *x_prev_out) {

@@ -442,6 +442,79 @@ def test_gate_backward_tails_and_zero(oracle):
     np.testing.assert_allclose(g1 + g2, d, rtol=1e-14)
 
 
+def _shift_loss(oracle, mu, x, xp, d_out, d_xpo):
+    out, xpo = oracle.token_shift(mu, x, xp)
+    return float(np.sum(d_out * out) + np.sum(d_xpo * xpo))
+
+
+def test_token_shift_backward_per_element_differences(oracle):
+    """Every partial derivative of sum(d_out * out) + sum(d_xpo * x_prev_out),
+    by central differences of the oracle's own token shift (the loss is
+    bilinear in mu and x, so the differences are exact up to rounding)."""
+    rng = np.random.default_rng(21)
+    B, T, C, M = 2, 4, 3, 2
+    mu, x, xp = rng.uniform(0, 1, (M, C)), rng.normal(size=(B, T, C)), rng.normal(size=(B, C))
+    d_out, d_xpo = rng.normal(size=(M, B, T, C)), rng.normal(size=(B, C))
+    dx, dxp, dmu = oracle.token_shift_backward(mu, x, xp, d_out, d_xpo)
+    h = 1e-6
+    for arr, got in ((x, dx), (xp, dxp), (mu, dmu)):
+        num = np.empty_like(arr)
+        for i in np.ndindex(arr.shape):
+            keep = arr[i]
+            arr[i] = keep + h
+            lp = _shift_loss(oracle, mu, x, xp, d_out, d_xpo)
+            arr[i] = keep - h
+            lm = _shift_loss(oracle, mu, x, xp, d_out, d_xpo)
+            arr[i] = keep
+            num[i] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(got, num, rtol=1e-7, atol=1e-8)
+
+
+def test_token_shift_backward_directional_differences(oracle):
+    """Along random directions on a larger case, with and without a carried
+    token (x_prev None is zeros and receives no gradient that matters)."""
+    rng = np.random.default_rng(22)
+    B, T, C, M = 3, 50, 7, 3
+    mu, x = rng.uniform(0, 1, (M, C)), rng.normal(size=(B, T, C))
+    d_out, d_xpo = rng.normal(size=(M, B, T, C)), rng.normal(size=(B, C))
+    for xp in (rng.normal(size=(B, C)), None):
+        dx, dxp, dmu = oracle.token_shift_backward(mu, x, xp, d_out, d_xpo)
+        xp0 = np.zeros((B, C)) if xp is None else xp
+        h = 1e-5
+        for _ in range(3):
+            ex, ep, em = rng.normal(size=x.shape), rng.normal(size=(B, C)), rng.normal(size=mu.shape)
+            lp = _shift_loss(oracle, mu + h * em, x + h * ex, xp0 + h * ep, d_out, d_xpo)
+            lm = _shift_loss(oracle, mu - h * em, x - h * ex, xp0 - h * ep, d_out, d_xpo)
+            want = (lp - lm) / (2 * h)
+            got = float(np.sum(dx * ex) + np.sum(dxp * ep) + np.sum(dmu * em))
+            assert abs(got - want) <= 1e-7 * (1 + abs(want)), (got, want)
+
+
+def test_token_shift_backward_limits(oracle):
+    rng = np.random.default_rng(23)
+    B, T, C, M = 2, 6, 4, 3
+    x, xp = rng.normal(size=(B, T, C)), rng.normal(size=(B, C))
+    d_out, d_xpo = rng.normal(size=(M, B, T, C)), rng.normal(size=(B, C))
+    # mu = 1: no shift; every mix passes its gradient straight to its own token
+    dx, dxp, _ = oracle.token_shift_backward(np.ones((M, C)), x, xp, d_out, d_xpo)
+    want = d_out.sum(axis=0)
+    want[:, T - 1] += d_xpo
+    np.testing.assert_allclose(dx, want, rtol=1e-15, atol=1e-15)
+    assert np.all(dxp == 0)
+    # mu = 0: a pure shift by one token
+    dx, dxp, _ = oracle.token_shift_backward(np.zeros((M, C)), x, xp, d_out, d_xpo)
+    want = np.zeros_like(x)
+    want[:, :T - 1] = d_out.sum(axis=0)[:, 1:]
+    want[:, T - 1] = d_xpo
+    np.testing.assert_allclose(dx, want, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(dxp, d_out.sum(axis=0)[:, 0], rtol=1e-15)
+    # no tokens: the carried token's gradient passes through; dmu is zero
+    dx, dxp, dmu = oracle.token_shift_backward(rng.uniform(0, 1, (M, C)), np.zeros((B, 0, C)),
+                                               xp, np.zeros((M, B, 0, C)), d_xpo)
+    np.testing.assert_array_equal(dxp, d_xpo)
+    assert dx.size == 0 and np.all(dmu == 0)
+
+
 def _shift_fixture():
     rows = {"x": [], "mu": [], "out": {}, "prev": None, "last": None}
     with open(os.path.join(GOLDEN, "token_shift_worked.txt")) as f:
