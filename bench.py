@@ -25,6 +25,7 @@ workloads with extra measurements, not the headline:
     gpt_gated, decode_gated   the same with the output gate sigmoid(r) fused in
     gpt_bf16, gpt_f16         the GPT forward with 16-bit activations (state fp32)
     token_shift               the token shift at the GPT shape (3 mixes)
+    token_shift_bwd           its backward (dx, d_x_prev, dmu)
     copy                      a 1 GiB device copy, the bandwidth reference
 """
 from __future__ import annotations
@@ -650,11 +651,12 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
             "cpu_baseline": cpu}
 
 
-def bench_shift(args, torch, wkv, synth):
+def bench_shift(args, torch, wkv, synth, backward: bool = False):
     """Token shift at the GPT shape (B=8 T=1024 C=2048) with the three mixes of
     the R, K and V inputs, the carried token updated in place; rotating over
     4 input sets (1 GiB of traffic in all, beyond the 256 MB last-level
-    cache)."""
+    cache).  backward: the shift's backward (dx, d_x_prev, dmu) from seeded
+    gradients of the mixes and of the carried token."""
     sh = synth.SHAPES[synth.GPT]
     B, T, C, M, NSET = sh["B"], sh["T"], sh["C"], 3, 4
     dev = torch.device("cuda")
@@ -662,13 +664,30 @@ def bench_shift(args, torch, wkv, synth):
     sets = []
     for i in range(NSET):
         mu, x, xp = synth.shift_inputs(synth.GPT, 100 + i, B, T, C, M, device=dev)
-        sets.append(dict(mu=mu, x=x, xp=xp,
-                         out=torch.empty((M, B, T, C), device=dev)))
+        e = dict(mu=mu, x=x, xp=xp)
+        if backward:
+            e["d"] = synth.normal((M, B, T, C), 1.0, synth.seed_of(synth.GPT, 9800 + i, 0),
+                                  device=dev)
+            e["dxpo"] = synth.normal((B, C), 1.0, synth.seed_of(synth.GPT, 9900 + i, 0),
+                                     device=dev)
+            e["dx"], e["dxp"] = torch.empty_like(x), torch.empty((B, C), device=dev)
+            e["dmu"] = torch.empty((M, C), device=dev)
+        else:
+            e["out"] = torch.empty((M, B, T, C), device=dev)
+        sets.append(e)
+    if backward:
+        ws = torch.empty(max(1, int(wkv.load_library().wkv_token_shift_backward_workspace_size(
+            B, T, C, M))), device=dev, dtype=torch.uint8)
 
     def call(i):
         e = sets[i % NSET]
-        wkv.wkv_token_shift(e["mu"], e["x"], e["xp"], out=e["out"], x_prev_out=e["xp"],
-                            stream=stream)
+        if backward:
+            wkv.wkv_token_shift_backward(e["mu"], e["x"], e["d"], x_prev=e["xp"],
+                                         d_x_prev_out=e["dxpo"], dx=e["dx"], d_x_prev=e["dxp"],
+                                         dmu=e["dmu"], workspace=ws, stream=stream)
+        else:
+            wkv.wkv_token_shift(e["mu"], e["x"], e["xp"], out=e["out"], x_prev_out=e["xp"],
+                                stream=stream)
 
     for i in range(args.warmup * NSET):
         call(i)
@@ -681,9 +700,16 @@ def bench_shift(args, torch, wkv, synth):
     ms = tm.stop_ms()
     per = ms / n
     elems = B * T * C
-    # x in, M outputs out; mu; carried token in and out
-    algo = (4 + 4 * M) * elems + 4 * M * C + 8 * B * C
-    kname = f"shift_kernel<4, {M}>"
+    if backward:
+        # x and the M mix gradients in, dx out; mu in, dmu out; the carried
+        # token's gradient in, d_x_prev out
+        algo = (8 + 4 * M) * elems + 8 * M * C + 8 * B * C
+        kname = f"shift_bwd_kernel<4, {M}>"
+    else:
+        # x in, M outputs out; mu; carried token in and out
+        algo = (4 + 4 * M) * elems + 4 * M * C + 8 * B * C
+        kname = f"shift_kernel<4, {M}>"
+    wl = "token_shift_bwd" if backward else "token_shift"
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -693,25 +719,33 @@ def bench_shift(args, torch, wkv, synth):
                 return None
             e = sets[i]
             a = [e[nm].double().cpu().numpy() for nm in ("mu", "x", "xp")]
-            t0 = time.perf_counter()
-            oracle.token_shift(*a)
+            if backward:
+                dd, dp = e["d"].double().cpu().numpy(), e["dxpo"].double().cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.token_shift_backward(*a, dd, dp)
+            else:
+                t0 = time.perf_counter()
+                oracle.token_shift(*a)
             return elems, time.perf_counter() - t0
 
         done, secs, calls = timed_oracle(one, args.cpu_seconds)
         cpu = {"value": done / secs, "unit": "tok·ch/s", "cores": 1, "kind": "oracle",
                "sample": f"{calls} of the 4 input sets (B=8 T=1024 C=2048, M=3), float64 "
                          f"loop on 1 thread ({secs:.1f} s)"}
-    return {"metric": "token shift tokens·channels/sec, B=8 T=1024 C=2048, 3 mixes, fp32",
+    metric = "token shift tokens·channels/sec, B=8 T=1024 C=2048, 3 mixes, fp32"
+    if backward:
+        metric = metric.replace("token shift", "token shift backward")
+    return {"metric": metric,
             "value": elems / (per * 1e-3), "unit": "tok·ch/s", "n_gpus": 1, "steps": n,
             "warmup": args.warmup * NSET, "ms_per_step": per, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic (seeded; x, x_prev ~ N(0,1), mu ~ U(0,1))",
-            "config": {"workload": "token_shift", "B": B, "T": T, "C": C, "mixes": M,
+            "config": {"workload": wl, "B": B, "T": T, "C": C, "mixes": M,
                        "kernel": kname},
             "roofline": {"bound": "hbm", "achieved": algo / (per * 1e-3) / 1e9,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": algo / (per * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "traffic": measured_traffic(kname, "token_shift"),
+                         "traffic": measured_traffic(kname, wl),
                          "algorithmic_bytes_per_launch": algo, "avg_launch_us": per * 1e3},
             "cpu_baseline": cpu}
 
@@ -752,7 +786,7 @@ def main():
                              "decode_gated", "stability_fwd", "stability_bwd",
                              "stability_bwd_state", "stability_bwd_bf16", "stability_fwd_ckpt",
                              "stability_bwd_ckpt", "stability_bwd_ckpt_bf16",
-                             "stability_bwd_gated_ckpt", "token_shift",
+                             "stability_bwd_gated_ckpt", "token_shift", "token_shift_bwd",
                              "copy"])
     ap.add_argument("--plan", type=int, nargs="+", default=None,
                     metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
@@ -777,6 +811,7 @@ def main():
           "gpt_f16": lambda a, t, w, s: bench_gpt(a, t, w, s, False, "f16"),
           "decode_gated": lambda a, t, w, s: bench_decode(a, t, w, s, True),
           "token_shift": bench_shift,
+          "token_shift_bwd": lambda a, t, w, s: bench_shift(a, t, w, s, True),
           "stability_fwd": lambda a, t, w, s: bench_stability(a, t, w, s, False),
           "stability_bwd": lambda a, t, w, s: bench_stability(a, t, w, s, True),
           "stability_bwd_state": lambda a, t, w, s: bench_stability(a, t, w, s, True, True),

@@ -457,6 +457,43 @@ WKV_API wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, c
                                    const float *x, const float *x_prev, float *out,
                                    float *x_prev_out, hipStream_t stream);
 
+/*
+ * Backward of wkv_token_shift, for training the time-mixing block.  With d_out
+ * the gradients of the M mixes and d_x_prev_out that of the carried token the
+ * forward handed on, token t feeds mix t with weight mu and mix t + 1 with
+ * 1 - mu (RWKV architecture deep dive, section "Token shift"; the pages state
+ * no backward):
+ *   dx[b][t][c]   = sum_m mu[m][c] d_out[m][b][t][c]
+ *                 + sum_m (1 - mu[m][c]) d_out[m][b][t+1][c]   (t + 1 < T)
+ *                 + d_x_prev_out[b][c]                        (t = T - 1)
+ *   d_x_prev[b][c] = sum_m (1 - mu[m][c]) d_out[m][b][0][c]    (T > 0;
+ *                    d_x_prev_out when T = 0)
+ *   dmu[m][c]     = sum_{b,t} d_out[m][b][t][c] (x[b][t][c] - x[b][t-1][c])
+ * with x[b][-1] = x_prev (zeros when NULL).
+ *
+ *   mu, x, x_prev  as for the forward call
+ *   d_out          [M][B][T][C]; required when M*B*T*C > 0
+ *   d_x_prev_out   [B][C] or NULL (no gradient reaches the carried token)
+ *   dx             [B][T][C] output; required when B*T*C > 0
+ *   d_x_prev       [B][C] output, or NULL to discard it
+ *   dmu            [M][C] output, the sum over B and T in a fixed order
+ *                  (bitwise reproducible); required when M*C > 0
+ *   workspace      device scratch of at least
+ *                  wkv_token_shift_backward_workspace_size(B,T,C,M) bytes,
+ *                  caller-owned; may be NULL when that size is 0
+ * Outputs overlap neither the inputs nor each other.  M above
+ * WKV_TOKEN_SHIFT_MAX_MIXES is WKV_ERR_UNSUPPORTED; other errors as for
+ * wkv_backward.
+ */
+WKV_API size_t wkv_token_shift_backward_workspace_size(int64_t B, int64_t T, int64_t C,
+                                                       int64_t M);
+WKV_API wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M,
+                                            const float *mu, const float *x,
+                                            const float *x_prev, const float *d_out,
+                                            const float *d_x_prev_out, float *dx,
+                                            float *d_x_prev, float *dmu, void *workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -478,6 +478,54 @@ WKV_API wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, c
     return from_hip(wkv::launch_token_shift(a, in_place, stream));
 }
 
+// Scratch of the token shift's backward: one dmu partial per (sequence,
+// 256-token tile, mix, channel).
+int64_t shift_bwd_ws_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {
+    if (B <= 0 || T <= 0 || C <= 0 || M <= 0) return 0;
+    const int64_t n = bytes_of(wkv::shift_bwd_tiles(T) * B, M, C);
+    return n < 0 ? -1 : (n + 255) / 256 * 256;
+}
+
+WKV_API size_t wkv_token_shift_backward_workspace_size(int64_t B, int64_t T, int64_t C,
+                                                       int64_t M) {
+    if (B < 0 || T < 0 || C < 0 || M < 0 || M > WKV_TOKEN_SHIFT_MAX_MIXES) return 0;
+    const int64_t n = shift_bwd_ws_bytes(B, T, C, M);
+    return n < 0 ? 0 : (size_t)n;
+}
+
+WKV_API wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M,
+                                            const float *mu, const float *x,
+                                            const float *x_prev, const float *d_out,
+                                            const float *d_x_prev_out, float *dx,
+                                            float *d_x_prev, float *dmu, void *workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || T < 0 || C < 0 || M < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(B, T, C);
+    const int64_t lanes = bytes_of(1, B, C);
+    const int64_t mus = bytes_of(M, 1, C);
+    const int64_t outs = seq < 0 ? -1 : bytes_of(M, 1, seq, 1);
+    const int64_t need = shift_bwd_ws_bytes(B, T, C, M);
+    if (seq < 0 || lanes < 0 || mus < 0 || outs < 0 || need < 0) return WKV_ERR_OVERFLOW;
+    if (M > WKV_TOKEN_SHIFT_MAX_MIXES) return WKV_ERR_UNSUPPORTED;
+    if (seq > 0 && (!x || !dx)) return WKV_ERR_NULL;
+    if (outs > 0 && (!mu || !d_out)) return WKV_ERR_NULL;
+    if (mus > 0 && !dmu) return WKV_ERR_NULL;
+    if (need > 0 && (!workspace || workspace_bytes < (size_t)need)) return WKV_ERR_WORKSPACE;
+    const Range rmu = rng(mu, mus), rx = rng(x, seq), rxp = rng(x_prev, lanes),
+                rd = rng(d_out, outs), rdp = rng(d_x_prev_out, lanes);
+    const Range o[] = {rng(dx, seq), rng(d_x_prev, lanes), rng(dmu, mus), rng(workspace, need)};
+    for (int i = 0; i < 4; ++i) {
+        for (Range q : {rmu, rx, rxp, rd, rdp})
+            if (overlap(o[i], q)) return WKV_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(o[i], o[j])) return WKV_ERR_ALIAS;
+    }
+    const wkv::ShiftBwdArgs a{B,     T,  C,        M,   mu,  x,
+                              x_prev, d_out, d_x_prev_out, dx, d_x_prev, dmu,
+                              (float *)workspace};
+    return from_hip(wkv::launch_token_shift_backward(a, stream));
+}
+
 WKV_API size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
     if (B < 0 || T < 0 || C < 0 || bytes_of(B, T, C) < 0) return 0;
     return wkv::backward_workspace_bytes(B, T, C);

@@ -102,6 +102,17 @@ hipError_t launch_step(const StepArgs &a, hipStream_t st);
 constexpr int64_t kMaxMixes = 8;
 hipError_t launch_token_shift(const ShiftArgs &a, bool in_place_state, hipStream_t st);
 
+// Backward of the token shift: d_out [M][B][T][C] and d_xpo [B][C] (NULL: zero)
+// in; dx [B][T][C], dxp [B][C] (NULL: not wanted) and dmu [M][C] out; part is
+// scratch of shift_bwd_tiles(T) * B * M * C floats.
+struct ShiftBwdArgs {
+    int64_t B, T, C, M;
+    const float *mu, *x, *x_prev, *d_out, *d_xpo;
+    float *dx, *dxp, *dmu, *part;
+};
+int64_t shift_bwd_tiles(int64_t T);
+hipError_t launch_token_shift_backward(const ShiftBwdArgs &a, hipStream_t st);
+
 // backward (wkv_backward.hip)
 size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t st);

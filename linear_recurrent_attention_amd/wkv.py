@@ -43,7 +43,8 @@ EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backw
             "wkv_status_string", "wkv_forward_ex", "wkv_forward_plan_auto",
             "wkv_forward_gated", "wkv_step_gated", "wkv_token_shift", "wkv_forward_typed",
             "wkv_step_typed", "wkv_backward_state", "wkv_backward_typed",
-            "wkv_forward_checkpointed", "wkv_backward_checkpointed", "wkv_backward_gated")
+            "wkv_forward_checkpointed", "wkv_backward_checkpointed", "wkv_backward_gated",
+            "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward")
 
 # wkv_dtype values
 WKV_DTYPE_F32 = 0
@@ -122,6 +123,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_backward_checkpointed.restype = ctypes.c_int
     lib.wkv_backward_gated.argtypes = [i64, i64, i64, ctypes.c_int] + [vp] * 16 + [vp, sz, vp]
     lib.wkv_backward_gated.restype = ctypes.c_int
+    lib.wkv_token_shift_backward_workspace_size.argtypes = [i64, i64, i64, i64]
+    lib.wkv_token_shift_backward_workspace_size.restype = sz
+    lib.wkv_token_shift_backward.argtypes = [i64, i64, i64, i64] + [vp] * 8 + [vp, sz, vp]
+    lib.wkv_token_shift_backward.restype = ctypes.c_int
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -353,6 +358,35 @@ def wkv_token_shift(mu, x, x_prev=None, out=None, x_prev_out=None, stream=None):
                                         _ptr(x_prev_out), _stream(stream))
     _check("wkv_token_shift", st)
     return out, x_prev_out
+
+
+def wkv_token_shift_backward(mu, x, d_out, x_prev=None, d_x_prev_out=None, dx=None,
+                             d_x_prev=None, dmu=None, workspace=None, stream=None):
+    """Backward of ``wkv_token_shift``: the gradients d_out [M][B][T][C] of the
+    mixes and d_x_prev_out [B][C] of the carried token (None: zero) give
+    (dx [B][T][C], d_x_prev [B][C] or None, dmu [M][C]).  Pass d_x_prev=True
+    to have it allocated."""
+    if x.dim() != 3 or mu.dim() != 2:
+        raise ValueError("x must be [B][T][C] and mu [M][C]")
+    B, T, C = (int(a) for a in x.shape)
+    M = int(mu.shape[0])
+    dev = x.device
+    dx = torch.empty_like(x) if dx is None else dx
+    if d_x_prev is True:
+        d_x_prev = torch.empty((B, C), device=dev, dtype=torch.float32)
+    dmu = torch.empty((M, C), device=dev, dtype=torch.float32) if dmu is None else dmu
+    lib = load_library()
+    need = int(lib.wkv_token_shift_backward_workspace_size(B, T, C, M))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
+    st = lib.wkv_token_shift_backward(B, T, C, M, _ptr(mu), _ptr(x), _ptr(x_prev), _ptr(d_out),
+                                      _ptr(d_x_prev_out), _ptr(dx), _ptr(d_x_prev), _ptr(dmu),
+                                      ws_ptr, workspace.numel(), _stream(stream))
+    _check("wkv_token_shift_backward", st)
+    return dx, d_x_prev, dmu
 
 
 def wkv_backward_workspace_size(B: int, T: int, C: int) -> int:

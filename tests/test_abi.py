@@ -246,6 +246,40 @@ def test_gated_backward_rejects_invalid_arguments(lib):
     assert call(ck=vp(P + 12 * 0x10000000 + 256)) == W.WKV_ERR_ALIAS    # checkpoints under dr
 
 
+def test_token_shift_backward_rejects_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    B, T, C, M = 2, 100, 64, 3
+    need = lib.wkv_token_shift_backward_workspace_size(B, T, C, M)
+    assert need == 2 * 1 * 3 * 64 * 4                      # one 256-token tile per sequence
+    assert lib.wkv_token_shift_backward_workspace_size(B, 0, C, M) == 0
+    assert lib.wkv_token_shift_backward_workspace_size(B, T, C, 9) == 0
+    mu, x, xp, d, dxpo = (vp(P + i * 0x10000000) for i in range(5))
+    dx, dxp, dmu, ws = (vp(P + (8 + i) * 0x10000000) for i in range(4))
+    f = lib.wkv_token_shift_backward
+    ok = [B, T, C, M, mu, x, xp, d, dxpo, dx, dxp, dmu, ws, need, None]
+
+    def call(**over):
+        names = ["B", "T", "C", "M", "mu", "x", "xp", "d", "dxpo", "dx", "dxp", "dmu", "ws", "n",
+                 "stream"]
+        args = list(ok)
+        for key, val in over.items():
+            args[names.index(key)] = val
+        return f(*args)
+
+    assert call(B=-1) == W.WKV_ERR_DIM
+    assert call(M=9) == W.WKV_ERR_UNSUPPORTED
+    assert call(x=None) == W.WKV_ERR_NULL
+    assert call(d=None) == W.WKV_ERR_NULL
+    assert call(dmu=None) == W.WKV_ERR_NULL
+    assert call(n=need - 1) == W.WKV_ERR_WORKSPACE
+    assert call(ws=None) == W.WKV_ERR_WORKSPACE
+    assert call(dx=vp(P + 1 * 0x10000000 + 128)) == W.WKV_ERR_ALIAS      # dx over x
+    assert call(dmu=vp(P + 8 * 0x10000000 + 64)) == W.WKV_ERR_ALIAS      # dmu over dx
+    assert call(dxp=vp(P + 4 * 0x10000000)) == W.WKV_ERR_ALIAS           # d_x_prev on d_x_prev_out
+    assert call(ws=vp(P + 3 * 0x10000000 + 4)) == W.WKV_ERR_ALIAS        # workspace over d_out
+
+
 def test_forward_ex_rejects_unknown_plans(lib):
     from linear_recurrent_attention_amd import wkv as W
     vp = ctypes.c_void_p
