@@ -144,18 +144,29 @@ def test_captured_time_mixing_calls_replay_exactly():
 
 
 def test_captured_training_path_replays_exactly():
-    """The forward that writes its 128-token checkpoints and the backward that
-    starts from them, captured together: every replay reproduces the eager bits
-    (the segmented forward and the backward are bitwise reproducible)."""
+    """The forward that writes its 128-token checkpoints, the backward that
+    starts from them (plain and gated) and the token shift's backward, captured
+    together: every replay reproduces the eager bits (the segmented forward and
+    every backward are bitwise reproducible)."""
     dev = torch.device("cuda")
     B, T, C = 2, 700, 96
     side = torch.cuda.Stream()
     d = synth.make(synth.STABILITY, index=94, B=B, T=T, C=C, device=dev, with_dy=True)
     ws = torch.empty(wkv.wkv_backward_workspace_size(B, T, C), device=dev, dtype=torch.uint8)
+    r = synth.receptance(synth.STABILITY, 94, (B, T, C), device=dev)
+    mu, x, xp = (t.to(dev) for t in synth.shift_inputs(synth.GPT, 95, B, T, C, 3))
+    d_mix = synth.normal((3, B, T, C), 1.0, synth.seed_of(synth.GPT, 96, 0), device=dev)
+    d_xpo = synth.normal((B, C), 1.0, synth.seed_of(synth.GPT, 97, 0), device=dev)
+    ws_shift = torch.empty(max(1, int(wkv.load_library().wkv_token_shift_backward_workspace_size(
+        B, T, C, 3))), device=dev, dtype=torch.uint8)
     outs = dict(y=torch.empty_like(d["k"]), so=torch.empty((3, B, C), device=dev),
                 ck=torch.empty((wkv.checkpoint_count(T), 3, B, C), device=dev),
                 dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["k"]),
-                dw=torch.empty(C, device=dev), du=torch.empty(C, device=dev))
+                dw=torch.empty(C, device=dev), du=torch.empty(C, device=dev),
+                gdk=torch.empty_like(d["k"]), gdv=torch.empty_like(d["k"]),
+                gdr=torch.empty_like(d["k"]), gdw=torch.empty(C, device=dev),
+                gdu=torch.empty(C, device=dev), sdx=torch.empty_like(x),
+                sdxp=torch.empty((B, C), device=dev), sdmu=torch.empty((3, C), device=dev))
 
     def work(stream):
         wkv.wkv_forward_checkpointed(d["w"], d["u"], d["k"], d["v"], y=outs["y"],
@@ -164,6 +175,12 @@ def test_captured_training_path_replays_exactly():
         wkv.wkv_backward_checkpointed(d["w"], d["u"], d["k"], d["v"], d["dy"], outs["ck"],
                                       dk=outs["dk"], dv=outs["dv"], dw=outs["dw"], du=outs["du"],
                                       workspace=ws, stream=stream)
+        wkv.wkv_backward_gated(d["w"], d["u"], d["k"], d["v"], r, d["dy"], checkpoints=outs["ck"],
+                               dk=outs["gdk"], dv=outs["gdv"], dr=outs["gdr"], dw=outs["gdw"],
+                               du=outs["gdu"], workspace=ws, stream=stream)
+        wkv.wkv_token_shift_backward(mu, x, d_mix, x_prev=xp, d_x_prev_out=d_xpo, dx=outs["sdx"],
+                                     d_x_prev=outs["sdxp"], dmu=outs["sdmu"], workspace=ws_shift,
+                                     stream=stream)
 
     work(torch.cuda.current_stream())
     torch.cuda.synchronize()
