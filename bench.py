@@ -795,9 +795,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the WKV lanes are independent, so the operator "
-              "shards across GPUs without communication and this build runs on one GPU only "
-              "(--gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU (--gpus 1): the WKV lanes are independent, so the "
+              "operator shards across GPUs without communication, and libwkv has no multi-GPU "
+              "path to measure.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
