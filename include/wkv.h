@@ -458,6 +458,20 @@ WKV_API wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, c
                                    float *x_prev_out, hipStream_t stream);
 
 /*
+ * wkv_token_shift with x, x_prev, out and x_prev_out holding `dtype` elements
+ * (wkv_dtype; mu stays float32): the mixes are computed in float32 and rounded
+ * once to `dtype` (nearest, ties to even); the carried token is copied
+ * exactly.  Arguments, semantics and errors as for wkv_token_shift, with byte
+ * sizes at the element size of dtype; an unknown dtype returns
+ * WKV_ERR_UNSUPPORTED.  Cites: as wkv_token_shift; 16-bit activations as for
+ * wkv_forward_typed.
+ */
+WKV_API wkv_status wkv_token_shift_typed(int64_t B, int64_t T, int64_t C, int64_t M,
+                                         wkv_dtype dtype, const float *mu, const void *x,
+                                         const void *x_prev, void *out, void *x_prev_out,
+                                         hipStream_t stream);
+
+/*
  * Backward of wkv_token_shift, for training the time-mixing block.  With d_out
  * the gradients of the M mixes and d_x_prev_out that of the carried token the
  * forward handed on, token t feeds mix t with weight mu and mix t + 1 with
@@ -493,6 +507,21 @@ WKV_API wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int
                                             const float *d_x_prev_out, float *dx,
                                             float *d_x_prev, float *dmu, void *workspace,
                                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * wkv_token_shift_backward with x, x_prev, d_out, d_x_prev_out, dx and
+ * d_x_prev holding `dtype` elements (mu and dmu stay float32; all arithmetic
+ * is float32, dx and d_x_prev are rounded once to `dtype`).  Arguments,
+ * workspace size and errors as for wkv_token_shift_backward, with byte sizes
+ * at the element size of dtype.
+ */
+WKV_API wkv_status wkv_token_shift_backward_typed(int64_t B, int64_t T, int64_t C, int64_t M,
+                                                  wkv_dtype dtype, const float *mu,
+                                                  const void *x, const void *x_prev,
+                                                  const void *d_out, const void *d_x_prev_out,
+                                                  void *dx, void *d_x_prev, float *dmu,
+                                                  void *workspace, size_t workspace_bytes,
+                                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

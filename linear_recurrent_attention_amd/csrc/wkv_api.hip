@@ -372,6 +372,81 @@ wkv_status backward_impl(int64_t B, int64_t T, int64_t C, int io, const float *w
     return from_hip(wkv::launch_backward(a, stream));
 }
 
+// Scratch of the token shift's backward: one dmu partial per (sequence,
+// 256-token tile, mix, channel).
+int64_t shift_bwd_ws_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {
+    if (B <= 0 || T <= 0 || C <= 0 || M <= 0) return 0;
+    const int64_t n = bytes_of(wkv::shift_bwd_tiles(T) * B, M, C);
+    return n < 0 ? -1 : (n + 255) / 256 * 256;
+}
+
+// wkv_token_shift and wkv_token_shift_typed: io is the wkv_dtype of x, x_prev,
+// out and x_prev_out (mu is float32).
+wkv_status token_shift_impl(int64_t B, int64_t T, int64_t C, int64_t M, int io,
+                            const float *mu, const void *x, const void *x_prev, void *out,
+                            void *x_prev_out, hipStream_t stream) {
+    const int64_t esize = elem_bytes(io);
+    if (esize == 0) return WKV_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || C < 0 || M < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(B, T, C, esize);
+    const int64_t lanes = bytes_of(1, B, C, esize);
+    const int64_t mus = bytes_of(M, 1, C);
+    const int64_t outs = seq < 0 ? -1 : bytes_of(M, 1, seq, 1);
+    if (seq < 0 || lanes < 0 || mus < 0 || outs < 0) return WKV_ERR_OVERFLOW;
+    if (M > WKV_TOKEN_SHIFT_MAX_MIXES) return WKV_ERR_UNSUPPORTED;
+    if (lanes == 0) return WKV_OK;
+    if (seq > 0 && !x) return WKV_ERR_NULL;
+    if (outs > 0 && (!mu || !out)) return WKV_ERR_NULL;
+    const Range rmu = rng(mu, seq > 0 ? mus : 0), rx = rng(x, seq), rp = rng(x_prev, lanes);
+    const Range ro = rng(out, outs), rpo = rng(x_prev_out, lanes);
+    for (Range q : {rmu, rx, rp, rpo})
+        if (overlap(ro, q)) return WKV_ERR_ALIAS;
+    for (Range q : {rmu, rx})
+        if (overlap(rpo, q)) return WKV_ERR_ALIAS;
+    if (overlap(rpo, rp) && x_prev_out != (const void *)x_prev) return WKV_ERR_ALIAS;
+    if (!x_prev_out && outs == 0) return WKV_OK;
+    wkv::ShiftArgs a{B, T, C, M, mu, x, x_prev, out, x_prev_out};
+    a.io = io;
+    const bool in_place = x_prev_out != nullptr && x_prev_out == (const void *)x_prev;
+    return from_hip(wkv::launch_token_shift(a, in_place, stream));
+}
+
+// wkv_token_shift_backward and wkv_token_shift_backward_typed: io is the
+// wkv_dtype of x, x_prev, d_out, d_x_prev_out, dx and d_x_prev.
+wkv_status token_shift_backward_impl(int64_t B, int64_t T, int64_t C, int64_t M, int io,
+                                     const float *mu, const void *x, const void *x_prev,
+                                     const void *d_out, const void *d_x_prev_out, void *dx,
+                                     void *d_x_prev, float *dmu, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+    const int64_t esize = elem_bytes(io);
+    if (esize == 0) return WKV_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || C < 0 || M < 0) return WKV_ERR_DIM;
+    const int64_t seq = bytes_of(B, T, C, esize);
+    const int64_t lanes = bytes_of(1, B, C, esize);
+    const int64_t mus = bytes_of(M, 1, C);
+    const int64_t outs = seq < 0 ? -1 : bytes_of(M, 1, seq, 1);
+    const int64_t need = shift_bwd_ws_bytes(B, T, C, M);
+    if (seq < 0 || lanes < 0 || mus < 0 || outs < 0 || need < 0) return WKV_ERR_OVERFLOW;
+    if (M > WKV_TOKEN_SHIFT_MAX_MIXES) return WKV_ERR_UNSUPPORTED;
+    if (seq > 0 && (!x || !dx)) return WKV_ERR_NULL;
+    if (outs > 0 && (!mu || !d_out)) return WKV_ERR_NULL;
+    if (mus > 0 && !dmu) return WKV_ERR_NULL;
+    if (need > 0 && (!workspace || workspace_bytes < (size_t)need)) return WKV_ERR_WORKSPACE;
+    const Range rmu = rng(mu, mus), rx = rng(x, seq), rxp = rng(x_prev, lanes),
+                rd = rng(d_out, outs), rdp = rng(d_x_prev_out, lanes);
+    const Range o[] = {rng(dx, seq), rng(d_x_prev, lanes), rng(dmu, mus), rng(workspace, need)};
+    for (int i = 0; i < 4; ++i) {
+        for (Range q : {rmu, rx, rxp, rd, rdp})
+            if (overlap(o[i], q)) return WKV_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(o[i], o[j])) return WKV_ERR_ALIAS;
+    }
+    wkv::ShiftBwdArgs a{B, T, C, M, mu, x, x_prev, d_out, d_x_prev_out, dx, d_x_prev, dmu,
+                        (float *)workspace};
+    a.io = io;
+    return from_hip(wkv::launch_token_shift_backward(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -455,35 +530,14 @@ WKV_API wkv_status wkv_step_typed(int64_t L, int64_t B, int64_t C, wkv_dtype dty
 WKV_API wkv_status wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const float *mu,
                                    const float *x, const float *x_prev, float *out,
                                    float *x_prev_out, hipStream_t stream) {
-    if (B < 0 || T < 0 || C < 0 || M < 0) return WKV_ERR_DIM;
-    const int64_t seq = bytes_of(B, T, C);
-    const int64_t lanes = bytes_of(1, B, C);
-    const int64_t mus = bytes_of(M, 1, C);
-    const int64_t outs = seq < 0 ? -1 : bytes_of(M, 1, seq, 1);
-    if (seq < 0 || lanes < 0 || mus < 0 || outs < 0) return WKV_ERR_OVERFLOW;
-    if (M > WKV_TOKEN_SHIFT_MAX_MIXES) return WKV_ERR_UNSUPPORTED;
-    if (lanes == 0) return WKV_OK;
-    if (seq > 0 && !x) return WKV_ERR_NULL;
-    if (outs > 0 && (!mu || !out)) return WKV_ERR_NULL;
-    const Range rmu = rng(mu, seq > 0 ? mus : 0), rx = rng(x, seq), rp = rng(x_prev, lanes);
-    const Range ro = rng(out, outs), rpo = rng(x_prev_out, lanes);
-    for (Range q : {rmu, rx, rp, rpo})
-        if (overlap(ro, q)) return WKV_ERR_ALIAS;
-    for (Range q : {rmu, rx})
-        if (overlap(rpo, q)) return WKV_ERR_ALIAS;
-    if (overlap(rpo, rp) && x_prev_out != (float *)x_prev) return WKV_ERR_ALIAS;
-    if (!x_prev_out && outs == 0) return WKV_OK;
-    const wkv::ShiftArgs a{B, T, C, M, mu, x, x_prev, out, x_prev_out};
-    const bool in_place = x_prev_out != nullptr && x_prev_out == (float *)x_prev;
-    return from_hip(wkv::launch_token_shift(a, in_place, stream));
+    return token_shift_impl(B, T, C, M, WKV_DTYPE_F32, mu, x, x_prev, out, x_prev_out, stream);
 }
 
-// Scratch of the token shift's backward: one dmu partial per (sequence,
-// 256-token tile, mix, channel).
-int64_t shift_bwd_ws_bytes(int64_t B, int64_t T, int64_t C, int64_t M) {
-    if (B <= 0 || T <= 0 || C <= 0 || M <= 0) return 0;
-    const int64_t n = bytes_of(wkv::shift_bwd_tiles(T) * B, M, C);
-    return n < 0 ? -1 : (n + 255) / 256 * 256;
+WKV_API wkv_status wkv_token_shift_typed(int64_t B, int64_t T, int64_t C, int64_t M,
+                                         wkv_dtype dtype, const float *mu, const void *x,
+                                         const void *x_prev, void *out, void *x_prev_out,
+                                         hipStream_t stream) {
+    return token_shift_impl(B, T, C, M, (int)dtype, mu, x, x_prev, out, x_prev_out, stream);
 }
 
 WKV_API size_t wkv_token_shift_backward_workspace_size(int64_t B, int64_t T, int64_t C,
@@ -499,31 +553,21 @@ WKV_API wkv_status wkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int
                                             const float *d_x_prev_out, float *dx,
                                             float *d_x_prev, float *dmu, void *workspace,
                                             size_t workspace_bytes, hipStream_t stream) {
-    if (B < 0 || T < 0 || C < 0 || M < 0) return WKV_ERR_DIM;
-    const int64_t seq = bytes_of(B, T, C);
-    const int64_t lanes = bytes_of(1, B, C);
-    const int64_t mus = bytes_of(M, 1, C);
-    const int64_t outs = seq < 0 ? -1 : bytes_of(M, 1, seq, 1);
-    const int64_t need = shift_bwd_ws_bytes(B, T, C, M);
-    if (seq < 0 || lanes < 0 || mus < 0 || outs < 0 || need < 0) return WKV_ERR_OVERFLOW;
-    if (M > WKV_TOKEN_SHIFT_MAX_MIXES) return WKV_ERR_UNSUPPORTED;
-    if (seq > 0 && (!x || !dx)) return WKV_ERR_NULL;
-    if (outs > 0 && (!mu || !d_out)) return WKV_ERR_NULL;
-    if (mus > 0 && !dmu) return WKV_ERR_NULL;
-    if (need > 0 && (!workspace || workspace_bytes < (size_t)need)) return WKV_ERR_WORKSPACE;
-    const Range rmu = rng(mu, mus), rx = rng(x, seq), rxp = rng(x_prev, lanes),
-                rd = rng(d_out, outs), rdp = rng(d_x_prev_out, lanes);
-    const Range o[] = {rng(dx, seq), rng(d_x_prev, lanes), rng(dmu, mus), rng(workspace, need)};
-    for (int i = 0; i < 4; ++i) {
-        for (Range q : {rmu, rx, rxp, rd, rdp})
-            if (overlap(o[i], q)) return WKV_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(o[i], o[j])) return WKV_ERR_ALIAS;
-    }
-    const wkv::ShiftBwdArgs a{B,     T,  C,        M,   mu,  x,
-                              x_prev, d_out, d_x_prev_out, dx, d_x_prev, dmu,
-                              (float *)workspace};
-    return from_hip(wkv::launch_token_shift_backward(a, stream));
+    return token_shift_backward_impl(B, T, C, M, WKV_DTYPE_F32, mu, x, x_prev, d_out,
+                                     d_x_prev_out, dx, d_x_prev, dmu, workspace,
+                                     workspace_bytes, stream);
+}
+
+WKV_API wkv_status wkv_token_shift_backward_typed(int64_t B, int64_t T, int64_t C, int64_t M,
+                                                  wkv_dtype dtype, const float *mu,
+                                                  const void *x, const void *x_prev,
+                                                  const void *d_out, const void *d_x_prev_out,
+                                                  void *dx, void *d_x_prev, float *dmu,
+                                                  void *workspace, size_t workspace_bytes,
+                                                  hipStream_t stream) {
+    return token_shift_backward_impl(B, T, C, M, (int)dtype, mu, x, x_prev, d_out,
+                                     d_x_prev_out, dx, d_x_prev, dmu, workspace,
+                                     workspace_bytes, stream);
 }
 
 WKV_API size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {

@@ -42,10 +42,13 @@ struct StepArgs {
     int io;
 };
 
+// x, x_prev, out and x_prev_out hold elements of format `io`; mu is float32.
 struct ShiftArgs {
     int64_t B, T, C, M;
-    const float *mu, *x, *x_prev;
-    float *out, *x_prev_out;
+    const float *mu;
+    const void *x, *x_prev;
+    void *out, *x_prev_out;
+    int io = kIoF32;
 };
 
 // s_in: state before the first token (NULL: empty); s_out, ds_out: the state
@@ -104,11 +107,15 @@ hipError_t launch_token_shift(const ShiftArgs &a, bool in_place_state, hipStream
 
 // Backward of the token shift: d_out [M][B][T][C] and d_xpo [B][C] (NULL: zero)
 // in; dx [B][T][C], dxp [B][C] (NULL: not wanted) and dmu [M][C] out; part is
-// scratch of shift_bwd_tiles(T) * B * M * C floats.
+// scratch of shift_bwd_tiles(T) * B * M * C floats.  x, x_prev, d_out, d_xpo,
+// dx and dxp hold elements of format `io`; mu, dmu and part are float32.
 struct ShiftBwdArgs {
     int64_t B, T, C, M;
-    const float *mu, *x, *x_prev, *d_out, *d_xpo;
-    float *dx, *dxp, *dmu, *part;
+    const float *mu;
+    const void *x, *x_prev, *d_out, *d_xpo;
+    void *dx, *dxp;
+    float *dmu, *part;
+    int io = kIoF32;
 };
 int64_t shift_bwd_tiles(int64_t T);
 hipError_t launch_token_shift_backward(const ShiftBwdArgs &a, hipStream_t st);

@@ -30,57 +30,95 @@ struct Vec {
     float x[VEC];
 };
 
-template <int VEC>
-__device__ __forceinline__ Vec<VEC> vload(const float *p) {
+// VEC consecutive elements of format IO (float32 or a 16-bit format), widened
+// to float; 16-byte (float32) or 8-byte (16-bit) accesses when VEC = 4.
+template <class IO, int VEC>
+__device__ __forceinline__ Vec<VEC> vload(const typename IO::T *p) {
     Vec<VEC> r;
-    if constexpr (VEC == 4) {
-        typedef float f4 __attribute__((ext_vector_type(4)));
-        const f4 q = __builtin_nontemporal_load((const f4 *)p);
+    if constexpr (IO::kBytes == 4) {
+        if constexpr (VEC == 4) {
+            typedef float f4 __attribute__((ext_vector_type(4)));
+            const f4 q = __builtin_nontemporal_load((const f4 *)p);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.x[i] = q[i];
+            for (int i = 0; i < 4; ++i) r.x[i] = q[i];
+        } else {
+            r.x[0] = __builtin_nontemporal_load((const float *)p);
+        }
     } else {
-        r.x[0] = __builtin_nontemporal_load(p);
+        using T = typename IO::T;
+        if constexpr (VEC == 4) {
+            // one 8-byte access, as two 32-bit words (a vector of four 16-bit
+            // elements is split by the compiler into narrower accesses)
+            typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+            const u2 q = __builtin_nontemporal_load((const u2 *)p);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const unsigned short h = (unsigned short)(q[i >> 1] >> (16 * (i & 1)));
+                r.x[i] = IO::to_f(__builtin_bit_cast(T, h));
+            }
+        } else {
+            const unsigned short q = __builtin_nontemporal_load((const unsigned short *)p);
+            r.x[0] = IO::to_f(__builtin_bit_cast(T, q));
+        }
     }
     return r;
 }
 
-template <int VEC>
-__device__ __forceinline__ void vstore(float *p, const Vec<VEC> &r) {
-    if constexpr (VEC == 4) {
-        typedef float f4 __attribute__((ext_vector_type(4)));
-        f4 q;
+// Rounds once to IO (nearest, ties to even) and stores.
+template <class IO, int VEC>
+__device__ __forceinline__ void vstore(typename IO::T *p, const Vec<VEC> &r) {
+    if constexpr (IO::kBytes == 4) {
+        if constexpr (VEC == 4) {
+            typedef float f4 __attribute__((ext_vector_type(4)));
+            f4 q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = r.x[i];
-        __builtin_nontemporal_store(q, (f4 *)p);
+            for (int i = 0; i < 4; ++i) q[i] = r.x[i];
+            __builtin_nontemporal_store(q, (f4 *)p);
+        } else {
+            __builtin_nontemporal_store(r.x[0], (float *)p);
+        }
     } else {
-        __builtin_nontemporal_store(r.x[0], p);
+        if constexpr (VEC == 4) {
+            typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+            u2 q;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                q[j] = (unsigned int)__builtin_bit_cast(unsigned short, IO::from_f(r.x[2 * j])) |
+                       ((unsigned int)__builtin_bit_cast(unsigned short, IO::from_f(r.x[2 * j + 1]))
+                        << 16);
+            __builtin_nontemporal_store(q, (u2 *)p);
+        } else {
+            __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, IO::from_f(r.x[0])),
+                                        (unsigned short *)p);
+        }
     }
 }
 
-template <int VEC, int M>
-__device__ __forceinline__ void emit(float *out, int64_t plane, int64_t off, const Vec<VEC> (&mu)[M],
-                                     const Vec<VEC> (&nu)[M], const Vec<VEC> &cur,
-                                     const Vec<VEC> &prev) {
+template <class IO, int VEC, int M>
+__device__ __forceinline__ void emit(typename IO::T *out, int64_t plane, int64_t off,
+                                     const Vec<VEC> (&mu)[M], const Vec<VEC> (&nu)[M],
+                                     const Vec<VEC> &cur, const Vec<VEC> &prev) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         Vec<VEC> o;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) o.x[i] = fmaf(mu[m].x[i], cur.x[i], nu[m].x[i] * prev.x[i]);
-        vstore<VEC>(out + m * plane + off, o);
+        vstore<IO, VEC>(out + m * plane + off, o);
     }
 }
 
 // 1-D grid: column block fastest, then tile, then sequence.  write_last: this
 // kernel also stores x[b][T-1] into x_prev_out (the host clears it when
 // x_prev_out is x_prev itself and another workgroup may still read x_prev).
-template <int VEC, int M>
+// IO: element format of x, x_prev, out and x_prev_out (mu is float32).
+template <class IO, int VEC, int M>
 __global__ __launch_bounds__(256) void shift_kernel(int64_t B, int64_t T, int64_t C,
                                                     uint32_t cblocks, uint32_t ntiles,
                                                     const float *__restrict__ mu,
-                                                    const float *__restrict__ x,
-                                                    const float *x_prev,
-                                                    float *__restrict__ out, float *x_prev_out,
-                                                    int write_last) {
+                                                    const typename IO::T *__restrict__ x,
+                                                    const typename IO::T *x_prev,
+                                                    typename IO::T *__restrict__ out,
+                                                    typename IO::T *x_prev_out, int write_last) {
     const uint32_t cb = blockIdx.x % cblocks;
     const uint32_t rest = blockIdx.x / cblocks;
     const uint32_t tile = rest % ntiles;
@@ -101,9 +139,9 @@ __global__ __launch_bounds__(256) void shift_kernel(int64_t B, int64_t T, int64_
     const int64_t plane = B * T * C;
     Vec<VEC> prev;
     if (t0 > 0) {
-        prev = vload<VEC>(x + (row0 + t0 - 1) * C + c);
+        prev = vload<IO, VEC>(x + (row0 + t0 - 1) * C + c);
     } else if (x_prev) {
-        prev = vload<VEC>(x_prev + bb * C + c);
+        prev = vload<IO, VEC>(x_prev + bb * C + c);
     } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) prev.x[i] = 0.0f;
@@ -112,59 +150,63 @@ __global__ __launch_bounds__(256) void shift_kernel(int64_t B, int64_t T, int64_
         // whole tile: every row load issued before the first use
         Vec<VEC> cur[kTT];
 #pragma unroll
-        for (int t = 0; t < kTT; ++t) cur[t] = vload<VEC>(x + (row0 + t0 + t) * C + c);
+        for (int t = 0; t < kTT; ++t) cur[t] = vload<IO, VEC>(x + (row0 + t0 + t) * C + c);
 #pragma unroll
         for (int t = 0; t < kTT; ++t) {
-            emit<VEC, M>(out, plane, (row0 + t0 + t) * C + c, m_, n_, cur[t], prev);
+            emit<IO, VEC, M>(out, plane, (row0 + t0 + t) * C + c, m_, n_, cur[t], prev);
             prev = cur[t];
         }
     } else {
         for (int64_t t = t0; t < T; ++t) {
-            const Vec<VEC> cur = vload<VEC>(x + (row0 + t) * C + c);
-            emit<VEC, M>(out, plane, (row0 + t) * C + c, m_, n_, cur, prev);
+            const Vec<VEC> cur = vload<IO, VEC>(x + (row0 + t) * C + c);
+            emit<IO, VEC, M>(out, plane, (row0 + t) * C + c, m_, n_, cur, prev);
             prev = cur;
         }
     }
-    if (write_last && x_prev_out && t0 + kTT >= T) vstore<VEC>(x_prev_out + bb * C + c, prev);
+    // (the carried token is an x row, so it is stored exactly)
+    if (write_last && x_prev_out && t0 + kTT >= T) vstore<IO, VEC>(x_prev_out + bb * C + c, prev);
 }
 
 // x_prev_out[b][c] <- x[b][T-1][c] (T > 0), or x_prev (zero when NULL) for T == 0.
+template <class IO>
 __global__ __launch_bounds__(256) void shift_last_kernel(int64_t B, int64_t T, int64_t C,
-                                                         const float *x, const float *x_prev,
-                                                         float *x_prev_out) {
+                                                         const typename IO::T *x,
+                                                         const typename IO::T *x_prev,
+                                                         typename IO::T *x_prev_out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= B * C) return;
     const int64_t bb = i / C, c = i - bb * C;
-    float val;
+    typename IO::T val;
     if (T > 0)
         val = x[(bb * T + T - 1) * C + c];
     else
-        val = x_prev ? x_prev[i] : 0.0f;
+        val = x_prev ? x_prev[i] : IO::from_f(0.0f);
     x_prev_out[i] = val;
 }
 
-template <int VEC, int M>
+template <class IO, int VEC, int M>
 hipError_t launch_shift_m(const ShiftArgs &a, uint32_t cblocks, uint32_t ntiles, int write_last,
                           hipStream_t st) {
+    using T = typename IO::T;
     const int64_t grid = (int64_t)cblocks * ntiles * a.B;
-    hipLaunchKernelGGL((shift_kernel<VEC, M>), dim3((unsigned)grid), dim3(256), 0, st, a.B, a.T,
-                       a.C, cblocks, ntiles, a.mu, a.x, a.x_prev, a.out, a.x_prev_out,
-                       write_last);
+    hipLaunchKernelGGL((shift_kernel<IO, VEC, M>), dim3((unsigned)grid), dim3(256), 0, st, a.B,
+                       a.T, a.C, cblocks, ntiles, a.mu, (const T *)a.x, (const T *)a.x_prev,
+                       (T *)a.out, (T *)a.x_prev_out, write_last);
     return hipGetLastError();
 }
 
-template <int VEC>
+template <class IO, int VEC>
 hipError_t launch_shift_vec(const ShiftArgs &a, uint32_t cblocks, uint32_t ntiles,
                             int write_last, hipStream_t st) {
     switch (a.M) {
-        case 1: return launch_shift_m<VEC, 1>(a, cblocks, ntiles, write_last, st);
-        case 2: return launch_shift_m<VEC, 2>(a, cblocks, ntiles, write_last, st);
-        case 3: return launch_shift_m<VEC, 3>(a, cblocks, ntiles, write_last, st);
-        case 4: return launch_shift_m<VEC, 4>(a, cblocks, ntiles, write_last, st);
-        case 5: return launch_shift_m<VEC, 5>(a, cblocks, ntiles, write_last, st);
-        case 6: return launch_shift_m<VEC, 6>(a, cblocks, ntiles, write_last, st);
-        case 7: return launch_shift_m<VEC, 7>(a, cblocks, ntiles, write_last, st);
-        case 8: return launch_shift_m<VEC, 8>(a, cblocks, ntiles, write_last, st);
+        case 1: return launch_shift_m<IO, VEC, 1>(a, cblocks, ntiles, write_last, st);
+        case 2: return launch_shift_m<IO, VEC, 2>(a, cblocks, ntiles, write_last, st);
+        case 3: return launch_shift_m<IO, VEC, 3>(a, cblocks, ntiles, write_last, st);
+        case 4: return launch_shift_m<IO, VEC, 4>(a, cblocks, ntiles, write_last, st);
+        case 5: return launch_shift_m<IO, VEC, 5>(a, cblocks, ntiles, write_last, st);
+        case 6: return launch_shift_m<IO, VEC, 6>(a, cblocks, ntiles, write_last, st);
+        case 7: return launch_shift_m<IO, VEC, 7>(a, cblocks, ntiles, write_last, st);
+        case 8: return launch_shift_m<IO, VEC, 8>(a, cblocks, ntiles, write_last, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -188,12 +230,15 @@ hipError_t launch_shift_vec(const ShiftArgs &a, uint32_t cblocks, uint32_t ntile
 constexpr int kBT = 64;  // tokens per wave
 constexpr int kBW = 4;   // waves per workgroup, stacked along the sequence
 
-template <int VEC, int M>
+// IO: element format of x, x_prev, d_out, d_xpo, dx and dxp (mu, dmu and the
+// partials are float32).
+template <class IO, int VEC, int M>
 __global__ __launch_bounds__(256) void shift_bwd_kernel(
     int64_t B, int64_t T, int64_t C, uint32_t cblocks, uint32_t nwt, const float *__restrict__ mu,
-    const float *__restrict__ x, const float *__restrict__ x_prev,
-    const float *__restrict__ dout, const float *__restrict__ dxpo, float *__restrict__ dx,
-    float *__restrict__ dxp, float *__restrict__ part) {
+    const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ x_prev,
+    const typename IO::T *__restrict__ dout, const typename IO::T *__restrict__ dxpo,
+    typename IO::T *__restrict__ dx, typename IO::T *__restrict__ dxp,
+    float *__restrict__ part) {
     __shared__ float red[kBW][M][64 * VEC];
     const uint32_t cb = blockIdx.x % cblocks;
     const uint32_t rest = blockIdx.x / cblocks;
@@ -217,12 +262,12 @@ __global__ __launch_bounds__(256) void shift_bwd_kernel(
         for (int m = 0; m < M; ++m) {
 #pragma unroll
             for (int i = 0; i < VEC; ++i) mu_[m].x[i] = mu[m * C + c + i];
-            dcur[m] = vload<VEC>(dout + m * plane + (bb * T + t0) * C + c);
+            dcur[m] = vload<IO, VEC>(dout + m * plane + (bb * T + t0) * C + c);
         }
         if (t0 > 0) {
-            xprev = vload<VEC>(x + (bb * T + t0 - 1) * C + c);
+            xprev = vload<IO, VEC>(x + (bb * T + t0 - 1) * C + c);
         } else if (x_prev) {
-            xprev = vload<VEC>(x_prev + bb * C + c);
+            xprev = vload<IO, VEC>(x_prev + bb * C + c);
         } else {
 #pragma unroll
             for (int i = 0; i < VEC; ++i) xprev.x[i] = 0.0f;
@@ -235,25 +280,25 @@ __global__ __launch_bounds__(256) void shift_bwd_kernel(
             for (int m = 0; m < M; ++m)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) g.x[i] = fmaf(1.0f - mu_[m].x[i], dcur[m].x[i], g.x[i]);
-            vstore<VEC>(dxp + bb * C + c, g);
+            vstore<IO, VEC>(dxp + bb * C + c, g);
         }
 #pragma unroll 4
         for (int64_t t = t0; t < t1; ++t) {
             const int64_t row = (bb * T + t) * C + c;
-            const Vec<VEC> xcur = vload<VEC>(x + row);
+            const Vec<VEC> xcur = vload<IO, VEC>(x + row);
             const bool more = t + 1 < T;
             Vec<VEC> dnext[M], g;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 if (more) {
-                    dnext[m] = vload<VEC>(dout + m * plane + row + C);
+                    dnext[m] = vload<IO, VEC>(dout + m * plane + row + C);
                 } else {
 #pragma unroll
                     for (int i = 0; i < VEC; ++i) dnext[m].x[i] = 0.0f;
                 }
             }
             if (!more && dxpo) {
-                g = vload<VEC>(dxpo + bb * C + c);
+                g = vload<IO, VEC>(dxpo + bb * C + c);
             } else {
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) g.x[i] = 0.0f;
@@ -267,7 +312,7 @@ __global__ __launch_bounds__(256) void shift_bwd_kernel(
                     acc[m].x[i] = fmaf(dc, xcur.x[i] - xprev.x[i], acc[m].x[i]);
                     dcur[m].x[i] = dn;
                 }
-            vstore<VEC>(dx + row, g);
+            vstore<IO, VEC>(dx + row, g);
             xprev = xcur;
         }
     }
@@ -303,116 +348,123 @@ __global__ __launch_bounds__(256) void shift_bwd_reduce_kernel(int64_t n_part, i
 
 // No mixes: dx is the carried token's gradient at T - 1 and zero elsewhere;
 // x_prev feeds nothing, so dx_prev is zero.
+template <class IO>
 __global__ __launch_bounds__(256) void shift_bwd_nomix_kernel(int64_t B, int64_t T, int64_t C,
-                                                              const float *dxpo, float *dx,
-                                                              float *dxp) {
+                                                              const typename IO::T *dxpo,
+                                                              typename IO::T *dx,
+                                                              typename IO::T *dxp) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < B * T * C) {
         const int64_t c = i % C, t = (i / C) % T, bb = i / (C * T);
-        dx[i] = (t == T - 1 && dxpo) ? dxpo[bb * C + c] : 0.0f;
+        dx[i] = (t == T - 1 && dxpo) ? dxpo[bb * C + c] : IO::from_f(0.0f);
     }
-    if (dxp && i < B * C) dxp[i] = 0.0f;
+    if (dxp && i < B * C) dxp[i] = IO::from_f(0.0f);
 }
 
 // No tokens: dx_prev = d_xpo (or 0) and dmu = 0.
+template <class IO>
 __global__ __launch_bounds__(256) void shift_bwd_empty_kernel(int64_t BC, int64_t MC,
-                                                              const float *dxpo, float *dxp,
-                                                              float *dmu) {
+                                                              const typename IO::T *dxpo,
+                                                              typename IO::T *dxp, float *dmu) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (dxp && i < BC) dxp[i] = dxpo ? dxpo[i] : 0.0f;
+    if (dxp && i < BC) dxp[i] = dxpo ? dxpo[i] : IO::from_f(0.0f);
     if (dmu && i < MC) dmu[i] = 0.0f;
 }
 
-template <int VEC, int M>
+template <class IO, int VEC, int M>
 hipError_t launch_shift_bwd_m(const ShiftBwdArgs &a, uint32_t cblocks, uint32_t nwt,
                               hipStream_t st) {
+    using T = typename IO::T;
     const int64_t grid = (int64_t)cblocks * nwt * a.B;
-    hipLaunchKernelGGL((shift_bwd_kernel<VEC, M>), dim3((unsigned)grid), dim3(256), 0, st, a.B,
-                       a.T, a.C, cblocks, nwt, a.mu, a.x, a.x_prev, a.d_out, a.d_xpo, a.dx,
-                       a.dxp, a.part);
+    hipLaunchKernelGGL((shift_bwd_kernel<IO, VEC, M>), dim3((unsigned)grid), dim3(256), 0, st,
+                       a.B, a.T, a.C, cblocks, nwt, a.mu, (const T *)a.x, (const T *)a.x_prev,
+                       (const T *)a.d_out, (const T *)a.d_xpo, (T *)a.dx, (T *)a.dxp, a.part);
     return hipGetLastError();
 }
 
-template <int VEC>
+template <class IO, int VEC>
 hipError_t launch_shift_bwd_vec(const ShiftBwdArgs &a, uint32_t cblocks, uint32_t nwt,
                                 hipStream_t st) {
     switch (a.M) {
-        case 1: return launch_shift_bwd_m<VEC, 1>(a, cblocks, nwt, st);
-        case 2: return launch_shift_bwd_m<VEC, 2>(a, cblocks, nwt, st);
-        case 3: return launch_shift_bwd_m<VEC, 3>(a, cblocks, nwt, st);
-        case 4: return launch_shift_bwd_m<VEC, 4>(a, cblocks, nwt, st);
+        case 1: return launch_shift_bwd_m<IO, VEC, 1>(a, cblocks, nwt, st);
+        case 2: return launch_shift_bwd_m<IO, VEC, 2>(a, cblocks, nwt, st);
+        case 3: return launch_shift_bwd_m<IO, VEC, 3>(a, cblocks, nwt, st);
+        case 4: return launch_shift_bwd_m<IO, VEC, 4>(a, cblocks, nwt, st);
         default: break;
     }
     if constexpr (VEC == 1) {
         switch (a.M) {
-            case 5: return launch_shift_bwd_m<1, 5>(a, cblocks, nwt, st);
-            case 6: return launch_shift_bwd_m<1, 6>(a, cblocks, nwt, st);
-            case 7: return launch_shift_bwd_m<1, 7>(a, cblocks, nwt, st);
-            case 8: return launch_shift_bwd_m<1, 8>(a, cblocks, nwt, st);
+            case 5: return launch_shift_bwd_m<IO, 1, 5>(a, cblocks, nwt, st);
+            case 6: return launch_shift_bwd_m<IO, 1, 6>(a, cblocks, nwt, st);
+            case 7: return launch_shift_bwd_m<IO, 1, 7>(a, cblocks, nwt, st);
+            case 8: return launch_shift_bwd_m<IO, 1, 8>(a, cblocks, nwt, st);
             default: break;
         }
     }
     return hipErrorInvalidValue;
 }
 
-}  // namespace
-
-int64_t shift_bwd_tiles(int64_t T) { return (T + kBW * kBT - 1) / (kBW * kBT); }
-
-// B*C > 0 here.  Four channels per lane when C and every pointer allow 16-byte
-// accesses and M <= 4 (the registers of more mixes would limit occupancy).
-hipError_t launch_token_shift_backward(const ShiftBwdArgs &a, hipStream_t st) {
+// The host side of both directions, for one element format.
+template <class IO>
+hipError_t token_shift_backward_io(const ShiftBwdArgs &a, hipStream_t st) {
+    using T = typename IO::T;
     const int64_t BC = a.B * a.C, MC = a.M * a.C;
     if (a.T == 0 || BC == 0) {
         // no tokens (or no lanes): dx_prev = d_xpo, dmu = 0
         const int64_t n = BC > MC ? BC : MC;
         if (n == 0) return hipSuccess;
         if ((n + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(shift_bwd_empty_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
-                           0, st, BC, MC, a.d_xpo, a.dxp, a.dmu);
+        hipLaunchKernelGGL(shift_bwd_empty_kernel<IO>, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), 0, st, BC, MC, (const T *)a.d_xpo, (T *)a.dxp, a.dmu);
         return hipGetLastError();
     }
     if (a.M == 0) {
         const int64_t n = a.B * a.T * a.C;
         if ((n + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(shift_bwd_nomix_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
-                           0, st, a.B, a.T, a.C, a.d_xpo, a.dx, a.dxp);
+        hipLaunchKernelGGL(shift_bwd_nomix_kernel<IO>, dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), 0, st, a.B, a.T, a.C, (const T *)a.d_xpo, (T *)a.dx,
+                           (T *)a.dxp);
         return hipGetLastError();
     }
-    const uintptr_t mis = (uintptr_t)a.mu | (uintptr_t)a.x | (uintptr_t)a.x_prev |
-                          (uintptr_t)a.d_out | (uintptr_t)a.d_xpo | (uintptr_t)a.dx |
-                          (uintptr_t)a.dxp;
-    const bool vec4 = (a.C % 4 == 0) && (mis % 16 == 0) && a.M <= 4;
+    // four channels per lane when C and every pointer allow 4-element accesses
+    // and M <= 4 (the registers of more mixes would limit occupancy)
+    const uintptr_t mis = (uintptr_t)a.x | (uintptr_t)a.x_prev | (uintptr_t)a.d_out |
+                          (uintptr_t)a.d_xpo | (uintptr_t)a.dx | (uintptr_t)a.dxp;
+    const bool vec4 = (a.C % 4 == 0) && (mis % (4 * IO::kBytes) == 0) &&
+                      ((uintptr_t)a.mu % 16 == 0) && a.M <= 4;
     const int64_t per_block = 64 * (vec4 ? 4 : 1);
     const int64_t cblocks = (a.C + per_block - 1) / per_block;
     const int64_t nwt = shift_bwd_tiles(a.T);
     if (cblocks > 0x7fffffffLL / nwt || cblocks * nwt > 0x7fffffffLL / a.B)
         return hipErrorInvalidConfiguration;
-    hipError_t e = vec4 ? launch_shift_bwd_vec<4>(a, (uint32_t)cblocks, (uint32_t)nwt, st)
-             : launch_shift_bwd_vec<1>(a, (uint32_t)cblocks, (uint32_t)nwt, st);
+    hipError_t e = vec4 ? launch_shift_bwd_vec<IO, 4>(a, (uint32_t)cblocks, (uint32_t)nwt, st)
+                        : launch_shift_bwd_vec<IO, 1>(a, (uint32_t)cblocks, (uint32_t)nwt, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(shift_bwd_reduce_kernel, dim3((unsigned)((MC + 255) / 256)), dim3(256), 0,
                        st, a.B * nwt, MC, a.part, a.dmu);
     return hipGetLastError();
 }
 
-// B*C > 0 here.  M == 0 or T == 0 only update x_prev_out.
-hipError_t launch_token_shift(const ShiftArgs &a, bool in_place_state, hipStream_t st) {
+template <class IO>
+hipError_t token_shift_io(const ShiftArgs &a, bool in_place_state, hipStream_t st) {
+    using T = typename IO::T;
     const int64_t lanes = a.B * a.C;
     const int64_t last_grid = (lanes + 255) / 256;
     if (last_grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     auto launch_last = [&]() {
-        hipLaunchKernelGGL(shift_last_kernel, dim3((unsigned)last_grid), dim3(256), 0, st, a.B,
-                           a.T, a.C, a.x, a.x_prev, a.x_prev_out);
+        hipLaunchKernelGGL(shift_last_kernel<IO>, dim3((unsigned)last_grid), dim3(256), 0, st,
+                           a.B, a.T, a.C, (const T *)a.x, (const T *)a.x_prev,
+                           (T *)a.x_prev_out);
         return hipGetLastError();
     };
     if (a.T == 0 || a.M == 0) {
         if (!a.x_prev_out || (a.T == 0 && in_place_state)) return hipSuccess;
         return launch_last();
     }
-    const uintptr_t mis = (uintptr_t)a.mu | (uintptr_t)a.x | (uintptr_t)a.x_prev |
-                          (uintptr_t)a.out | (uintptr_t)a.x_prev_out;
-    const bool vec4 = (a.C % 4 == 0) && (mis % 16 == 0);
+    const uintptr_t mis =
+        (uintptr_t)a.x | (uintptr_t)a.x_prev | (uintptr_t)a.out | (uintptr_t)a.x_prev_out;
+    const bool vec4 =
+        (a.C % 4 == 0) && (mis % (4 * IO::kBytes) == 0) && ((uintptr_t)a.mu % 16 == 0);
     const int64_t per_block = 256 * (vec4 ? 4 : 1);
     const int64_t cblocks = (a.C + per_block - 1) / per_block;
     const int64_t ntiles = (a.T + kTT - 1) / kTT;
@@ -423,10 +475,35 @@ hipError_t launch_token_shift(const ShiftArgs &a, bool in_place_state, hipStream
     // new state in a second launch instead.
     const bool late = a.x_prev_out && in_place_state && ntiles > 1;
     const int write_last = a.x_prev_out && !late ? 1 : 0;
-    hipError_t e = vec4 ? launch_shift_vec<4>(a, (uint32_t)cblocks, (uint32_t)ntiles, write_last, st)
-                        : launch_shift_vec<1>(a, (uint32_t)cblocks, (uint32_t)ntiles, write_last, st);
+    hipError_t e =
+        vec4 ? launch_shift_vec<IO, 4>(a, (uint32_t)cblocks, (uint32_t)ntiles, write_last, st)
+             : launch_shift_vec<IO, 1>(a, (uint32_t)cblocks, (uint32_t)ntiles, write_last, st);
     if (e != hipSuccess || !late) return e;
     return launch_last();
+}
+
+}  // namespace
+
+int64_t shift_bwd_tiles(int64_t T) { return (T + kBW * kBT - 1) / (kBW * kBT); }
+
+// B*C > 0 here (the backward also handles T == 0 and B*C == 0).
+hipError_t launch_token_shift_backward(const ShiftBwdArgs &a, hipStream_t st) {
+    switch (a.io) {
+        case kIoF32: return token_shift_backward_io<IoF32>(a, st);
+        case kIoF16: return token_shift_backward_io<IoF16>(a, st);
+        case kIoBF16: return token_shift_backward_io<IoBF16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// B*C > 0 here.  M == 0 or T == 0 only update x_prev_out.
+hipError_t launch_token_shift(const ShiftArgs &a, bool in_place_state, hipStream_t st) {
+    switch (a.io) {
+        case kIoF32: return token_shift_io<IoF32>(a, in_place_state, st);
+        case kIoF16: return token_shift_io<IoF16>(a, in_place_state, st);
+        case kIoBF16: return token_shift_io<IoBF16>(a, in_place_state, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace wkv

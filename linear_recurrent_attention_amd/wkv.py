@@ -44,7 +44,8 @@ EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backw
             "wkv_forward_gated", "wkv_step_gated", "wkv_token_shift", "wkv_forward_typed",
             "wkv_step_typed", "wkv_backward_state", "wkv_backward_typed",
             "wkv_forward_checkpointed", "wkv_backward_checkpointed", "wkv_backward_gated",
-            "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward")
+            "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward",
+            "wkv_token_shift_typed", "wkv_token_shift_backward_typed")
 
 # wkv_dtype values
 WKV_DTYPE_F32 = 0
@@ -127,6 +128,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_token_shift_backward_workspace_size.restype = sz
     lib.wkv_token_shift_backward.argtypes = [i64, i64, i64, i64] + [vp] * 8 + [vp, sz, vp]
     lib.wkv_token_shift_backward.restype = ctypes.c_int
+    lib.wkv_token_shift_typed.argtypes = [i64, i64, i64, i64, ctypes.c_int] + [vp] * 5 + [vp]
+    lib.wkv_token_shift_typed.restype = ctypes.c_int
+    lib.wkv_token_shift_backward_typed.argtypes = ([i64, i64, i64, i64, ctypes.c_int] +
+                                                   [vp] * 8 + [vp, sz, vp])
+    lib.wkv_token_shift_backward_typed.restype = ctypes.c_int
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -350,13 +356,24 @@ def wkv_token_shift(mu, x, x_prev=None, out=None, x_prev_out=None, stream=None):
         raise ValueError("x must be [B][T][C] and mu [M][C]")
     B, T, C = (int(a) for a in x.shape)
     M = int(mu.shape[0])
+    dt = x.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported element type {dt}")
     if out is None:
-        out = torch.empty((M, B, T, C), device=x.device, dtype=torch.float32)
+        out = torch.empty((M, B, T, C), device=x.device, dtype=dt)
     if x_prev_out is True:
-        x_prev_out = torch.empty((B, C), device=x.device, dtype=torch.float32)
-    st = load_library().wkv_token_shift(B, T, C, M, _ptr(mu), _ptr(x), _ptr(x_prev), _ptr(out),
-                                        _ptr(x_prev_out), _stream(stream))
-    _check("wkv_token_shift", st)
+        x_prev_out = torch.empty((B, C), device=x.device, dtype=dt)
+    lib = load_library()
+    if dt == torch.float32:
+        st = lib.wkv_token_shift(B, T, C, M, _ptr(mu), _ptr(x), _ptr(x_prev), _ptr(out),
+                                 _ptr(x_prev_out), _stream(stream))
+        _check("wkv_token_shift", st)
+    else:
+        # x, x_prev, out and x_prev_out in x's 16-bit format; mu float32
+        st = lib.wkv_token_shift_typed(B, T, C, M, _DTYPES[dt], _ptr(mu), _ptr(x, dt),
+                                       _ptr(x_prev, dt), _ptr(out, dt), _ptr(x_prev_out, dt),
+                                       _stream(stream))
+        _check("wkv_token_shift_typed", st)
     return out, x_prev_out
 
 
@@ -371,9 +388,12 @@ def wkv_token_shift_backward(mu, x, d_out, x_prev=None, d_x_prev_out=None, dx=No
     B, T, C = (int(a) for a in x.shape)
     M = int(mu.shape[0])
     dev = x.device
+    dt = x.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported element type {dt}")
     dx = torch.empty_like(x) if dx is None else dx
     if d_x_prev is True:
-        d_x_prev = torch.empty((B, C), device=dev, dtype=torch.float32)
+        d_x_prev = torch.empty((B, C), device=dev, dtype=dt)
     dmu = torch.empty((M, C), device=dev, dtype=torch.float32) if dmu is None else dmu
     lib = load_library()
     need = int(lib.wkv_token_shift_backward_workspace_size(B, T, C, M))
@@ -382,10 +402,19 @@ def wkv_token_shift_backward(mu, x, d_out, x_prev=None, d_x_prev_out=None, dx=No
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise TypeError("workspace must be a contiguous uint8 tensor")
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
-    st = lib.wkv_token_shift_backward(B, T, C, M, _ptr(mu), _ptr(x), _ptr(x_prev), _ptr(d_out),
-                                      _ptr(d_x_prev_out), _ptr(dx), _ptr(d_x_prev), _ptr(dmu),
-                                      ws_ptr, workspace.numel(), _stream(stream))
-    _check("wkv_token_shift_backward", st)
+    if dt == torch.float32:
+        st = lib.wkv_token_shift_backward(B, T, C, M, _ptr(mu), _ptr(x), _ptr(x_prev),
+                                          _ptr(d_out), _ptr(d_x_prev_out), _ptr(dx),
+                                          _ptr(d_x_prev), _ptr(dmu), ws_ptr, workspace.numel(),
+                                          _stream(stream))
+        _check("wkv_token_shift_backward", st)
+    else:
+        # x, x_prev, the gradients in and dx, d_x_prev out in x's format
+        st = lib.wkv_token_shift_backward_typed(
+            B, T, C, M, _DTYPES[dt], _ptr(mu), _ptr(x, dt), _ptr(x_prev, dt), _ptr(d_out, dt),
+            _ptr(d_x_prev_out, dt), _ptr(dx, dt), _ptr(d_x_prev, dt), _ptr(dmu), ws_ptr,
+            workspace.numel(), _stream(stream))
+        _check("wkv_token_shift_backward_typed", st)
     return dx, d_x_prev, dmu
 
 

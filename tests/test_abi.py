@@ -280,6 +280,32 @@ def test_token_shift_backward_rejects_invalid_arguments(lib):
     assert call(ws=vp(P + 3 * 0x10000000 + 4)) == W.WKV_ERR_ALIAS        # workspace over d_out
 
 
+def test_typed_token_shift_calls_reject_invalid_arguments(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    vp = ctypes.c_void_p
+    mu, x, xp, out, xpo = (vp(P + i * 0x10000000) for i in range(5))
+    f = lib.wkv_token_shift_typed
+    assert f(2, 8, 16, 3, 7, mu, x, xp, out, xpo, None) == W.WKV_ERR_UNSUPPORTED
+    assert f(2, 8, 16, 9, W.WKV_DTYPE_BF16, mu, x, xp, out, xpo, None) == W.WKV_ERR_UNSUPPORTED
+    assert f(2, 8, 16, 3, W.WKV_DTYPE_BF16, mu, None, xp, out, xpo, None) == W.WKV_ERR_NULL
+    # 2 x 8 x 16 bf16 elements are 512 bytes: out 500 bytes into x overlaps it
+    assert f(2, 8, 16, 3, W.WKV_DTYPE_BF16, mu, x, xp, vp(P + 0x10000000 + 500), xpo,
+             None) == W.WKV_ERR_ALIAS
+    # the carried token is 2 x 16 bf16 = 64 bytes: x_prev_out 32 bytes into x_prev
+    assert f(2, 8, 16, 3, W.WKV_DTYPE_F16, mu, x, xp, out, vp(P + 2 * 0x10000000 + 32),
+             None) == W.WKV_ERR_ALIAS
+    g = lib.wkv_token_shift_backward_typed
+    need = lib.wkv_token_shift_backward_workspace_size(2, 100, 64, 3)
+    d, dxpo, dx, dxp, dmu, ws = (vp(P + (5 + i) * 0x10000000) for i in range(6))
+    assert g(2, 100, 64, 3, 4, mu, x, xp, d, dxpo, dx, dxp, dmu, ws, need, None) == \
+        W.WKV_ERR_UNSUPPORTED
+    # dx 2 x 100 x 64 bf16 = 25,600 bytes: x placed just below dx overlaps it
+    assert g(2, 100, 64, 3, W.WKV_DTYPE_BF16, mu, vp(P + 7 * 0x10000000 - 25000), xp, d, dxpo,
+             dx, dxp, dmu, ws, need, None) == W.WKV_ERR_ALIAS
+    assert g(2, 100, 64, 3, W.WKV_DTYPE_BF16, mu, x, xp, d, dxpo, dx, dxp, dmu, ws, need - 1,
+             None) == W.WKV_ERR_WORKSPACE
+
+
 def test_forward_ex_rejects_unknown_plans(lib):
     from linear_recurrent_attention_amd import wkv as W
     vp = ctypes.c_void_p
