@@ -704,11 +704,11 @@ def bench_shift(args, torch, wkv, synth, backward: bool = False):
         # x and the M mix gradients in, dx out; mu in, dmu out; the carried
         # token's gradient in, d_x_prev out
         algo = (8 + 4 * M) * elems + 8 * M * C + 8 * B * C
-        kname = f"shift_bwd_kernel<4, {M}>"
+        kname = f"shift_bwd_kernel<wkv::IoF32, 4, {M}>"
     else:
         # x in, M outputs out; mu; carried token in and out
         algo = (4 + 4 * M) * elems + 4 * M * C + 8 * B * C
-        kname = f"shift_kernel<4, {M}>"
+        kname = f"shift_kernel<wkv::IoF32, 4, {M}>"
     wl = "token_shift_bwd" if backward else "token_shift"
     cpu = None
     if not args.no_cpu_baseline:
