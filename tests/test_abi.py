@@ -407,6 +407,19 @@ def test_binding_fails_loudly_without_library(tmp_path):
             wkv._lib = wkv._lib_saved
 
 
+def test_autograd_functions_refuse_host_tensors(lib):
+    """The differentiable wrappers marshal arguments only: host tensors are
+    refused before any call, with no CPU fallback."""
+    import torch
+    from linear_recurrent_attention_amd.autograd import token_shift, wkv_time_mix
+    w, u = torch.ones(8), torch.zeros(8)
+    k = torch.zeros(1, 4, 8, requires_grad=True)
+    with pytest.raises(TypeError, match="HIP device"):
+        wkv_time_mix(w, u, k, torch.zeros(1, 4, 8))
+    with pytest.raises(TypeError, match="HIP device"):
+        token_shift(torch.full((3, 8), 0.5), torch.zeros(1, 4, 8))
+
+
 def test_auto_plan_follows_its_thresholds(lib):
     """The automatic kernel choice is host arithmetic (with 256 CUs when no
     device answers): lane kernel for T <= 16 or for >= 131072 lanes with
