@@ -15,7 +15,8 @@ sigmoid(r) * wkv of the deep dive's "RWKV architecture overview" block figure.
 
 Everything runs in libwkv's kernels.  The only work here is choosing the
 entry point, making tensors contiguous and allocating outputs; there is no
-fallback.
+fallback.  The backward is a kernel call, so it is differentiable once: a
+second derivative raises.
 
 The state's gradient: whatever consumes state_out sees only its true sums
 A = a e^o and B = b e^o.  So the gradient of state_out flows through its a and
@@ -28,6 +29,7 @@ o plane other than through A and B is outside this contract.
 from __future__ import annotations
 
 import torch
+from torch.autograd.function import once_differentiable
 
 from . import wkv as _w
 
@@ -57,6 +59,7 @@ class WkvFunction(torch.autograd.Function):
         return y, s_out
 
     @staticmethod
+    @once_differentiable
     def backward(ctx, dy, d_state_out):
         w, u, k, v, r, s_in, s_out, ck = ctx.saved_tensors
         dy = torch.zeros_like(k) if dy is None else dy.to(k.dtype).contiguous()
@@ -95,6 +98,7 @@ class TokenShiftFunction(torch.autograd.Function):
         return out, xpo
 
     @staticmethod
+    @once_differentiable
     def backward(ctx, d_out, d_x_prev_out):
         mu, x, xp = ctx.saved_tensors
         M, (B, T, C) = mu.shape[0], x.shape
