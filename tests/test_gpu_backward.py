@@ -73,6 +73,38 @@ def test_extreme_bonus_backward(oracle):
     check(g, r, d)
 
 
+@pytest.mark.parametrize("recipe", [synth.GPT, synth.STABILITY])
+def test_extreme_decay_backward(oracle, recipe):
+    """Per-channel decay rates spread geometrically from 1e-6 (nothing decays
+    over the sequence) to 60 (the past vanishes within two tokens): the plain
+    backward, the backward from the GPU forward's checkpoints and the gated
+    backward, against the oracle."""
+    B, T, C = 2, 600, 96
+    d = synth.make(recipe, index=8, B=B, T=T, C=C, with_dy=True)
+    d["w"] = torch.from_numpy(np.geomspace(1e-6, 60.0, C).astype(np.float32))
+    note(f"backward extreme decay recipe={recipe}")
+    check(gpu_grads(d), oracle.backward_scan(*(f64(d[n]) for n in ("w", "u", "k", "v", "dy"))), d)
+    dev = torch.device("cuda")
+    w, u, k, v, dy = (d[n].to(dev) for n in ("w", "u", "k", "v", "dy"))
+    _, _, ck = wkv.wkv_forward_checkpointed(w, u, k, v)
+    g = [f64(t) for t in wkv.wkv_backward_checkpointed(w, u, k, v, dy, ck)[:4]]
+    torch.cuda.synchronize()
+    check(g, oracle.backward_scan(*(f64(d[n]) for n in ("w", "u", "k", "v", "dy"))), d)
+    # gated: the recurrence receives g = dy sigmoid(r)
+    r = synth.receptance(recipe, 8, (B, T, C))
+    dk, dv, dr, dw, du, _ = wkv.wkv_backward_gated(w, u, k, v, r.to(dev), dy, checkpoints=ck)
+    torch.cuda.synchronize()
+    a = [f64(d[n]) for n in ("w", "u", "k", "v")]
+    y, _ = oracle.forward_scan(*a)
+    gg, dr_ref = oracle.gate_backward(y, f64(r), f64(d["dy"]))
+    ref = oracle.backward_scan(*a, gg)
+    v64 = f64(d["v"])
+    for name, x, rr in (("dk", dk, ref[0]), ("dv", dv, ref[1]), ("dr", dr, dr_ref),
+                        ("dw", dw, ref[2]), ("du", du, ref[3])):
+        assert_grad_close(f64(x), rr, f"gated {name}",
+                          roundoff_floor(gg, v64, summed=name in ("dw", "du")))
+
+
 def test_empty_backward():
     dev = torch.device("cuda")
     C = 33

@@ -307,6 +307,27 @@ def test_backward_brute_equals_scan(oracle, seed):
         np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12 * (1 + np.abs(b).max()))
 
 
+def test_backward_brute_equals_scan_at_extreme_decays(oracle):
+    """Decay rates from 1e-6 (no decay over the sequence) to 60 (the past
+    vanishes within two tokens): the O(T) scan still equals the O(T^2) closed
+    form, and dw equals central differences of the loss."""
+    d = synth.make(synth.STABILITY, index=8, B=2, T=60, C=12, with_dy=True)
+    d = {n: t.double().numpy() for n, t in d.items()}
+    w = np.geomspace(1e-6, 60.0, 12)
+    gb = oracle.backward_brute(w, d["u"], d["k"], d["v"], d["dy"])
+    gs = oracle.backward_scan(w, d["u"], d["k"], d["v"], d["dy"])
+    for a, b in zip(gs, gb):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12 * (1 + np.abs(b).max()))
+    for c in (0, 5, 11):
+        h = 1e-6 * max(1.0, w[c])
+        wp, wm = w.copy(), w.copy()
+        wp[c] += h
+        wm[c] -= h
+        ref = (_loss(oracle, wp, d["u"], d["k"], d["v"], d["dy"]) -
+               _loss(oracle, wm, d["u"], d["k"], d["v"], d["dy"])) / (2 * h)
+        assert abs(gs[2][c] - ref) <= 1e-6 * max(1e-3, np.abs(gs[2]).max()), (c, gs[2][c], ref)
+
+
 @pytest.mark.parametrize("outlier", [False, True])
 def test_backward_matches_finite_differences(oracle, outlier):
     """Central differences of L = sum dy*y on a B=1, T=32, C=8 slice of the
