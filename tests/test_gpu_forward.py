@@ -113,6 +113,23 @@ def test_wide_exponents_match_oracle(oracle, plan):
     assert_state_close(f64(so), sr)
 
 
+@pytest.mark.parametrize("plan", list(PLANS))
+@pytest.mark.parametrize("with_state", [False, True])
+def test_extreme_decays_match_oracle(oracle, plan, with_state):
+    """Decay rates spread geometrically from 1e-6 (nothing decays over the
+    sequence) to 60 (the past vanishes within two tokens), stability keys."""
+    B, T, C = 2, 700, 96
+    d = synth.make(synth.STABILITY, index=9, B=B, T=T, C=C)
+    d["w"] = torch.from_numpy(np.geomspace(1e-6, 60.0, C).astype(np.float32))
+    si = reachable_state(oracle, B, C, 9) if with_state else None
+    note(f"extreme decays plan={plan} state={with_state}")
+    y, so = run(d, PLANS[plan], si)
+    yr, sr = oracle.forward_scan(*(f64(d[n]) for n in ("w", "u", "k", "v")),
+                                 None if si is None else si.double().numpy(), nthreads=NTHREADS)
+    assert_y_close(f64(y), yr)
+    assert_state_close(f64(so), sr)
+
+
 @pytest.mark.parametrize("plan", ["lane", "seg16x16", "seg8x32", "seg32x8c16", "lb4x16",
                                   "lb4x16c128"])
 def test_extreme_bonus_takes_the_two_exponential_path(oracle, plan):
