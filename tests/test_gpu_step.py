@@ -67,6 +67,33 @@ def test_steps_match_oracle(oracle, shape):
         assert_state_close(f64(st[l]), sr, f"state layer {l}")
 
 
+def test_steps_at_extreme_decays_match_oracle(oracle):
+    """Decay rates from 1e-6 to 60 across the channels of every layer, bonus
+    from -70 to +75: 40 steps from oracle states, state updated in place."""
+    L, B, C = 2, 3, 96
+    dev = torch.device("cuda")
+    w = torch.from_numpy(np.geomspace(1e-6, 60.0, C).astype(np.float32)).repeat(L, 1)
+    u = torch.from_numpy(np.linspace(-70.0, 75.0, C).astype(np.float32))[torch.randperm(
+        C, generator=torch.Generator().manual_seed(5))].repeat(L, 1)
+    s0 = oracle_states(oracle, L, B, C, 3)
+    st = s0.to(dev).clone()
+    ks, vs, ys = [], [], []
+    note("step extreme decays")
+    for r in range(40):
+        k, v = synth.sequence(synth.DECODE, 300 + r, (L, B, C))
+        y, _ = wkv.wkv_step(w.to(dev), u.to(dev), k.to(dev), v.to(dev), st)
+        ks.append(k)
+        vs.append(v)
+        ys.append(y.cpu())
+    torch.cuda.synchronize()
+    for l in range(L):
+        k = torch.stack([x[l] for x in ks], dim=1)
+        v = torch.stack([x[l] for x in vs], dim=1)
+        yr, sr = oracle.forward_scan(f64(w[l]), f64(u[l]), f64(k), f64(v), f64(s0[l]))
+        assert_y_close(f64(torch.stack([x[l] for x in ys], dim=1)), yr, f"y layer {l}")
+        assert_state_close(f64(st[l]), sr, f"state layer {l}")
+
+
 def test_step_equals_forward_with_one_token(oracle):
     L, B, C = 3, 8, 256
     dev = torch.device("cuda")
