@@ -32,10 +32,20 @@
  *       w, u, dw, du        : [C]             (wkv_step: w, u are [L][C])
  *       state               : [3][B][C]       planes a, b, o
  *                                             (wkv_step: [L][3][B][C])
- *   - The library owns nothing of the caller's; it may keep one small internal
- *     scratch buffer per (device, stream) for cross-workgroup scan state,
- *     allocated on the first call that needs it and kept until the process
- *     ends.  The backward takes its scratch from the caller (workspace).
+ *   - The library owns nothing of the caller's.  The backward and the token
+ *     shift's backward take their scratch from the caller (workspace).  The
+ *     forward's look-back kernel keeps one scratch buffer per (device, stream)
+ *     for the states that workgroups pass along a sequence: the forward's
+ *     signature (wkv_forward(B,T,C,w,u,k,v,y,state_in,state_out)) has no
+ *     workspace argument.  That buffer holds a 256-byte header and two slot
+ *     arrays of 2 KiB per (block, sequence, 64-channel group), for example
+ *     8 MiB at B=8 T=1024 C=2048, at most 256 MiB (longer shapes use a kernel
+ *     that needs none).  It is allocated in stream order (hipMallocAsync) on
+ *     the first call that needs it, grown in stream order (the old buffer is
+ *     released with hipFreeAsync after the launches already queued on the
+ *     stream, so no call blocks the host or the device), and kept until
+ *     wkv_release_stream_scratch(stream) or the end of the process; a caller
+ *     that cycles through many streams releases each one it retires.
  *
  * Execution
  *   - Every call is asynchronous on `stream` (0 = the default stream) and
@@ -62,8 +72,13 @@
  *     inputs; NaN and Inf propagate.
  *   - No C++ exception crosses this interface.
  *   - The library keeps no mutable global state other than its per-device
- *     caches, which are guarded by a mutex; calls may come from several
- *     threads.
+ *     caches, the per-stream scratch above and the look-back spin limit, all
+ *     guarded (a mutex, an atomic); calls may come from several threads.
+ *   - The look-back kernel relies on the hardware dispatching workgroups in
+ *     index order (it does; HIP does not promise it).  Each of its waits is
+ *     bounded: past the bound the wait gives up, that block's outputs, every
+ *     later block's outputs of the same sequence and the state handed on are
+ *     NaN, and wkv_lookback_status reports WKV_ERR_LOOKBACK for the stream.
  */
 #ifndef LIBWKV_WKV_H
 #define LIBWKV_WKV_H
@@ -87,7 +102,8 @@ typedef enum wkv_status {
     WKV_ERR_ALIAS = 4,
     WKV_ERR_WORKSPACE = 5,
     WKV_ERR_UNSUPPORTED = 6,
-    WKV_ERR_HIP = 7
+    WKV_ERR_HIP = 7,
+    WKV_ERR_LOOKBACK = 8  /* reported by wkv_lookback_status only */
 } wkv_status;
 
 /*
@@ -522,6 +538,40 @@ WKV_API wkv_status wkv_token_shift_backward_typed(int64_t B, int64_t T, int64_t 
                                                   void *dx, void *d_x_prev, float *dmu,
                                                   void *workspace, size_t workspace_bytes,
                                                   hipStream_t stream);
+
+/*
+ * Bytes of look-back scratch wkv_forward would use for this shape on the
+ * current device (0 when its kernel needs none, or for an invalid shape).
+ */
+WKV_API size_t wkv_forward_scratch_size(int64_t B, int64_t T, int64_t C);
+
+/*
+ * Releases the look-back scratch the library keeps for `stream` on the current
+ * device, in stream order (hipFreeAsync on `stream`), so that launches already
+ * queued on it finish first.  The next look-back forward on that stream
+ * allocates a fresh buffer.  `stream` must still be valid.  Returns WKV_OK
+ * (also when there is none) or WKV_ERR_HIP.
+ */
+WKV_API wkv_status wkv_release_stream_scratch(hipStream_t stream);
+
+/*
+ * Synchronises `stream`, then reports whether any look-back wait of a forward
+ * on this stream (on the current device) gave up since the last call:
+ * WKV_ERR_LOOKBACK if one did (those launches' outputs from the stalled block
+ * on, and their state_out, are NaN), WKV_OK if none did, WKV_ERR_HIP on a
+ * runtime error.  Clears the record.  Forwards are asynchronous, so this is
+ * the only place the condition can be returned as a status.
+ */
+WKV_API wkv_status wkv_lookback_status(hipStream_t stream);
+
+/*
+ * Test hook: the number of look-back rounds without progress after which a
+ * wait gives up (default 65536, tens of milliseconds).  Returns the previous
+ * value.  Applies to launches issued after the call, from every thread.  A
+ * limit of 0 makes every wait that finds no predecessor ready give up at once,
+ * which exercises the give-up path while every workgroup still exits normally.
+ */
+WKV_API uint32_t wkv_set_lookback_spin_limit(uint32_t rounds);
 
 #ifdef __cplusplus
 }

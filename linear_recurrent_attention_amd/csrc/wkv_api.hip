@@ -4,6 +4,7 @@
 // invalid call returns its status without a launch (and without needing a
 // device).  The kernels live in wkv_forward.hip, wkv_step.hip and
 // wkv_backward.hip.
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <new>
@@ -43,35 +44,52 @@ bool overlap(Range a, Range b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-// Cached per-device facts (compute-unit count), guarded by a mutex.
-struct DeviceInfo {
-    int cus = 0;
-};
+// Cached per-device facts (compute-unit count), guarded by a mutex.  Fixed
+// arrays indexed by device, so that no call ever allocates host memory for
+// them.
+constexpr int kMaxDevices = 64;
 std::mutex g_mu;
-std::vector<DeviceInfo> g_dev;
+int g_cus[kMaxDevices] = {};
 
 int device_cus() {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
     std::lock_guard<std::mutex> lk(g_mu);
-    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
-    if (g_dev[dev].cus == 0) {
+    if (g_cus[dev] == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        g_dev[dev].cus = n;
+        g_cus[dev] = n;
     }
-    return g_dev[dev].cus;
+    return g_cus[dev];
 }
 
-// Scratch of the look-back forward, one buffer per (device, stream) so that
-// calls on different streams never share it.  Allocated and zeroed on first
-// use, grown (after draining the stream) when a larger shape needs more, and
-// kept until the process ends.  Every launch gets a fresh epoch, which tags
-// the states it publishes; the epoch advances only when a launch was
-// accepted, under the same lock as the launch itself, so launches from several
-// host threads onto one stream stay consistent.
+// Look-back rounds without progress before a wait gives up (a test hook can
+// lower it, see wkv_set_lookback_spin_limit).
+std::atomic<uint32_t> g_spin_limit{wkv::kDefaultSpinLimit};
+
+// Advances a scratch buffer's epoch after an accepted launch.  At the end of
+// the 30-bit tag range the slots (not the header) are cleared by a kernel
+// queued on the stream, so that no stale tag can match a reused epoch.
+hipError_t advance_epoch(void *p, size_t bytes, uint32_t &epoch, hipStream_t st) {
+    if (++epoch <= 0x3fffffffu) return hipSuccess;
+    epoch = 1;
+    return wkv::launch_zero_fill((char *)p + wkv::kLookbackHeaderBytes,
+                                 bytes - wkv::kLookbackHeaderBytes, st);
+}
+
+// Scratch of the look-back forward owned by the library: one buffer per
+// (device, stream), so that calls on different streams never share it.  It is
+// allocated on first use and grown, without blocking the host or the device,
+// in stream order: the new buffer comes from hipMallocAsync and is zeroed by a
+// kernel on the stream, the old one's give-up count is carried over and the
+// old buffer released with hipFreeAsync after the launches already queued on
+// the stream.  A buffer is kept until wkv_release_stream_scratch or the end of
+// the process; its size is bounded by kLookbackScratchMax.  Every launch gets
+// a fresh epoch, which tags the states it publishes; the epoch advances only
+// when a launch was accepted, under the same lock as the launch itself, so
+// launches from several host threads onto one stream stay consistent.
 struct Scratch {
     void *p = nullptr;
     size_t bytes = 0;
@@ -87,27 +105,42 @@ hipError_t launch_with_scratch(const FwdArgs &a, int cg, int ns, int ls, size_t 
     std::lock_guard<std::mutex> lk(g_mu);
     Scratch &s = g_scratch[std::make_pair(dev, st)];
     if (s.bytes < need) {
-        if (s.p) {
-            // a launch still queued on this stream may use the old buffer
-            if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-            if ((e = hipFree(s.p)) != hipSuccess) return e;
-            s.p = nullptr;
-            s.bytes = 0;
-        }
         const size_t bytes = need < ((size_t)4 << 20) ? ((size_t)4 << 20) : need;
-        if ((e = hipMalloc(&s.p, bytes)) != hipSuccess) return e;
-        if ((e = hipMemsetAsync(s.p, 0, bytes, st)) != hipSuccess) return e;
+        void *np = nullptr;
+        if ((e = hipMallocAsync(&np, bytes, st)) != hipSuccess) return e;
+        if ((e = wkv::launch_zero_fill(np, bytes, st)) != hipSuccess) {
+            (void)hipFreeAsync(np, st);
+            return e;
+        }
+        if (s.p) {
+            if ((e = hipMemcpyAsync(np, s.p, sizeof(uint32_t), hipMemcpyDeviceToDevice, st)) !=
+                    hipSuccess ||
+                (e = hipFreeAsync(s.p, st)) != hipSuccess) {
+                (void)hipFreeAsync(np, st);
+                return e;
+            }
+        }
+        s.p = np;
         s.bytes = bytes;
-    }
-    const wkv::LookbackScratch sc{s.p, s.epoch};
-    e = wkv::launch_forward_lookback(a, cg, ns, ls, sc, st);
-    if (e == hipSuccess && ++s.epoch > 0x3fffffffu) {
-        // end of the 30-bit tag range: clear the slots, so that no stale tag
-        // can match a reused epoch
-        if ((e = hipMemsetAsync(s.p, 0, s.bytes, st)) != hipSuccess) return e;
         s.epoch = 1;
     }
+    const wkv::LookbackScratch sc{s.p, s.epoch, g_spin_limit.load()};
+    e = wkv::launch_forward_lookback(a, cg, ns, ls, sc, st);
+    if (e == hipSuccess) e = advance_epoch(s.p, s.bytes, s.epoch, st);
     return e;
+}
+
+// Reads and clears the give-up count in the header at p (synchronous).
+hipError_t take_giveups(void *p, uint32_t *count) {
+    uint32_t c = 0;
+    hipError_t e = hipMemcpy(&c, p, sizeof c, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    if (c) {
+        const uint32_t zero = 0;
+        if ((e = hipMemcpy(p, &zero, sizeof zero, hipMemcpyHostToDevice)) != hipSuccess) return e;
+    }
+    *count += c;
+    return hipSuccess;
 }
 
 // Largest look-back scratch a call may ask for; longer sequences use the
@@ -461,6 +494,8 @@ WKV_API const char *wkv_status_string(wkv_status s) {
         case WKV_ERR_WORKSPACE: return "workspace missing or too small";
         case WKV_ERR_UNSUPPORTED: return "no compiled kernel for this plan or shape";
         case WKV_ERR_HIP: return "HIP runtime or launch error";
+        case WKV_ERR_LOOKBACK:
+            return "a look-back wait gave up: the affected forward outputs and states are NaN";
         default: return "unknown status";
     }
 }
@@ -641,5 +676,37 @@ WKV_API wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype
                          dk, dv, dw, du, d_state_in, workspace, workspace_bytes, stream,
                          checkpoints != nullptr, checkpoints, true, r, dr);
 }
+
+WKV_API size_t wkv_forward_scratch_size(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0 || bytes_of(B, T, C) < 0 || B * C == 0 || T == 0) return 0;
+    const wkv_forward_plan p = auto_plan(B, T, C, device_cus());
+    if (p.kernel != WKV_KERNEL_LOOKBACK) return 0;
+    return wkv::lookback_scratch_bytes(B, T, C, p.segments, p.seg_len);
+}
+
+WKV_API wkv_status wkv_release_stream_scratch(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return WKV_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_scratch.find(std::make_pair(dev, stream));
+    if (it == g_scratch.end()) return WKV_OK;
+    const hipError_t e = it->second.p ? hipFreeAsync(it->second.p, stream) : hipSuccess;
+    g_scratch.erase(it);
+    return from_hip(e);
+}
+
+WKV_API wkv_status wkv_lookback_status(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return WKV_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return WKV_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    uint32_t count = 0;
+    auto it = g_scratch.find(std::make_pair(dev, stream));
+    if (it != g_scratch.end() && it->second.p && take_giveups(it->second.p, &count) != hipSuccess)
+        return WKV_ERR_HIP;
+    return count ? WKV_ERR_LOOKBACK : WKV_OK;
+}
+
+WKV_API uint32_t wkv_set_lookback_spin_limit(uint32_t rounds) { return g_spin_limit.exchange(rounds); }
 
 }  // extern "C"

@@ -453,6 +453,20 @@ hipError_t launch_forward_seg(const FwdArgs &a, int nseg, int ls, int cw, hipStr
     return hipErrorInvalidValue;
 }
 
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        p[i] = 0u;
+}
+
+hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t st) {
+    const size_t n = bytes / 4;
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256),
+                       0, st, (uint32_t *)p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_state_copy(int64_t lanes, const float *s_in, float *s_out, hipStream_t st) {
     const int64_t grid = (3 * lanes + 255) / 256;
     hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)grid), dim3(256), 0, st, lanes, s_in,

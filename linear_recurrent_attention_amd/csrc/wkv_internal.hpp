@@ -83,17 +83,29 @@ bool forward_seg_supported(int nseg, int ls, int cw, int io);
 hipError_t launch_forward_seg(const FwdArgs &a, int nseg, int ls, int cw, hipStream_t st);
 hipError_t launch_state_copy(int64_t lanes, const float *s_in, float *s_out, hipStream_t st);
 
+// Fills n bytes (a multiple of 4) with zeros with a kernel on st (wkv_forward.hip).
+hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t st);
+
 // forward with decoupled look-back (wkv_lookback.hip)
+// The scratch starts with a header of kLookbackHeaderBytes: a 32-bit count of
+// look-back waits that gave up (the kernel adds to it; the host reads and
+// clears it), then the slot arrays.
+constexpr size_t kLookbackHeaderBytes = 256;
 struct LookbackScratch {
-    void *base;      // zero-initialised when allocated
-    uint32_t epoch;  // distinct for every launch on it, never 0
+    void *base;           // header then slots; zero-initialised before first use
+    uint32_t epoch;       // distinct for every launch on it, never 0
+    uint32_t spin_limit;  // look-back rounds without progress before a wait gives up
 };
+// Default spin limit: 2^16 rounds of a sleep and a device-scope load, tens of
+// milliseconds, far above any wait in a healthy launch.
+constexpr uint32_t kDefaultSpinLimit = 1u << 16;
 // (cg, ns, ls): groups of 64 channels side by side, segments stacked, tokens
 // per segment
 // (the gated kernel is compiled for the variants with ls <= 16 only, and the
 // 16-bit formats for the variants the automatic choice uses)
 bool forward_lookback_supported(int cg, int ns, int ls, bool gated, int io);
 bool lookback_grid_ok(int64_t B, int64_t T, int64_t C, int cg, int ns, int ls);
+// bytes of scratch a look-back launch needs, the header included
 size_t lookback_scratch_bytes(int64_t B, int64_t T, int64_t C, int ns, int ls);
 hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,
                                    const LookbackScratch &sc, hipStream_t st);

@@ -38,9 +38,12 @@
 // blocks < j.  A workgroup waits only on
 // blocks before its own, so the earliest unfinished workgroup never waits on
 // one that has not started, and the look-back always terminates.  The host
-// gives each launch a fresh epoch (per stream), so nothing on the device has to
-// be reset between launches.  Every spin is bounded as well: past the bound the
-// affected outputs become NaN instead of the kernel hanging.
+// gives each launch a fresh epoch (per scratch buffer), so nothing on the
+// device has to be reset between launches.  Every spin is bounded as well:
+// past the bound the wait gives up, the block's outputs become NaN, the
+// inclusive state it publishes carries the NaN to every later block of the
+// sequence and to the final state, and a counter in the scratch header records
+// the event for the host.
 #include "wkv_device.hpp"
 #include "wkv_internal.hpp"
 
@@ -50,7 +53,6 @@ namespace {
 
 constexpr uint32_t kAgg = 1u;   // block aggregate published
 constexpr uint32_t kIncl = 2u;  // inclusive state (after the block) published
-constexpr uint32_t kMaxSpin = 1u << 16;
 
 // One published state: [4][64] tagged words (a, b, e0, n per lane).
 using Word = unsigned long long;
@@ -125,6 +127,7 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
                                         typename IO::T *yseq, const float *__restrict__ s_in,
                                         float *__restrict__ s_out, float *__restrict__ ck,
                                         Word *aggs, Word *incls, uint32_t epoch,
+                                        uint32_t *giveups, uint32_t spin_limit,
                                         LbShared<CG, NS> &sh) {
     constexpr int TB = NS * LS;
     const int lane = q.lane, g = q.g, s = q.s;
@@ -136,11 +139,29 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
 
     // K holds the keys in log2 units (k log2 e)
 
-    // (1) segment summary from the empty state, shared through LDS
+    // (1) segment summary from the empty state, shared through LDS.  On a
+    // whole block it is taken in one frame: the largest decayed exponent
+    // x_t = K_t - (LS-1-t) W of the segment at its last token, so that each
+    // token costs one exponential and no rescaling (the sums are anchored at
+    // that exponent with no decay steps yet).
     Lane S = lane_empty();
+    if constexpr (FULL) {
+        float M = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < LS; ++t)
-        if (FULL || q.t0 + t < T) absorb(S, K[t], V[t], ch);
+        for (int t = 0; t < LS; ++t) M = fmaxf(M, fmaf((float)(t - (LS - 1)), ch.W, K[t]));
+        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int t = 0; t < LS; ++t) {
+            const float e = ex2(fmaf((float)(t - (LS - 1)), ch.W, K[t]) - M);
+            sa = fmaf(e, V[t], sa);
+            sb += e;
+        }
+        S = Lane{sa, sb, M, 0.0f};
+    } else {
+#pragma unroll
+        for (int t = 0; t < LS; ++t)
+            if (q.t0 + t < T) absorb(S, K[t], V[t], ch);
+    }
     lds_put(sh.s, s, g, lane, S);
     __syncthreads();
     // the block's aggregate (the summaries stay in LDS: the segment prefixes
@@ -212,7 +233,7 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
                 base -= use;
                 if (base < 0) done = true;
                 if (!done && use == 0) {
-                    if (++spins > kMaxSpin) {
+                    if (++spins > spin_limit) {
                         failed = true;
                         done = true;
                     } else {
@@ -229,17 +250,23 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
             if (all) break;
         }
     }
+    const float poison = failed ? __builtin_nanf("") : 0.0f;
     if (s == 0 && q.gok) {
+        // a block whose wait gave up hands NaN on in its inclusive state, so
+        // that every later block of the sequence and the final state show it
         Lane incl = P;
         compose(incl, agg, ch.W, (float)TB);
+        incl.a += poison;
+        incl.b += poison;
         publish(incls + slot_of(j), lane, incl, tag_incl);
+        if (failed && lane == 0)
+            __hip_atomic_fetch_add(giveups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // (3) re-sweep from this segment's starting state, writing y: in one frame
     // when the whole wave's range allows it, else token by token
     Lane R = P;
     for (int w = 0; w < s; ++w) compose(R, lds_lane(sh.s, w, g, lane), ch.W, (float)LS);
-    const float poison = failed ? __builtin_nanf("") : 0.0f;
     // a segment that starts on a checkpoint token stores its starting state
     static_assert(kCkptTokens % LS == 0, "checkpoints fall on segment starts");
     if (ck && q.active && q.t0 > 0 && q.t0 < T && q.t0 % kCkptTokens == 0)
@@ -298,7 +325,8 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
     int64_t B, int64_t T, int64_t C, const float *__restrict__ w, const float *__restrict__ u,
     const typename IO::T *__restrict__ k, const typename IO::T *__restrict__ v,
     const typename IO::T *__restrict__ r, typename IO::T *__restrict__ y, const float *s_in,
-    float *s_out, float *ck, Word *aggs, Word *incls, uint32_t epoch, uint32_t nsets) {
+    float *s_out, float *ck, Word *aggs, Word *incls, uint32_t epoch, uint32_t *giveups,
+    uint32_t spin_limit, uint32_t nsets) {
     constexpr int TB = NS * LS;
     __shared__ LbShared<CG, NS> sh;
     LbWave q;
@@ -368,17 +396,17 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
     if (fast) {
         if (full)
             lb_body<CG, NS, LS, false, true, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
-                                                   s_out, ck, aggs, incls, epoch, sh);
+                                                   s_out, ck, aggs, incls, epoch, giveups, spin_limit, sh);
         else
             lb_body<CG, NS, LS, false, false, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
-                                                    s_out, ck, aggs, incls, epoch, sh);
+                                                    s_out, ck, aggs, incls, epoch, giveups, spin_limit, sh);
     } else {
         if (full)
             lb_body<CG, NS, LS, true, true, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
-                                                  s_out, ck, aggs, incls, epoch, sh);
+                                                  s_out, ck, aggs, incls, epoch, giveups, spin_limit, sh);
         else
             lb_body<CG, NS, LS, true, false, GATE, IO>(B, T, C, ch, q, K, V, Rg, y + base, s_in,
-                                                   s_out, ck, aggs, incls, epoch, sh);
+                                                   s_out, ck, aggs, incls, epoch, giveups, spin_limit, sh);
     }
 }
 
@@ -416,12 +444,14 @@ hipError_t launch_lb(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st
     const int64_t nsets = (ngroups + CG - 1) / CG;
     const int64_t nblocks = (a.T + NS * LS - 1) / (NS * LS);
     const int64_t nslots = nblocks * a.B * ngroups;
-    Word *aggs = (Word *)sc.base;
-    Word *incls = (Word *)((char *)sc.base + align_up((size_t)nslots * kSlotWords * sizeof(Word)));
+    uint32_t *giveups = (uint32_t *)sc.base;
+    Word *aggs = (Word *)((char *)sc.base + kLookbackHeaderBytes);
+    Word *incls = (Word *)((char *)aggs + align_up((size_t)nslots * kSlotWords * sizeof(Word)));
     hipLaunchKernelGGL((fwd_lookback_kernel<CG, NS, LS, GATE, IO>),
                        dim3((unsigned)(nsets * a.B * nblocks)), dim3(CG * NS * 64), 0, st, a.B,
                        a.T, a.C, a.w, a.u, (const T *)a.k, (const T *)a.v, (const T *)a.r,
-                       (T *)a.y, a.s_in, a.s_out, a.ck, aggs, incls, sc.epoch, (uint32_t)nsets);
+                       (T *)a.y, a.s_in, a.s_out, a.ck, aggs, incls, sc.epoch, giveups,
+                       sc.spin_limit, (uint32_t)nsets);
     return hipGetLastError();
 }
 
@@ -459,7 +489,7 @@ bool lookback_grid_ok(int64_t B, int64_t T, int64_t C, int cg, int ns, int ls) {
 size_t lookback_scratch_bytes(int64_t B, int64_t T, int64_t C, int ns, int ls) {
     const int64_t nblocks = (T + (int64_t)ns * ls - 1) / ((int64_t)ns * ls);
     const int64_t nslots = nblocks * B * ((C + 63) / 64);
-    return 2 * align_up((size_t)nslots * kSlotWords * sizeof(Word));
+    return kLookbackHeaderBytes + 2 * align_up((size_t)nslots * kSlotWords * sizeof(Word));
 }
 
 template <int CG, int NS, int LS, class IO>

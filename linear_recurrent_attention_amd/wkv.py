@@ -32,6 +32,7 @@ WKV_ERR_ALIAS = 4
 WKV_ERR_WORKSPACE = 5
 WKV_ERR_UNSUPPORTED = 6
 WKV_ERR_HIP = 7
+WKV_ERR_LOOKBACK = 8
 
 # wkv_kernel values
 WKV_KERNEL_AUTO = 0
@@ -45,7 +46,9 @@ EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backw
             "wkv_step_typed", "wkv_backward_state", "wkv_backward_typed",
             "wkv_forward_checkpointed", "wkv_backward_checkpointed", "wkv_backward_gated",
             "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward",
-            "wkv_token_shift_typed", "wkv_token_shift_backward_typed")
+            "wkv_token_shift_typed", "wkv_token_shift_backward_typed",
+            "wkv_forward_scratch_size", "wkv_release_stream_scratch", "wkv_lookback_status",
+            "wkv_set_lookback_spin_limit")
 
 # wkv_dtype values
 WKV_DTYPE_F32 = 0
@@ -135,6 +138,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_token_shift_backward_typed.restype = ctypes.c_int
     lib.wkv_status_string.argtypes = [ctypes.c_int]
     lib.wkv_status_string.restype = ctypes.c_char_p
+    lib.wkv_forward_scratch_size.argtypes = [i64, i64, i64]
+    lib.wkv_forward_scratch_size.restype = sz
+    lib.wkv_release_stream_scratch.argtypes = [vp]
+    lib.wkv_release_stream_scratch.restype = ctypes.c_int
+    lib.wkv_lookback_status.argtypes = [vp]
+    lib.wkv_lookback_status.restype = ctypes.c_int
+    lib.wkv_set_lookback_spin_limit.argtypes = [ctypes.c_uint32]
+    lib.wkv_set_lookback_spin_limit.restype = ctypes.c_uint32
     _lib = lib
     return lib
 
@@ -168,10 +179,66 @@ def _check(fn, status):
         raise WkvError(fn, status)
 
 
-def _bundle_shape(k, state, L=None):
+def _bundle_shape(k):
+    if not isinstance(k, torch.Tensor):
+        raise TypeError("k: expected a torch.Tensor")
     if k.dim() != 3:
         raise ValueError("k must be 3-D")
     return tuple(int(x) for x in k.shape)
+
+
+def _expect(device, *spec):
+    """Checks (name, tensor, shape) triples before a call: every tensor given
+    (None is skipped) must have exactly that shape and, when non-empty, live on
+    ``device``.  The C ABI takes bare pointers and cannot check sizes, so a
+    wrong-sized buffer would be read or written out of bounds."""
+    for name, t, shape in spec:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch.Tensor")
+        if tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.numel() > 0 and t.device != device:
+            raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _expect_workspace(device, ws, need):
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace: expected a torch.Tensor")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    if ws.numel() > 0 and ws.device != device:
+        raise ValueError(f"workspace: on {ws.device}, expected {device}")
+    if ws.numel() < need:
+        raise ValueError(f"workspace: {ws.numel()} bytes, need {need}")
+
+
+def _fwd_expect(k, w, u, v, r, y, state_in, state_out, checkpoints=None):
+    B, T, C = (int(x) for x in k.shape)
+    _expect(k.device, ("w", w, (C,)), ("u", u, (C,)), ("v", v, (B, T, C)), ("r", r, (B, T, C)),
+            ("y", y, (B, T, C)), ("state_in", state_in, (3, B, C)),
+            ("state_out", state_out, (3, B, C)),
+            ("checkpoints", checkpoints, (checkpoint_count(T), 3, B, C)))
+
+
+def _bwd_expect(k, w, u, v, dy, dk, dv, dw, du, state_in=None, state_out=None,
+                d_state_out=None, d_state_in=None, checkpoints=None, r=None, dr=None):
+    B, T, C = (int(x) for x in k.shape)
+    seq, st = (B, T, C), (3, B, C)
+    _expect(k.device, ("w", w, (C,)), ("u", u, (C,)), ("v", v, seq), ("dy", dy, seq),
+            ("dk", dk, seq), ("dv", dv, seq), ("dw", dw, (C,)), ("du", du, (C,)),
+            ("state_in", state_in, st), ("state_out", state_out, st),
+            ("d_state_out", d_state_out, st), ("d_state_in", d_state_in, st),
+            ("checkpoints", checkpoints, (checkpoint_count(T), 3, B, C)), ("r", r, seq),
+            ("dr", dr, seq))
+
+
+def _step_expect(k, w, u, v, r, y, state_in, state_out):
+    L, B, C = (int(x) for x in k.shape)
+    _expect(k.device, ("w", w, (L, C)), ("u", u, (L, C)), ("v", v, (L, B, C)),
+            ("r", r, (L, B, C)), ("y", y, (L, B, C)), ("state_in", state_in, (L, 3, B, C)),
+            ("state_out", state_out, (L, 3, B, C)))
 
 
 def wkv_forward(w, u, k, v, y=None, state_in=None, state_out=None, stream=None, plan=None):
@@ -182,11 +249,12 @@ def wkv_forward(w, u, k, v, y=None, state_in=None, state_out=None, stream=None, 
     is an optional (kernel, segments, seg_len[, channels]) tuple for
     ``wkv_forward_ex``.
     """
-    B, T, C = _bundle_shape(k, state_in)
+    B, T, C = _bundle_shape(k)
     if y is None:
         y = torch.empty_like(k)
     if state_out is True:
         state_out = torch.empty((3, B, C), device=k.device, dtype=torch.float32)
+    _fwd_expect(k, w, u, v, None, y, state_in, state_out)
     lib = load_library()
     args = [B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(state_in),
             _ptr(state_out)]
@@ -210,11 +278,12 @@ def wkv_forward_gated(w, u, k, v, r, y=None, state_in=None, state_out=None, stre
     """Forward with the time-mixing output gate: y = sigmoid(r) * wkv.
     Arguments as for ``wkv_forward``; r has the layout of k.  Returns
     (y, state_out)."""
-    B, T, C = _bundle_shape(k, state_in)
+    B, T, C = _bundle_shape(k)
     if y is None:
         y = torch.empty_like(k)
     if state_out is True:
         state_out = torch.empty((3, B, C), device=k.device, dtype=torch.float32)
+    _fwd_expect(k, w, u, v, r, y, state_in, state_out)
     st = load_library().wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
                                           _ptr(y), _ptr(state_in), _ptr(state_out), _plan(plan),
                                           _stream(stream))
@@ -230,11 +299,12 @@ def wkv_forward_typed(w, u, k, v, r=None, y=None, state_in=None, state_out=None,
     if k.dtype not in _DTYPES:
         raise TypeError(f"unsupported element type {k.dtype}")
     dt = k.dtype
-    B, T, C = _bundle_shape(k, state_in)
+    B, T, C = _bundle_shape(k)
     if y is None:
         y = torch.empty_like(k)
     if state_out is True:
         state_out = torch.empty((3, B, C), device=k.device, dtype=torch.float32)
+    _fwd_expect(k, w, u, v, r, y, state_in, state_out)
     st = load_library().wkv_forward_typed(B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt),
                                           _ptr(v, dt), _ptr(r, dt), _ptr(y, dt),
                                           _ptr(state_in), _ptr(state_out), _plan(plan),
@@ -252,7 +322,7 @@ def wkv_forward_checkpointed(w, u, k, v, r=None, y=None, state_in=None, state_ou
     if k.dtype not in _DTYPES:
         raise TypeError(f"unsupported element type {k.dtype}")
     dt = k.dtype
-    B, T, C = _bundle_shape(k, state_in)
+    B, T, C = _bundle_shape(k)
     if y is None:
         y = torch.empty_like(k)
     if state_out is True:
@@ -260,6 +330,7 @@ def wkv_forward_checkpointed(w, u, k, v, r=None, y=None, state_in=None, state_ou
     if checkpoints is None:
         checkpoints = torch.empty((checkpoint_count(T), 3, B, C), device=k.device,
                                   dtype=torch.float32)
+    _fwd_expect(k, w, u, v, r, y, state_in, state_out, checkpoints)
     st = load_library().wkv_forward_checkpointed(
         B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt), _ptr(v, dt), _ptr(r, dt),
         _ptr(y, dt), _ptr(state_in), _ptr(state_out), _ptr(checkpoints), _plan(plan),
@@ -274,7 +345,8 @@ def bind_forward(w, u, k, v, y, state_in=None, state_out=None, stream=None, plan
     may change between calls).  For loops bound by the launch rate, such as
     RNN mode over many short chunks, where re-checking every tensor in Python
     on each call would cost as much as the kernel."""
-    B, T, C = _bundle_shape(k, state_in)
+    B, T, C = _bundle_shape(k)
+    _fwd_expect(k, w, u, v, None, y, state_in, state_out)
     lib = load_library()
     p = None if plan is None else (ForwardPlan(*plan) if len(plan) == 4 else ForwardPlan(*plan, 0))
     args = (B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(state_in),
@@ -288,6 +360,32 @@ def bind_forward(w, u, k, v, y, state_in=None, state_out=None, stream=None, plan
             raise WkvError("wkv_forward_ex", st)
     call.keep = keep
     return call
+
+
+def wkv_forward_scratch_size(B: int, T: int, C: int) -> int:
+    """Bytes of look-back scratch wkv_forward uses for this shape (0: none)."""
+    return int(load_library().wkv_forward_scratch_size(B, T, C))
+
+
+def wkv_release_stream_scratch(stream=None):
+    """Release (in stream order) the look-back scratch kept for ``stream``."""
+    _check("wkv_release_stream_scratch", load_library().wkv_release_stream_scratch(_stream(stream)))
+
+
+def wkv_lookback_status(stream=None) -> int:
+    """Synchronise ``stream`` and return WKV_OK, or WKV_ERR_LOOKBACK if a
+    look-back wait of a forward on it gave up since the last call (clears the
+    record).  Other failures raise."""
+    st = load_library().wkv_lookback_status(_stream(stream))
+    if st not in (WKV_OK, WKV_ERR_LOOKBACK):
+        raise WkvError("wkv_lookback_status", st)
+    return st
+
+
+def wkv_set_lookback_spin_limit(rounds: int) -> int:
+    """Test hook: look-back rounds without progress before a wait gives up.
+    Returns the previous limit."""
+    return int(load_library().wkv_set_lookback_spin_limit(int(rounds)))
 
 
 def wkv_forward_plan_auto(B: int, T: int, C: int):
@@ -306,6 +404,7 @@ def wkv_step(w, u, k, v, state_in, state_out=None, y=None, stream=None):
         y = torch.empty_like(k)
     if state_out is None:
         state_out = state_in
+    _step_expect(k, w, u, v, None, y, state_in, state_out)
     st = load_library().wkv_step(L, B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                  _ptr(state_in), _ptr(state_out), _stream(stream))
     _check("wkv_step", st)
@@ -321,6 +420,7 @@ def wkv_step_gated(w, u, k, v, r, state_in, state_out=None, y=None, stream=None)
         y = torch.empty_like(k)
     if state_out is None:
         state_out = state_in
+    _step_expect(k, w, u, v, r, y, state_in, state_out)
     st = load_library().wkv_step_gated(L, B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
                                        _ptr(y), _ptr(state_in), _ptr(state_out), _stream(stream))
     _check("wkv_step_gated", st)
@@ -339,6 +439,7 @@ def wkv_step_typed(w, u, k, v, state_in, r=None, state_out=None, y=None, stream=
         y = torch.empty_like(k)
     if state_out is None:
         state_out = state_in
+    _step_expect(k, w, u, v, r, y, state_in, state_out)
     st = load_library().wkv_step_typed(L, B, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt),
                                        _ptr(v, dt), _ptr(r, dt), _ptr(y, dt), _ptr(state_in),
                                        _ptr(state_out), _stream(stream))
@@ -363,6 +464,8 @@ def wkv_token_shift(mu, x, x_prev=None, out=None, x_prev_out=None, stream=None):
         out = torch.empty((M, B, T, C), device=x.device, dtype=dt)
     if x_prev_out is True:
         x_prev_out = torch.empty((B, C), device=x.device, dtype=dt)
+    _expect(x.device, ("mu", mu, (M, C)), ("x_prev", x_prev, (B, C)), ("out", out, (M, B, T, C)),
+            ("x_prev_out", x_prev_out, (B, C)))
     lib = load_library()
     if dt == torch.float32:
         st = lib.wkv_token_shift(B, T, C, M, _ptr(mu), _ptr(x), _ptr(x_prev), _ptr(out),
@@ -395,12 +498,14 @@ def wkv_token_shift_backward(mu, x, d_out, x_prev=None, d_x_prev_out=None, dx=No
     if d_x_prev is True:
         d_x_prev = torch.empty((B, C), device=dev, dtype=dt)
     dmu = torch.empty((M, C), device=dev, dtype=torch.float32) if dmu is None else dmu
+    _expect(dev, ("mu", mu, (M, C)), ("x_prev", x_prev, (B, C)), ("d_out", d_out, (M, B, T, C)),
+            ("d_x_prev_out", d_x_prev_out, (B, C)), ("dx", dx, (B, T, C)),
+            ("d_x_prev", d_x_prev, (B, C)), ("dmu", dmu, (M, C)))
     lib = load_library()
     need = int(lib.wkv_token_shift_backward_workspace_size(B, T, C, M))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise TypeError("workspace must be a contiguous uint8 tensor")
+    _expect_workspace(dev, workspace, need)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
     if dt == torch.float32:
         st = lib.wkv_token_shift_backward(B, T, C, M, _ptr(mu), _ptr(x), _ptr(x_prev),
@@ -427,17 +532,17 @@ def wkv_backward(w, u, k, v, dy, dk=None, dv=None, dw=None, du=None, workspace=N
     """Gradients (dk, dv, dw, du) of sum(dy * y) for the GPT-mode forward with the
     empty initial state.  ``workspace`` is a uint8 device tensor of at least
     ``wkv_backward_workspace_size(B, T, C)`` bytes (allocated when omitted)."""
-    B, T, C = _bundle_shape(k, None)
+    B, T, C = _bundle_shape(k)
     dev = k.device
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(k) if dv is None else dv
     dw = torch.empty(C, device=dev, dtype=torch.float32) if dw is None else dw
     du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
+    _bwd_expect(k, w, u, v, dy, dk, dv, dw, du)
     need = wkv_backward_workspace_size(B, T, C)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise TypeError("workspace must be a contiguous uint8 tensor")
+    _expect_workspace(dev, workspace, need)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
     st = load_library().wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
                                      _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), ws_ptr,
@@ -453,7 +558,7 @@ def wkv_backward_state(w, u, k, v, dy, state_in=None, state_out=None, d_state_ou
     gradient in the coordinates of ``state_out`` (the state the forward
     returned); ``d_state_in=True`` allocates the gradient of ``state_in``.
     Returns (dk, dv, dw, du, d_state_in)."""
-    B, T, C = _bundle_shape(k, None)
+    B, T, C = _bundle_shape(k)
     dev = k.device
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(k) if dv is None else dv
@@ -461,11 +566,11 @@ def wkv_backward_state(w, u, k, v, dy, state_in=None, state_out=None, d_state_ou
     du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
     if d_state_in is True:
         d_state_in = torch.empty((3, B, C), device=dev, dtype=torch.float32)
+    _bwd_expect(k, w, u, v, dy, dk, dv, dw, du, state_in, state_out, d_state_out, d_state_in)
     need = wkv_backward_workspace_size(B, T, C)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise TypeError("workspace must be a contiguous uint8 tensor")
+    _expect_workspace(dev, workspace, need)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
     st = load_library().wkv_backward_state(
         B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy), _ptr(state_in), _ptr(state_out),
@@ -483,7 +588,7 @@ def wkv_backward_typed(w, u, k, v, dy, state_in=None, state_out=None, d_state_ou
     if k.dtype not in _DTYPES:
         raise TypeError(f"unsupported element type {k.dtype}")
     dt = k.dtype
-    B, T, C = _bundle_shape(k, None)
+    B, T, C = _bundle_shape(k)
     dev = k.device
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(k) if dv is None else dv
@@ -491,11 +596,11 @@ def wkv_backward_typed(w, u, k, v, dy, state_in=None, state_out=None, d_state_ou
     du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
     if d_state_in is True:
         d_state_in = torch.empty((3, B, C), device=dev, dtype=torch.float32)
+    _bwd_expect(k, w, u, v, dy, dk, dv, dw, du, state_in, state_out, d_state_out, d_state_in)
     need = wkv_backward_workspace_size(B, T, C)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise TypeError("workspace must be a contiguous uint8 tensor")
+    _expect_workspace(dev, workspace, need)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
     st = load_library().wkv_backward_typed(
         B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt), _ptr(v, dt), _ptr(dy, dt),
@@ -514,7 +619,7 @@ def wkv_backward_checkpointed(w, u, k, v, dy, checkpoints, state_in=None, state_
     if k.dtype not in _DTYPES:
         raise TypeError(f"unsupported element type {k.dtype}")
     dt = k.dtype
-    B, T, C = _bundle_shape(k, None)
+    B, T, C = _bundle_shape(k)
     dev = k.device
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(k) if dv is None else dv
@@ -522,11 +627,12 @@ def wkv_backward_checkpointed(w, u, k, v, dy, checkpoints, state_in=None, state_
     du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
     if d_state_in is True:
         d_state_in = torch.empty((3, B, C), device=dev, dtype=torch.float32)
+    _bwd_expect(k, w, u, v, dy, dk, dv, dw, du, state_in, state_out, d_state_out, d_state_in,
+                checkpoints)
     need = wkv_backward_workspace_size(B, T, C)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise TypeError("workspace must be a contiguous uint8 tensor")
+    _expect_workspace(dev, workspace, need)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
     st = load_library().wkv_backward_checkpointed(
         B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt), _ptr(v, dt), _ptr(dy, dt),
@@ -546,7 +652,7 @@ def wkv_backward_gated(w, u, k, v, r, dy, checkpoints=None, state_in=None, state
     if k.dtype not in _DTYPES:
         raise TypeError(f"unsupported element type {k.dtype}")
     dt = k.dtype
-    B, T, C = _bundle_shape(k, None)
+    B, T, C = _bundle_shape(k)
     dev = k.device
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(k) if dv is None else dv
@@ -555,11 +661,12 @@ def wkv_backward_gated(w, u, k, v, r, dy, checkpoints=None, state_in=None, state
     du = torch.empty(C, device=dev, dtype=torch.float32) if du is None else du
     if d_state_in is True:
         d_state_in = torch.empty((3, B, C), device=dev, dtype=torch.float32)
+    _bwd_expect(k, w, u, v, dy, dk, dv, dw, du, state_in, state_out, d_state_out, d_state_in,
+                checkpoints, r, dr)
     need = wkv_backward_workspace_size(B, T, C)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise TypeError("workspace must be a contiguous uint8 tensor")
+    _expect_workspace(dev, workspace, need)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() > 0 else None
     st = load_library().wkv_backward_gated(
         B, T, C, _DTYPES[dt], _ptr(w), _ptr(u), _ptr(k, dt), _ptr(v, dt), _ptr(r, dt),

@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     from linear_recurrent_attention_amd import wkv
     seen = set()
-    for s in range(8):
+    for s in range(9):
         txt = wkv.wkv_status_string(s)
         assert txt and txt not in seen
         seen.add(txt)
@@ -442,3 +442,90 @@ def test_auto_plan_follows_its_thresholds(lib):
         assert W.wkv_forward_plan_auto(*shape) == want, shape
     with pytest.raises(W.WkvError):
         W.wkv_forward_plan_auto(-1, 4, 4)
+
+
+def test_forward_scratch_size_is_host_arithmetic(lib):
+    """The look-back scratch a shape needs: a 256-byte header and two slot
+    arrays of 2 KiB per (block, sequence, 64-channel group); none for shapes the
+    automatic plan gives to a kernel without cross-workgroup state."""
+    from linear_recurrent_attention_amd import wkv as W
+    B, T, C = 8, 1024, 2048
+    plan = W.wkv_forward_plan_auto(B, T, C)
+    assert plan[0] == W.WKV_KERNEL_LOOKBACK
+    blocks = -(-T // (plan[1] * plan[2]))
+    slots = blocks * B * (C // 64)
+    assert W.wkv_forward_scratch_size(B, T, C) == 256 + 2 * slots * 2048
+    assert W.wkv_forward_scratch_size(1, 8, 64) == 0          # lane kernel
+    assert W.wkv_forward_scratch_size(-1, 8, 64) == 0         # invalid
+    assert W.wkv_forward_scratch_size(4, 0, 64) == 0          # nothing to do
+
+
+def test_spin_limit_hook_round_trips(lib):
+    from linear_recurrent_attention_amd import wkv as W
+    old = W.wkv_set_lookback_spin_limit(7)
+    assert old == 1 << 16
+    assert W.wkv_set_lookback_spin_limit(old) == 7
+
+
+def _bad_shape_cases():
+    """(name of the binding call, callable) pairs, each with exactly one tensor
+    of the wrong shape; the binding must raise before any library call."""
+    import torch
+    from linear_recurrent_attention_amd import wkv as W
+    B, T, C = 2, 5, 8
+    f = lambda *s: torch.zeros(*s)
+    seq, st = (B, T, C), (3, B, C)
+    k = f(*seq)
+    good = dict(w=f(C), u=f(C), k=k, v=f(*seq))
+    cases = [
+        ("v", lambda: W.wkv_forward(good["w"], good["u"], k, f(B, T, C + 1))),
+        ("w", lambda: W.wkv_forward(f(C - 1), good["u"], k, good["v"])),
+        ("u", lambda: W.wkv_forward(good["w"], f(C, 1), k, good["v"])),
+        ("y", lambda: W.wkv_forward(good["w"], good["u"], k, good["v"], y=f(B, T + 1, C))),
+        ("state_in", lambda: W.wkv_forward(good["w"], good["u"], k, good["v"], state_in=f(3, B, C + 1))),
+        ("state_out", lambda: W.wkv_forward(good["w"], good["u"], k, good["v"], state_out=f(2, B, C))),
+        ("r", lambda: W.wkv_forward_gated(good["w"], good["u"], k, good["v"], f(B, T, 1))),
+        ("r", lambda: W.wkv_forward_typed(good["w"], good["u"], k, good["v"], r=f(B, 1, C))),
+        ("checkpoints", lambda: W.wkv_forward_checkpointed(
+            good["w"], good["u"], f(B, 300, C), f(B, 300, C), checkpoints=f(1, 3, B, C))),
+        ("v", lambda: W.bind_forward(good["w"], good["u"], k, f(B, T), f(*seq))),
+        ("state_in", lambda: W.wkv_step(f(3, C), f(3, C), f(3, B, C), f(3, B, C), f(3, 3, B))),
+        ("w", lambda: W.wkv_step(f(C), f(3, C), f(3, B, C), f(3, B, C), f(3, 3, B, C))),
+        ("r", lambda: W.wkv_step_gated(f(3, C), f(3, C), f(3, B, C), f(3, B, C), f(3, B),
+                                       f(3, 3, B, C))),
+        ("dy", lambda: W.wkv_backward(good["w"], good["u"], k, good["v"], f(B, T, C + 2))),
+        ("dw", lambda: W.wkv_backward(good["w"], good["u"], k, good["v"], f(*seq), dw=f(C + 1))),
+        ("d_state_out", lambda: W.wkv_backward_state(
+            good["w"], good["u"], k, good["v"], f(*seq), state_out=f(*st), d_state_out=f(3, C))),
+        ("checkpoints", lambda: W.wkv_backward_checkpointed(
+            good["w"], good["u"], f(B, 300, C), f(B, 300, C), f(B, 300, C), f(3, 3, B, C))),
+        ("dr", lambda: W.wkv_backward_gated(good["w"], good["u"], k, good["v"], f(*seq), f(*seq),
+                                            dr=f(B, T, C, 1))),
+        ("workspace", lambda: W.wkv_backward(good["w"], good["u"], k, good["v"], f(*seq),
+                                             workspace=torch.zeros(1, dtype=torch.float32))),
+        ("x_prev", lambda: W.wkv_token_shift(f(3, C), f(*seq), x_prev=f(B, C + 1))),
+        ("mu", lambda: W.wkv_token_shift(f(3, C + 1), f(*seq))),
+        ("out", lambda: W.wkv_token_shift(f(3, C), f(*seq), out=f(2, B, T, C))),
+        ("d_out", lambda: W.wkv_token_shift_backward(f(3, C), f(*seq), f(3, B, T, C - 1))),
+        ("dmu", lambda: W.wkv_token_shift_backward(f(3, C), f(*seq), f(3, B, T, C), dmu=f(2, C))),
+    ]
+    return cases
+
+
+def test_binding_checks_every_shape_before_calling():
+    """Each binding call checks the shape of every tensor it passes against k's
+    (or x's) dimensions: the C ABI receives bare pointers and could not."""
+    for name, call in _bad_shape_cases():
+        with pytest.raises((ValueError, TypeError)) as e:
+            call()
+        assert name in str(e.value) or "workspace" in str(e.value), (name, str(e.value))
+
+
+def test_binding_checks_devices():
+    """A tensor on another device than k's is refused before any call."""
+    import torch
+    from linear_recurrent_attention_amd import wkv as W
+    k = torch.zeros(2, 3, 4, device="meta")
+    w = torch.zeros(4, device="meta")
+    with pytest.raises(ValueError, match="expected meta"):
+        W.wkv_forward(w, w, k, torch.zeros(2, 3, 4), y=torch.empty(2, 3, 4, device="meta"))
