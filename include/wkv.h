@@ -539,6 +539,38 @@ WKV_API wkv_status wkv_token_shift_backward_typed(int64_t B, int64_t T, int64_t 
                                                   void *workspace, size_t workspace_bytes,
                                                   hipStream_t stream);
 
+/* Size of the fixed scratch array behind wkv_forward_noalloc, per device. */
+#define WKV_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+
+/*
+ * wkv_forward for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation.  It calls no hipMalloc, hipFree or other allocating routine: the
+ * look-back kernel's scratch is a fixed array of WKV_NOALLOC_SCRATCH_BYTES in
+ * device memory that every device running the library holds until the process
+ * ends.  Same arguments, semantics and results (within the documented
+ * accuracy) as wkv_forward, with the automatic kernel choice.
+ *   - A shape whose look-back scratch (wkv_forward_scratch_size) exceeds
+ *     WKV_NOALLOC_SCRATCH_BYTES returns WKV_ERR_WORKSPACE with nothing
+ *     launched; such a shape can run through wkv_forward, or through
+ *     wkv_forward_ex with a WKV_KERNEL_SEGMENTED plan (no scratch).
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's contents (each launch tags what it writes, so nothing needs
+ *     clearing).  Calls that overlap in time on one device, from any stream or
+ *     thread, race on it: callers serialise them.
+ *   - The first call on a device takes the array's address on it (which may
+ *     load the library's device code, and with it the array); a caller that
+ *     will capture makes one call on each device beforehand.  Under graph
+ *     capture the automatic choice takes a kernel without cross-workgroup
+ *     state, as for wkv_forward.
+ * Waits that give up are reported by wkv_lookback_status on the stream of a
+ * later call.
+ */
+WKV_API wkv_status wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float *w,
+                                       const float *u, const float *k, const float *v, float *y,
+                                       const float *state_in, float *state_out,
+                                       hipStream_t stream);
+
 /*
  * Bytes of look-back scratch wkv_forward would use for this shape on the
  * current device (0 when its kernel needs none, or for an invalid shape).
@@ -556,7 +588,8 @@ WKV_API wkv_status wkv_release_stream_scratch(hipStream_t stream);
 
 /*
  * Synchronises `stream`, then reports whether any look-back wait of a forward
- * on this stream (on the current device) gave up since the last call:
+ * on this stream, or of a wkv_forward_noalloc call on the current device, gave
+ * up since the last call:
  * WKV_ERR_LOOKBACK if one did (those launches' outputs from the stalled block
  * on, and their state_out, are NaN), WKV_OK if none did, WKV_ERR_HIP on a
  * runtime error.  Clears the record.  Forwards are asynchronous, so this is

@@ -14,6 +14,12 @@
 #include "../../include/wkv.h"
 #include "wkv_internal.hpp"
 
+// Scratch of wkv_forward_noalloc (see launch_with_noalloc_scratch):
+// WKV_NOALLOC_SCRATCH_BYTES of device memory per device, zero when the code
+// object is loaded and held until the process ends.
+constexpr size_t kNoAllocScratchBytes = WKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned long long scratch[kNoAllocScratchBytes / 8];
+
 namespace {
 
 using wkv::BwdArgs;
@@ -130,6 +136,46 @@ hipError_t launch_with_scratch(const FwdArgs &a, int cg, int ns, int ls, size_t 
     return e;
 }
 
+// Scratch of wkv_forward_noalloc: a fixed array in device memory, one copy per
+// device, allocated with the library's code object and zero when loaded.  Its
+// address on each device is taken once, with that device current, and kept;
+// the host never passes the array's own name to a kernel (in host code that
+// name is a stand-in, not a device address).
+struct NoAllocScratch {
+    void *ptr = nullptr;  // device address of `scratch` on this device
+    uint32_t epoch = 1;
+};
+NoAllocScratch g_noalloc[kMaxDevices];
+
+// Address of this device's copy (under g_mu).
+hipError_t noalloc_address(int dev, void **out) {
+    NoAllocScratch &n = g_noalloc[dev];
+    if (!n.ptr) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        n.ptr = ptr;
+    }
+    *out = n.ptr;
+    return hipSuccess;
+}
+
+hipError_t launch_with_noalloc_scratch(const FwdArgs &a, int cg, int ns, int ls, hipStream_t st) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_mu);
+    void *p = nullptr;
+    if ((e = noalloc_address(dev, &p)) != hipSuccess) return e;
+    NoAllocScratch &n = g_noalloc[dev];
+    const wkv::LookbackScratch sc{p, n.epoch, g_spin_limit.load()};
+    e = wkv::launch_forward_lookback(a, cg, ns, ls, sc, st);
+    if (e == hipSuccess) e = advance_epoch(p, kNoAllocScratchBytes, n.epoch, st);
+    return e;
+}
+
 // Reads and clears the give-up count in the header at p (synchronous).
 hipError_t take_giveups(void *p, uint32_t *count) {
     uint32_t c = 0;
@@ -232,7 +278,7 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
                         const void *k, const void *v, const void *r, void *y,
                         const float *state_in, float *state_out, const wkv_forward_plan *plan,
                         bool gated, int io, hipStream_t stream, bool with_ck = false,
-                        float *ck = nullptr) {
+                        float *ck = nullptr, bool noalloc = false) {
     const int64_t esize = elem_bytes(io);
     if (esize == 0) return WKV_ERR_UNSUPPORTED;
     wkv_status st = check_forward(B, T, C, w, u, k, v, y, state_in, state_out, r, gated, esize);
@@ -308,6 +354,10 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
         const int cg = p.channels / 64;
         if (!wkv::lookback_grid_ok(B, T, C, cg, p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
         const size_t need = wkv::lookback_scratch_bytes(B, T, C, p.segments, p.seg_len);
+        if (noalloc) {
+            if (need > kNoAllocScratchBytes) return WKV_ERR_WORKSPACE;
+            return from_hip(launch_with_noalloc_scratch(a, cg, p.segments, p.seg_len, stream));
+        }
         if (need > kLookbackScratchMax) return WKV_ERR_UNSUPPORTED;
         return from_hip(launch_with_scratch(a, cg, p.segments, p.seg_len, need, stream));
     }
@@ -677,6 +727,14 @@ WKV_API wkv_status wkv_backward_gated(int64_t B, int64_t T, int64_t C, wkv_dtype
                          checkpoints != nullptr, checkpoints, true, r, dr);
 }
 
+WKV_API wkv_status wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float *w,
+                                       const float *u, const float *k, const float *v, float *y,
+                                       const float *state_in, float *state_out,
+                                       hipStream_t stream) {
+    return forward_impl(B, T, C, w, u, k, v, nullptr, y, state_in, state_out, nullptr, false,
+                        WKV_DTYPE_F32, stream, false, nullptr, true);
+}
+
 WKV_API size_t wkv_forward_scratch_size(int64_t B, int64_t T, int64_t C) {
     if (B < 0 || T < 0 || C < 0 || bytes_of(B, T, C) < 0 || B * C == 0 || T == 0) return 0;
     const wkv_forward_plan p = auto_plan(B, T, C, device_cus());
@@ -703,6 +761,9 @@ WKV_API wkv_status wkv_lookback_status(hipStream_t stream) {
     uint32_t count = 0;
     auto it = g_scratch.find(std::make_pair(dev, stream));
     if (it != g_scratch.end() && it->second.p && take_giveups(it->second.p, &count) != hipSuccess)
+        return WKV_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices && g_noalloc[dev].ptr &&
+        take_giveups(g_noalloc[dev].ptr, &count) != hipSuccess)
         return WKV_ERR_HIP;
     return count ? WKV_ERR_LOOKBACK : WKV_OK;
 }

@@ -48,7 +48,7 @@ EXPORTED = ("wkv_forward", "wkv_step", "wkv_backward_workspace_size", "wkv_backw
             "wkv_token_shift_backward_workspace_size", "wkv_token_shift_backward",
             "wkv_token_shift_typed", "wkv_token_shift_backward_typed",
             "wkv_forward_scratch_size", "wkv_release_stream_scratch", "wkv_lookback_status",
-            "wkv_set_lookback_spin_limit")
+            "wkv_set_lookback_spin_limit", "wkv_forward_noalloc")
 
 # wkv_dtype values
 WKV_DTYPE_F32 = 0
@@ -144,6 +144,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wkv_release_stream_scratch.restype = ctypes.c_int
     lib.wkv_lookback_status.argtypes = [vp]
     lib.wkv_lookback_status.restype = ctypes.c_int
+    lib.wkv_forward_noalloc.argtypes = [i64, i64, i64] + [vp] * 7 + [vp]
+    lib.wkv_forward_noalloc.restype = ctypes.c_int
     lib.wkv_set_lookback_spin_limit.argtypes = [ctypes.c_uint32]
     lib.wkv_set_lookback_spin_limit.restype = ctypes.c_uint32
     _lib = lib
@@ -360,6 +362,21 @@ def bind_forward(w, u, k, v, y, state_in=None, state_out=None, stream=None, plan
             raise WkvError("wkv_forward_ex", st)
     call.keep = keep
     return call
+
+
+WKV_NOALLOC_SCRATCH_BYTES = 40 << 20
+
+
+def wkv_forward_noalloc(w, u, k, v, y, state_in=None, state_out=None, stream=None):
+    """``wkv_forward`` through the entry point that allocates nothing (its
+    look-back scratch is a fixed array per device).  y and state_out (if
+    wanted) must be given: the call allocates no output either."""
+    B, T, C = _bundle_shape(k)
+    _fwd_expect(k, w, u, v, None, y, state_in, state_out)
+    st = load_library().wkv_forward_noalloc(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                            _ptr(state_in), _ptr(state_out), _stream(stream))
+    _check("wkv_forward_noalloc", st)
+    return y, state_out
 
 
 def wkv_forward_scratch_size(B: int, T: int, C: int) -> int:
