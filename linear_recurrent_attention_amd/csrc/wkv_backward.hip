@@ -294,6 +294,20 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
     }
 
     // ---------------- phase 2: tiles in reverse ----------------
+    // dw's terms are e^{k_i} times sums kept within 2^16 of their frame.  Where
+    // the bonus dominates every output (U - W beyond the one-exponential range)
+    // all weights of earlier tokens are near 2^{-U}, so that factor can fall
+    // below float's normal range, where the hardware exp2 flushes to zero,
+    // while the terms it scales make up the whole of dw.  On that path the
+    // factor is formed 2^{dwx} larger (dwx from U - W, at most 64) and dw is
+    // accumulated at that scale, which stays far inside the float range: each
+    // term is a weight of at most 1 times (t-1-i) g (v - y), so a lane's sum is
+    // below T^2 max|g| (|v| + |y|) before the factor 2^{dwx}.
+    float dwx = 0.0f, dws = 1.0f;
+    if constexpr (SAFE) {
+        dwx = fminf(fmaxf(rintf(ch.U - ch.W) - 64.0f, 0.0f), 64.0f);
+        dws = ex2(-dwx);
+    }
     float dw_acc = 0.0f, du_acc = 0.0f;
     Rev carry = rev_empty();
     // the upstream state gradient as R_{T-1}, S_{T-1} (frame -o_T), staged in
@@ -440,14 +454,16 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             if (FULL || t0 + j < T) {
                 const float K = Kc[j];
                 const float v = Vc[j], g = Gc[j], y = Y[j];
-                const float ek = ex2(fmaf(-suf.m, ch.W, K + suf.r0));
+                // (dwx = 0 and dws = 1 on the one-exponential path)
+                const float ekx = ex2(fmaf(-suf.m, ch.W, K + (SAFE ? suf.r0 + dwx : suf.r0)));
+                const float ek = SAFE ? ekx * dws : ekx;
                 const float own = PII[j] * g;
                 const float vy = v - y;
                 if (active) {
                     dvr.st(j, fmaf(ek, suf.R, own));
                     dkr.st(j, fmaf(own, vy, ek * fmaf(v, suf.R, -suf.S)));
                 }
-                dw_acc = fmaf(-ek, fmaf(v, suf.R1, -suf.S1), dw_acc);
+                dw_acc = fmaf(-ekx, fmaf(v, suf.R1, -suf.S1), dw_acc);
                 du_acc = fmaf(own, vy, du_acc);
                 rev_absorb(suf, g, y, LAM[j], ch.W);
             }
@@ -482,18 +498,19 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             o20 = o_in(s_in[(2 * B + bb) * C + c]);
         }
         // 2^{frame + o0}: bounded, since e^{o0 - t w} b0 <= D_t for every output
-        const float sc = ex2(q[256] + o20);
+        const float scx = ex2(SAFE ? (q[256] + o20) + dwx : q[256] + o20);
+        const float sc = SAFE ? scx * dws : scx;
         const float da = q[0] * sc, db = -q[64] * sc;
         if (ds_in) {
             ds_in[(0 * B + bb) * C + c] = da;
             ds_in[(1 * B + bb) * C + c] = db;
             ds_in[(2 * B + bb) * C + c] = fmaf(da, a0, db * b0);
         }
-        dw_acc = fmaf(-sc, fmaf(a0, q[128], -b0 * q[192]), dw_acc);
+        dw_acc = fmaf(-scx, fmaf(a0, q[128], -b0 * q[192]), dw_acc);
     }
 
     // dw, du of this lane: sum over the waves in a fixed order
-    sh.red[0][s][lane] = (double)dw_acc;
+    sh.red[0][s][lane] = (double)dw_acc * (double)dws;
     sh.red[1][s][lane] = (double)du_acc;
     __syncthreads();
     if (s == 0 && active) {
