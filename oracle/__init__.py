@@ -50,6 +50,7 @@ def _load():
         lib.wkvo_gate.argtypes = [i64, D, D, D]
         lib.wkvo_gate_backward.argtypes = [i64, D, D, D, D, D]
         lib.wkvo_backward_state.argtypes = [i64, i64, i64] + [D] * 13
+        lib.wkvo_backward_magnitude.argtypes = [i64, i64, i64] + [D] * 10 + [ctypes.c_int]
         lib.wkvo_token_shift.argtypes = [i64, i64, i64, i64, D, D, D, D, D]
         lib.wkvo_token_shift_backward.argtypes = [i64, i64, i64, i64] + [D] * 8
         for f in (lib.wkvo_forward_brute, lib.wkvo_forward_scan, lib.wkvo_backward_brute,
@@ -163,6 +164,30 @@ def backward_state(w, u, k, v, dy, state_in=None, state_out=None, d_state_out=No
     if rc:
         raise RuntimeError(f"wkvo_backward_state failed ({rc})")
     return dk, dv, dw, du, dsi
+
+
+def backward_magnitude(w, u, k, v, dy, state_in=None, state_out=None, d_state_out=None,
+                       nthreads: int = 0):
+    """Per channel, sums of the absolute values of the terms of dw (a bound:
+    |v_i - y_t| taken as |v_i| + |y_t|) and of du (exact), with the arguments of
+    ``backward_state``.  A scale for round-off bounds of dw and du in tests; not
+    an operator function.  Returns (mdw [C], mdu [C])."""
+    B, T, C = _shapes(k, w)
+    w, u, k, v, dy = _f64(w), _f64(u), _f64(k), _f64(v), _f64(dy)
+    si = None if state_in is None else _f64(state_in)
+    so = None if state_out is None else _f64(state_out)
+    ds = None if d_state_out is None else _f64(d_state_out)
+    if ds is not None and so is None:
+        raise ValueError("d_state_out needs state_out")
+    mdw, mdu = np.empty(C), np.empty(C)
+    if nthreads <= 0:
+        nthreads = max(1, min(16, os.cpu_count() or 1))
+    rc = _load().wkvo_backward_magnitude(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(dy),
+                                         _ptr(si), _ptr(so), _ptr(ds), _ptr(mdw), _ptr(mdu),
+                                         int(nthreads))
+    if rc:
+        raise RuntimeError(f"wkvo_backward_magnitude failed ({rc})")
+    return mdw, mdu
 
 
 def gate(y, r):

@@ -55,6 +55,12 @@
  *                          wkvo_token_shift, per element on a small case and
  *                          along random directions on a larger one; mu = 0
  *                          and mu = 1 limits)
+ *   wkvo_backward_magnitude  pinned (the same sums of absolute terms written
+ *                          out pair by pair from the closed form on small
+ *                          inputs; never below |dw|, |du| of
+ *                          wkvo_backward_state; the closed form of one token
+ *                          from the empty state, where du vanishes and its
+ *                          parts are |dy v| each).  Test tolerances only.
  */
 #include <math.h>
 #include <pthread.h>
@@ -702,5 +708,141 @@ int wkvo_backward_state(int64_t B, int64_t T, int64_t C, const double *w, const 
             }
         }
     free(x);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Magnitudes of the terms of dw and du (a scale for round-off bounds)        */
+/* ------------------------------------------------------------------------ */
+/*
+ * dw and du of wkvo_backward_state are sums of many signed terms that can
+ * cancel.  A float32 computation of such a sum errs relative to the sum of the
+ * terms' absolute values, not relative to the result; this returns, per
+ * channel (summed over the batch like dw, du),
+ *   mdu = sum_t |g_t| p_{t,t} (|v_t| + |y_t|)
+ *   mdw = sum_t sum_{i<t} (t-1-i) |g_t| p_{t,i} (|v_i| + |y_t|)
+ *       + sum_t t |g_t| e^{-t w} (|A0| + |y_t| B0) / D_t
+ *       + sum_{i<T} (T-1-i) e^{k_i-(T-1-i)w} (|gA v_i| + |gB|) + T e^{-T w} (|gA A0| + |gB| B0)
+ * Each term of either sum is a difference whose two parts are counted
+ * separately (|v - y| <= |v| + |y|): float32 forms the difference from parts
+ * that each carry rounding, so where v_t and y_t nearly agree (a token that
+ * holds almost all of its weight) the difference's error is relative to the
+ * parts.  This also lets the pair sum run as an O(T) reverse scan.  With
+ * l_t = ln D_t and P_{t,i} = e^{k_i - (t-1-i) w - l_t} = p_{t,i}, the pair sum is
+ *   sum_i e^{k_i} (|v_i| R1_i + S1_i),  R1_i = sum_{t>i} (t-1-i) |g_t| e^{-(t-1-i)w - l_t},
+ * S1_i the same with |g_t y_t|, and R1_{i-1} = e^{-w} (R1_i + R0_i),
+ * R0_{i-1} = |g_i| e^{-l_i} + e^{-w} R0_i.  Long double keeps every such
+ * exponential in range for the test inputs (|k|, |l| up to thousands).  Same
+ * arguments as wkvo_backward_state; outputs mdw, mdu [C].
+ */
+struct mag_job {
+    int64_t B, T, C, c0, c1;
+    const double *w, *u, *k, *v, *dy, *state_in, *state_out, *d_state_out;
+    double *mdw, *mdu;
+};
+
+static void *mag_job_run(void *arg) {
+    const struct mag_job *jb = (const struct mag_job *)arg;
+    const int64_t B = jb->B, T = jb->T, C = jb->C;
+    const double *w = jb->w, *u = jb->u, *k = jb->k, *v = jb->v, *dy = jb->dy;
+    const double *state_in = jb->state_in, *state_out = jb->state_out;
+    const double *d_state_out = jb->d_state_out;
+    double *mdw = jb->mdw, *mdu = jb->mdu;
+    long double *lt = (long double *)malloc(sizeof(long double) * (size_t)(T + 1));
+    long double *yt = (long double *)malloc(sizeof(long double) * (size_t)(T + 1));
+    for (int64_t c = jb->c0; c < jb->c1; ++c) {
+        mdw[c] = 0.0;
+        mdu[c] = 0.0;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = jb->c0; c < jb->c1; ++c) {
+            const long double wc = w[c], uc = u[c];
+            long double a0 = 0.0L, b0 = 0.0L, o0 = -INFINITY;
+            if (state_in) {
+                a0 = state_in[SIDX(0, b, c)];
+                b0 = state_in[SIDX(1, b, c)];
+                o0 = state_in[SIDX(2, b, c)];
+            }
+            const int has_state = b0 > 0.0L;
+            /* forward: the past sums (with the state) as A = an e^{lb}, B = e^{lb} bn */
+            long double lb = has_state ? o0 : -INFINITY;  /* log of the past denominator frame */
+            long double an = has_state ? a0 : 0.0L, bn = has_state ? b0 : 0.0L;
+            long double mu_sum = 0.0L;
+            for (int64_t t = 0; t < T; ++t) {
+                const long double kt = k[IDX(b, t, c)], vt = v[IDX(b, t, c)];
+                const long double xb = uc + kt;
+                const long double m = lb > xb ? lb : xb;
+                const long double ep = bn > 0.0L ? expl(lb - m) : 0.0L, eb = expl(xb - m);
+                const long double den = ep * bn + eb;
+                lt[t] = m + logl(den);
+                yt[t] = (ep * an + eb * vt) / den;
+                const long double g = fabsl((long double)dy[IDX(b, t, c)]);
+                mu_sum += g * (eb / den) * (fabsl(vt) + fabsl(yt[t]));
+                /* fold token t, decaying the past by e^{-w} */
+                const long double lp = lb - wc;
+                const long double m2 = lp > kt ? lp : kt;
+                const long double f1 = bn > 0.0L ? expl(lp - m2) : 0.0L, f2 = expl(kt - m2);
+                an = f1 * an + f2 * vt;
+                bn = f1 * bn + f2;
+                lb = m2;
+            }
+            long double acc = 0.0L;
+            /* pairs (t, i < t), by the reverse scan */
+            long double R0 = 0.0L, R1 = 0.0L, S0 = 0.0L, S1 = 0.0L;
+            const long double dec = expl(-wc);
+            for (int64_t i = T - 1; i >= 0; --i) {
+                acc += expl((long double)k[IDX(b, i, c)]) *
+                       (fabsl((long double)v[IDX(b, i, c)]) * R1 + S1);
+                const long double g = fabsl((long double)dy[IDX(b, i, c)]);
+                const long double e = expl(-lt[i]);
+                R1 = dec * (R1 + R0);
+                S1 = dec * (S1 + S0);
+                R0 = g * e + dec * R0;
+                S0 = g * fabsl(yt[i]) * e + dec * S0;
+            }
+            if (has_state)
+                for (int64_t t = 0; t < T; ++t)
+                    acc += (long double)t * fabsl((long double)dy[IDX(b, t, c)]) *
+                           expl(-(long double)t * wc + o0 - lt[t]) *
+                           (fabsl(a0) + fabsl(yt[t]) * b0);
+            if (d_state_out) {
+                const long double gaT = d_state_out[SIDX(0, b, c)];
+                const long double gbT = d_state_out[SIDX(1, b, c)];
+                const long double moT = -(long double)state_out[SIDX(2, b, c)];
+                for (int64_t i = 0; i < T; ++i)
+                    acc += (long double)(T - 1 - i) *
+                           expl((long double)k[IDX(b, i, c)] - (long double)(T - 1 - i) * wc + moT) *
+                           (fabsl(gaT * (long double)v[IDX(b, i, c)]) + fabsl(gbT));
+                if (has_state)
+                    acc += (long double)T * expl(o0 - (long double)T * wc + moT) *
+                           (fabsl(gaT * a0) + fabsl(gbT) * b0);
+            }
+            mdw[c] += (double)acc;
+            mdu[c] += (double)mu_sum;
+        }
+    free(lt);
+    free(yt);
+    return NULL;
+}
+
+/* Channels are split over nthreads threads (each owns its channels' sums). */
+int wkvo_backward_magnitude(int64_t B, int64_t T, int64_t C, const double *w, const double *u,
+                            const double *k, const double *v, const double *dy,
+                            const double *state_in, const double *state_out,
+                            const double *d_state_out, double *mdw, double *mdu, int nthreads) {
+    if (B < 0 || T < 0 || C < 0) return 1;
+    if (d_state_out && !state_out) return 1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 64) nthreads = 64;
+    if (C < nthreads) nthreads = C > 0 ? (int)C : 1;
+    struct mag_job jobs[64];
+    pthread_t th[64];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = (struct mag_job){B, T, C, C * i / nthreads, C * (i + 1) / nthreads, w, u, k, v,
+                                   dy, state_in, state_out, d_state_out, mdw, mdu};
+        if (i > 0) pthread_create(&th[i], NULL, mag_job_run, &jobs[i]);
+    }
+    mag_job_run(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) pthread_join(th[i], NULL);
     return 0;
 }

@@ -15,7 +15,8 @@ import torch
 
 from linear_recurrent_attention_amd import synth, wkv
 from linear_recurrent_attention_amd.autograd import token_shift, wkv_time_mix
-from parity import G_FLOOR, G_RTOL, assert_grad_close, assert_y_close, f64, roundoff_floor
+from parity import (G_FLOOR, G_RTOL, assert_chained_sums_close, assert_grad_close,
+                    assert_sums_close, assert_y_close, f64, roundoff_floor)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,8 +91,8 @@ def test_chunked_training_matches_one_call(oracle, chunks):
     fs = roundoff_floor(a["dy"], a["v"], summed=True)
     assert_grad_close(f64(torch.cat([k.grad for k in ks], 1)), dk, "dk", f)
     assert_grad_close(f64(torch.cat([v.grad for v in vs], 1)), dv, "dv", f)
-    assert_grad_close(f64(w.grad), dw, "dw", fs)
-    assert_grad_close(f64(u.grad), du, "du", fs)
+    assert_chained_sums_close(oracle, f64(w.grad), f64(u.grad), dw, du, a["w"], a["u"], a["k"],
+                              a["v"], a["dy"], chunks, s0)
     for pl in range(3):
         assert_grad_close(f64(s_first.grad)[pl], dsi[pl], f"d_state_in[{pl}]", fs)
 
@@ -121,12 +122,10 @@ def test_gated_time_mix_gradients(oracle, dt, shape):
     dk, dv, dw, du, _ = oracle.backward_state(a["w"], a["u"], a["k"], a["v"], g)
     h = HALF_ULP[dt]
     f = roundoff_floor(g, a["v"])
-    fs = roundoff_floor(g, a["v"], summed=True)
     close(k.grad, dk, "dk", h, f)
     close(v.grad, dv, "dv", h, f)
     close(rr.grad, dr, "dr", h, f)
-    assert_grad_close(f64(w.grad), dw, "dw", fs)
-    assert_grad_close(f64(u.grad), du, "du", fs)
+    assert_sums_close(oracle, f64(w.grad), f64(u.grad), dw, du, a["w"], a["u"], a["k"], a["v"], g)
 
 
 def test_state_gradient_through_a_loss_on_the_state(oracle):
@@ -158,8 +157,8 @@ def test_state_gradient_through_a_loss_on_the_state(oracle):
     fs = roundoff_floor(a["dy"], a["v"], summed=True)
     assert_grad_close(f64(k.grad), dk, "dk", f)
     assert_grad_close(f64(v.grad), dv, "dv", f)
-    assert_grad_close(f64(w.grad), dw, "dw", fs)
-    assert_grad_close(f64(u.grad), du, "du", fs)
+    assert_sums_close(oracle, f64(w.grad), f64(u.grad), dw, du, a["w"], a["u"], a["k"], a["v"],
+                      a["dy"], s0, so, g_out)
     for pl in range(3):
         assert_grad_close(f64(s_in.grad)[pl], dsi[pl], f"d_state_in[{pl}]", fs)
 
@@ -198,9 +197,7 @@ def test_time_mix_block_training_path(oracle, dt):
     mu_, x_, xp_ = f64(mu_d), f64(x_d), f64(xp_d)
     dx, dxp, dmu = oracle.token_shift_backward(mu_, x_, xp_, d_mix_r)
     h = HALF_ULP[dt]
-    fs = roundoff_floor(g, mx[1], summed=True)
-    assert_grad_close(f64(w.grad), dw, "dw", fs)
-    assert_grad_close(f64(u.grad), du, "du", fs)
+    assert_sums_close(oracle, f64(w.grad), f64(u.grad), dw, du, a["w"], a["u"], mx[0], mx[1], g)
     # Each mix gradient is within (G_RTOL + 2h)|d| + G_FLOOR rms(d) + f of its
     # rounded reference (one rounding to the format on either side), dx and
     # d_x_prev add their own rounding (h), and the shift's weights mu and

@@ -20,8 +20,8 @@ import pytest
 import torch
 
 from linear_recurrent_attention_amd import synth, wkv
-from parity import (G_FLOOR, G_RTOL, assert_grad_close, assert_state_close, assert_y_close, f64,
-                    roundoff_floor)
+from parity import (G_FLOOR, G_RTOL, assert_grad_close, assert_state_close, assert_sums_close,
+                    assert_y_close, f64, roundoff_floor)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,7 +167,7 @@ def backward_ref(oracle, d, s_in, s_out, g_out):
     return oracle.backward_state(a["w"], a["u"], a["k"], a["v"], a["dy"], s_in, s_out, g_out)
 
 
-def check_grads(got, ref, d, what, dt=torch.float32):
+def check_grads(oracle, got, ref, d, what, dt=torch.float32, states=(None, None, None)):
     dy, v = f64(d["dy"]), f64(d["v"])
     f = roundoff_floor(dy, v)
     fs = roundoff_floor(dy, v, summed=True)
@@ -180,8 +180,8 @@ def check_grads(got, ref, d, what, dt=torch.float32):
         rms = float(np.sqrt(np.mean(r * r)))
         e = float(np.max(np.abs(x - r) / ((G_RTOL + h) * np.abs(r) + G_FLOOR * rms + f + 1e-300)))
         assert e <= 1.0, f"{what} {name}: {e:.3g}x the tolerance"
-    assert_grad_close(f64(got[2]), ref[2], f"{what} dw", fs)
-    assert_grad_close(f64(got[3]), ref[3], f"{what} du", fs)
+    assert_sums_close(oracle, f64(got[2]), f64(got[3]), ref[2], ref[3],
+                      *(f64(d[n]) for n in ("w", "u", "k", "v", "dy")), *states, what=what)
     if got[4] is not None:
         for pl in range(3):
             assert_grad_close(f64(got[4])[pl], ref[4][pl], f"{what} d_state_in[{pl}]", fs)
@@ -211,7 +211,8 @@ def test_backward_from_oracle_checkpoints(oracle, shape, recipe, states):
                                         d_state_out=to_dev(g_out),
                                         d_state_in=True if states else None)
     torch.cuda.synchronize()
-    check_grads(got, backward_ref(oracle, d, s_in, s_out, g_out), d, "bwd ckpt")
+    check_grads(oracle, got, backward_ref(oracle, d, s_in, s_out, g_out), d, "bwd ckpt",
+                states=(s_in, s_out, g_out))
 
 
 @pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16],
@@ -231,7 +232,7 @@ def test_training_path_forward_then_backward(oracle, dt, shape):
     got = wkv.wkv_backward_checkpointed(w, u, k, v, dy, ck)
     torch.cuda.synchronize()
     assert got[0].dtype == dt
-    check_grads(got, backward_ref(oracle, d, None, None, None), d, "train", dt)
+    check_grads(oracle, got, backward_ref(oracle, d, None, None, None), d, "train", dt)
 
 
 def test_backward_checkpointed_is_reproducible(oracle):
@@ -286,7 +287,8 @@ def test_stability_training_path_full_size_sampled(oracle):
     fs = roundoff_floor(sub["dy"], sub["v"], summed=True)
     assert_grad_close(f64(got[0])[:, :, cs], ref[0], "dk", f)
     assert_grad_close(f64(got[1])[:, :, cs], ref[1], "dv", f)
-    assert_grad_close(f64(got[2])[cs], ref[2], "dw", fs)
-    assert_grad_close(f64(got[3])[cs], ref[3], "du", fs)
+    assert_sums_close(oracle, f64(got[2])[cs], f64(got[3])[cs], ref[2], ref[3], sub["w"],
+                      sub["u"], sub["k"], sub["v"], sub["dy"], s_in[:, :, cs], s_out_sub,
+                      g_out[:, :, cs])
     for pl in range(3):
         assert_grad_close(f64(got[4])[pl][:, cs], ref[4][pl], f"d_state_in[{pl}]", fs)

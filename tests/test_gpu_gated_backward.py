@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from linear_recurrent_attention_amd import synth, wkv
-from parity import G_FLOOR, G_RTOL, assert_grad_close, f64, roundoff_floor
+from parity import G_FLOOR, G_RTOL, assert_grad_close, assert_sums_close, f64, roundoff_floor
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,7 @@ def reference(oracle, a, r, dy, s_in, s_out, g_out):
     return dk, dv, dr, dw, du, dsi, g
 
 
-def check(got, ref, a, what, dt=torch.float32):
+def check(oracle, got, ref, a, what, dt=torch.float32, states=(None, None, None)):
     dk, dv, dr, dw, du, dsi, g = ref
     f = roundoff_floor(g, a["v"])
     fs = roundoff_floor(g, a["v"], summed=True)
@@ -71,8 +71,8 @@ def check(got, ref, a, what, dt=torch.float32):
         rms = float(np.sqrt(np.mean(r * r)))
         e = float(np.max(np.abs(x - r) / ((G_RTOL + h) * np.abs(r) + G_FLOOR * rms + f + 1e-300)))
         assert e <= 1.0, f"{what} {name}: {e:.3g}x the tolerance"
-    assert_grad_close(f64(got[3]), dw, f"{what} dw", fs)
-    assert_grad_close(f64(got[4]), du, f"{what} du", fs)
+    assert_sums_close(oracle, f64(got[3]), f64(got[4]), dw, du, a["w"], a["u"], a["k"], a["v"], g,
+                      *states, what=what)
     if got[5] is not None:
         for pl in range(3):
             assert_grad_close(f64(got[5])[pl], dsi[pl], f"{what} d_state_in[{pl}]", fs)
@@ -112,7 +112,7 @@ def test_gated_backward_matches_oracle(oracle, shape, recipe, mode):
                                  d_state_in=True if mode == "states" else None)
     torch.cuda.synchronize()
     ref = reference(oracle, a, f64(r), f64(d["dy"]), s_in, s_out, g_out)
-    check(got, ref, a, f"gated {mode}")
+    check(oracle, got, ref, a, f"gated {mode}", states=(s_in, s_out, g_out))
 
 
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
@@ -134,7 +134,7 @@ def test_gated_training_path_16bit(oracle, dt, shape):
     assert got[2].dtype == dt
     a = {n: f64(d[n]) for n in ("w", "u", "k", "v")}
     ref = reference(oracle, a, f64(r), f64(d["dy"]), None, None, None)
-    check(got, ref, a, f"gated {dt}", dt)
+    check(oracle, got, ref, a, f"gated {dt}", dt)
 
 
 @pytest.mark.parametrize("rv", [800.0, -800.0], ids=["open", "closed"])
@@ -153,7 +153,8 @@ def test_gated_backward_saturated_gate(oracle, rv):
         for x in got[:5]:
             assert torch.all(x == 0)
     a = {n: f64(d[n]) for n in ("w", "u", "k", "v")}
-    check(got, reference(oracle, a, f64(r), f64(d["dy"]), None, None, None), a, f"gate {rv}")
+    check(oracle, got, reference(oracle, a, f64(r), f64(d["dy"]), None, None, None), a,
+          f"gate {rv}")
 
 
 def test_gated_stability_training_path_full_size_sampled(oracle):
@@ -174,4 +175,4 @@ def test_gated_stability_training_path_full_size_sampled(oracle):
          for n in ("w", "u", "k", "v")}
     ref = reference(oracle, a, f64(r)[:, :, cs], f64(d["dy"])[:, :, cs], None, None, None)
     sub = (got[0][:, :, cs], got[1][:, :, cs], got[2][:, :, cs], got[3][cs], got[4][cs], None)
-    check(sub, ref, a, "gated stability")
+    check(oracle, sub, ref, a, "gated stability")

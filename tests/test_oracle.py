@@ -685,3 +685,75 @@ def test_backward_state_chains_over_chunks(oracle, cut):
     np.testing.assert_allclose(first[2] + second[2], full[2], rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(first[3] + second[3], full[3], rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(first[4], full[4], rtol=1e-9, atol=1e-12)
+
+
+# Magnitudes of dw's and du's terms: the scale the GPU tests' round-off bound
+# for these cancelling sums is taken from.
+
+def _magnitude_pairwise(w, u, k, v, dy, s_in=None, s_out=None, g_state=None):
+    """The sums of wkvo_backward_magnitude written out term by term from the
+    closed form ("WKV mechanism: core computation", with the carried state's
+    weight e^{-t w}), O(T^2) per lane, no scan."""
+    B, T, C = k.shape
+    mdw, mdu = np.zeros(C), np.zeros(C)
+    for b in range(B):
+        for c in range(C):
+            wc, uc = w[c], u[c]
+            A0 = B0 = 0.0
+            if s_in is not None and s_in[1, b, c] > 0:
+                A0 = s_in[0, b, c] * np.exp(s_in[2, b, c])
+                B0 = s_in[1, b, c] * np.exp(s_in[2, b, c])
+            kk, vv, gg = k[b, :, c], v[b, :, c], np.abs(dy[b, :, c])
+            for t in range(T):
+                past = np.exp(kk[:t] - (t - 1 - np.arange(t)) * wc)
+                bonus = np.exp(uc + kk[t])
+                st = np.exp(-t * wc)
+                D = st * B0 + past.sum() + bonus
+                y = (st * A0 + (past * vv[:t]).sum() + bonus * vv[t]) / D
+                mdu[c] += gg[t] * bonus / D * (abs(vv[t]) + abs(y))
+                mdw[c] += (gg[t] * (t - 1 - np.arange(t)) * past / D * (np.abs(vv[:t]) + abs(y))).sum()
+                mdw[c] += t * gg[t] * st * (abs(A0) + abs(y) * B0) / D
+            if g_state is not None:
+                gA = g_state[0, b, c] * np.exp(-s_out[2, b, c])
+                gB = g_state[1, b, c] * np.exp(-s_out[2, b, c])
+                dist = T - 1 - np.arange(T)
+                e = np.exp(kk - dist * wc)
+                mdw[c] += (dist * e * (np.abs(gA * vv) + abs(gB))).sum()
+                mdw[c] += T * np.exp(-T * wc) * (abs(gA * A0) + abs(gB) * B0)
+    return mdw, mdu
+
+
+@pytest.mark.parametrize("recipe", [synth.GPT, synth.STABILITY])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_backward_magnitude_matches_pairwise_sums(oracle, recipe, with_state):
+    B, T, C = 2, 23, 3
+    d = synth.make(recipe, index=41, B=B, T=T, C=C, with_dy=True)
+    d = {n: t.double().numpy() for n, t in d.items()}
+    w, u, k, v, dy = d["w"], d["u"], d["k"], d["v"], d["dy"]
+    s_in = s_out = g = None
+    if with_state:
+        s_in = rand_state(oracle, 42, B, C)
+        _, s_out = oracle.forward_brute(w, u, k, v, s_in)
+        g = np.random.default_rng(43).normal(size=(3, B, C))
+    mdw, mdu = oracle.backward_magnitude(w, u, k, v, dy, s_in, s_out, g)
+    rw, ru = _magnitude_pairwise(w, u, k, v, dy, s_in, s_out, g)
+    np.testing.assert_allclose(mdw, rw, rtol=1e-10)
+    np.testing.assert_allclose(mdu, ru, rtol=1e-10)
+    # never below the gradients themselves (every term counted by size)
+    _, _, dw, du, _ = oracle.backward_state(w, u, k, v, dy, s_in, s_out, g)
+    assert np.all(mdw >= np.abs(dw) * (1 - 1e-12))
+    assert np.all(mdu >= np.abs(du) * (1 - 1e-12))
+
+
+def test_backward_magnitude_one_token_closed_form(oracle):
+    """One token from the empty state: the output is v itself (its weight is
+    the whole denominator), du's term dy (v - y) vanishes while its two parts
+    are |dy| |v| each, and there is no pair for dw."""
+    B, T, C = 3, 1, 5
+    d = synth.make(synth.STABILITY, index=44, B=B, T=T, C=C, with_dy=True)
+    w, u, k, v, dy = (d[n].double().numpy() for n in ("w", "u", "k", "v", "dy"))
+    mdw, mdu = oracle.backward_magnitude(w, u, k, v, dy)
+    np.testing.assert_allclose(mdu, 2.0 * np.sum(np.abs(dy * v), axis=(0, 1)), rtol=1e-12)
+    np.testing.assert_array_equal(mdw, np.zeros(C))
+    _, _, dw, du, _ = oracle.backward_state(w, u, k, v, dy)
+    assert np.all(np.abs(du) <= 1e-12 * mdu)
