@@ -103,7 +103,11 @@ typedef enum wkv_status {
     WKV_ERR_WORKSPACE = 5,
     WKV_ERR_UNSUPPORTED = 6,
     WKV_ERR_HIP = 7,
-    WKV_ERR_LOOKBACK = 8  /* reported by wkv_lookback_status only */
+    WKV_ERR_LOOKBACK = 8, /* reported by wkv_lookback_status only */
+    /* not a status: makes every int a value of the type (C++ otherwise limits
+       an unfixed enum to the bits its enumerators need), so a caller may pass
+       any int to wkv_status_string */
+    WKV_STATUS_MAX_ENUM = 0x7FFFFFFF
 } wkv_status;
 
 /*
@@ -300,7 +304,8 @@ WKV_API wkv_status wkv_step_gated(int64_t L, int64_t B, int64_t C, const float *
 typedef enum wkv_dtype {
     WKV_DTYPE_F32 = 0,   /* IEEE binary32 */
     WKV_DTYPE_F16 = 1,   /* IEEE binary16 */
-    WKV_DTYPE_BF16 = 2   /* bfloat16: the upper 16 bits of a binary32 */
+    WKV_DTYPE_BF16 = 2,  /* bfloat16: the upper 16 bits of a binary32 */
+    WKV_DTYPE_MAX_ENUM = 0x7FFFFFFF  /* not a format: every int is a value of the type */
 } wkv_dtype;
 
 /*

@@ -11,7 +11,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wkv.h")
-LIB = os.path.join(ROOT, "linear_recurrent_attention_amd", "libwkv.so")
+LIB = os.environ.get("WKV_ABI_TEST_LIB") or os.path.join(ROOT, "linear_recurrent_attention_amd", "libwkv.so")
 
 
 @pytest.fixture(scope="module")
