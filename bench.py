@@ -79,12 +79,36 @@ def measured_traffic(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-def host_cores() -> int:
+ORACLE_MAX_THREADS = 256
+
+
+def host_cpus():
+    """(cores this job may run on, how that was decided, online CPUs).  The
+    job's share is its affinity mask, further limited by OMP_NUM_THREADS
+    where the machine sets it (a shared host gives each GPU a share of its
+    cores that way, whatever the online count)."""
+    online = os.cpu_count() or 1
     try:
         n = len(os.sched_getaffinity(0))
+        how = "affinity mask"
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        n, how = online, "online CPUs"
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and 0 < int(omp) < n:
+        n, how = int(omp), f"OMP_NUM_THREADS (affinity mask holds {n})"
+    if n > ORACLE_MAX_THREADS:
+        n, how = ORACLE_MAX_THREADS, (how + f" holds {n}; the oracle runs at most "
+                                      f"{ORACLE_MAX_THREADS} threads")
+    return max(1, n), how, online
+
+
+def host_cores() -> int:
+    return host_cpus()[0]
+
+
+def host_description() -> dict:
+    n, how, online = host_cpus()
+    return {"cpu_model": cpu_model(), "cpus_online": online, "cores_used_from": how}
 
 
 class Timer:
@@ -106,14 +130,22 @@ class Timer:
 
 
 def cpu_model() -> str:
+    """The host CPU's model name, with its family/model/stepping numbers where
+    the name alone is generic."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    key, val = (x.strip() for x in line.split(":", 1))
+                    info.setdefault(key, val)
+                if not line.strip() and info:
+                    break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return name + (f" ({', '.join(ids)})" if ids else "")
 
 
 def timed_oracle(fn, budget_s: float):
@@ -164,7 +196,7 @@ def cpu_baseline_gpt(torch, synth, inputs_fn, budget_s: float):
             "sample": f"{layer} of the 24 seeded B=8 T=1024 C=2048 layers, whole, "
                       f"float64 O(T) {what} on {cores} threads ({elapsed:.1f} s)",
             "value_1_thread": one, "effective_gbs": done / elapsed * per_tok / 1e9,
-            "cpu_model": cpu_model()}
+            **host_description()}
 
 
 def bench_gpt(args, torch, wkv, synth, gated: bool = False, io: str = "f32"):
@@ -208,7 +240,10 @@ def bench_gpt(args, torch, wkv, synth, gated: bool = False, io: str = "f32"):
         for d in layers:
             call(d)
     torch.cuda.synchronize()
-    # per-layer timing (median of repeats), reported as the mean over layers
+    # Isolated launches: each layer alone between two events on an idle
+    # stream (median of 5, mean over layers).  Reported beside the metric, not
+    # as it: an isolated launch also pays the grid's ramp-up and drain, which
+    # back-to-back launches overlap with their neighbours.
     per_layer = []
     tm = Timer(torch, stream)
     for d in layers:
@@ -258,7 +293,14 @@ def bench_gpt(args, torch, wkv, synth, gated: bool = False, io: str = "f32"):
         "config": {"workload": ("gpt_gated_forward" if gated else "gpt_forward") +
                    ("" if io == "f32" else "_" + io), "B": B, "T": T, "C": C, "layers": NL,
                    "kernel": kname, "plan": list(chosen),
-                   "mean_over_layers_of_median_ms": sum(per_layer) / len(per_layer),
+                   "timing": "value, ms_per_step and roofline come from the timed region: "
+                             f"{args.steps} steps x {NL} layers launched back to back on one "
+                             "stream between two HIP events",
+                   "isolated_launch_ms": sum(per_layer) / len(per_layer),
+                   "isolated_launch_note": "one layer alone between two events on an idle "
+                                           "stream (median of 5, mean over the layers): adds "
+                                           "the grid's ramp-up and drain, which back-to-back "
+                                           "launches overlap",
                    "hbm_gbs": achieved, "pct_peak_hbm": 100 * achieved / PEAK_HBM_GBS,
                    "wall_ms_timed_region": wall_ms},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
