@@ -51,10 +51,17 @@
  *   - Every call is asynchronous on `stream` (0 = the default stream) and
  *     runs on the device that is current on the calling thread.  Calls on one
  *     stream run in order.
- *   - Calls may be captured into a HIP graph (on a non-default stream).  Under
- *     capture, wkv_forward uses a kernel that keeps no state between launches
- *     (the look-back kernel's per-launch tags cannot be replayed), and a plan
- *     that forces the look-back kernel returns WKV_ERR_UNSUPPORTED.
+ *   - Calls may be captured into a HIP graph (on a non-default stream).  A
+ *     look-back forward recorded under capture allocates nothing: it runs in
+ *     the device's fixed scratch (the array of wkv_forward_noalloc, see there)
+ *     and takes its per-launch tag on the device, from a one-workgroup kernel
+ *     recorded before it, so every replay is a fresh launch.  Like
+ *     wkv_forward_noalloc calls, replays of such graphs that overlap in time
+ *     on one device race on that array: callers serialise them (replays on
+ *     one stream are serialised already).  A shape whose look-back scratch
+ *     exceeds WKV_NOALLOC_SCRATCH_BYTES is recorded with a kernel that keeps
+ *     no state between workgroups under the automatic plan, and a plan that
+ *     forces the look-back kernel for it returns WKV_ERR_UNSUPPORTED.
  *   - Indexing is 64-bit: a single call may exceed 2^31 elements.
  *
  * Errors
@@ -566,8 +573,8 @@ WKV_API wkv_status wkv_token_shift_backward_typed(int64_t B, int64_t T, int64_t 
  *   - The first call on a device takes the array's address on it (which may
  *     load the library's device code, and with it the array); a caller that
  *     will capture makes one call on each device beforehand.  Under graph
- *     capture the automatic choice takes a kernel without cross-workgroup
- *     state, as for wkv_forward.
+ *     capture the launch takes its per-launch tag on the device (a
+ *     one-workgroup kernel recorded before it), as wkv_forward does there.
  * Waits that give up are reported by wkv_lookback_status on the stream of a
  * later call.
  */

@@ -75,11 +75,12 @@ int device_cus() {
 // lower it, see wkv_set_lookback_spin_limit).
 std::atomic<uint32_t> g_spin_limit{wkv::kDefaultSpinLimit};
 
-// Advances a scratch buffer's epoch after an accepted launch.  At the end of
-// the 30-bit tag range the slots (not the header) are cleared by a kernel
-// queued on the stream, so that no stale tag can match a reused epoch.
+// Advances a scratch buffer's host epoch after an accepted launch.  At the end
+// of the host's range (below the device-side range) the slots (not the header)
+// are cleared by a kernel queued on the stream, so that no stale tag can match
+// a reused epoch.
 hipError_t advance_epoch(void *p, size_t bytes, uint32_t &epoch, hipStream_t st) {
-    if (++epoch <= 0x3fffffffu) return hipSuccess;
+    if (++epoch < wkv::kDeviceEpochFirst) return hipSuccess;
     epoch = 1;
     return wkv::launch_zero_fill((char *)p + wkv::kLookbackHeaderBytes,
                                  bytes - wkv::kLookbackHeaderBytes, st);
@@ -161,7 +162,11 @@ hipError_t noalloc_address(int dev, void **out) {
     return hipSuccess;
 }
 
-hipError_t launch_with_noalloc_scratch(const FwdArgs &a, int cg, int ns, int ls, hipStream_t st) {
+// device_epoch: the call is being recorded into a graph, whose replays cannot
+// take a new host epoch each; the launch then takes its epoch on the device
+// (a one-workgroup kernel before it advances the header's device epoch).
+hipError_t launch_with_noalloc_scratch(const FwdArgs &a, int cg, int ns, int ls,
+                                       bool device_epoch, hipStream_t st) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -170,6 +175,12 @@ hipError_t launch_with_noalloc_scratch(const FwdArgs &a, int cg, int ns, int ls,
     void *p = nullptr;
     if ((e = noalloc_address(dev, &p)) != hipSuccess) return e;
     NoAllocScratch &n = g_noalloc[dev];
+    if (device_epoch) {
+        if ((e = wkv::launch_lookback_device_epoch(p, kNoAllocScratchBytes, st)) != hipSuccess)
+            return e;
+        return wkv::launch_forward_lookback(a, cg, ns, ls,
+                                            wkv::LookbackScratch{p, 0u, g_spin_limit.load()}, st);
+    }
     const wkv::LookbackScratch sc{p, n.epoch, g_spin_limit.load()};
     e = wkv::launch_forward_lookback(a, cg, ns, ls, sc, st);
     if (e == hipSuccess) e = advance_epoch(p, kNoAllocScratchBytes, n.epoch, st);
@@ -329,21 +340,20 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
         if (!state_out || state_out == state_in) return WKV_OK;
         return from_hip(wkv::launch_state_copy(lanes, state_in, state_out, stream));
     }
-    // The look-back kernel tags what it publishes with a per-launch epoch that
-    // the host advances; a captured graph would replay one epoch forever, so
-    // under stream capture the segmented kernel (no state across workgroups)
-    // runs instead, and an explicit look-back plan is refused.
+    // The look-back kernel tags what it publishes with a per-launch epoch.  A
+    // launch recorded into a graph (stream capture) takes its epoch on the
+    // device, in the device's fixed scratch, which needs no allocation; a
+    // shape whose scratch would not fit there runs the segmented kernel (no
+    // state across workgroups) under the automatic plan, and is refused under
+    // an explicit look-back plan.
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (stream != nullptr && hipStreamIsCapturing(stream, &cap) != hipSuccess)
         return WKV_ERR_HIP;
     const bool capturing = cap != hipStreamCaptureStatusNone;
-    if (p.kernel == WKV_KERNEL_AUTO) {
+    const bool auto_chosen = p.kernel == WKV_KERNEL_AUTO;
+    if (auto_chosen) {
         p = auto_plan(B, T, C, device_cus());
         if (gated) p = gated_plan(p);
-        if (capturing && p.kernel == WKV_KERNEL_LOOKBACK)
-            p = wkv_forward_plan{WKV_KERNEL_SEGMENTED, 16, 16, 64};
-    } else if (capturing && p.kernel == WKV_KERNEL_LOOKBACK) {
-        return WKV_ERR_UNSUPPORTED;
     }
     const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr, io, ck};
     if (p.kernel == WKV_KERNEL_LANE) {
@@ -354,12 +364,17 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
         const int cg = p.channels / 64;
         if (!wkv::lookback_grid_ok(B, T, C, cg, p.segments, p.seg_len)) return WKV_ERR_UNSUPPORTED;
         const size_t need = wkv::lookback_scratch_bytes(B, T, C, p.segments, p.seg_len);
-        if (noalloc) {
-            if (need > kNoAllocScratchBytes) return WKV_ERR_WORKSPACE;
-            return from_hip(launch_with_noalloc_scratch(a, cg, p.segments, p.seg_len, stream));
+        if (noalloc || capturing) {
+            if (need <= kNoAllocScratchBytes)
+                return from_hip(
+                    launch_with_noalloc_scratch(a, cg, p.segments, p.seg_len, capturing, stream));
+            if (noalloc) return WKV_ERR_WORKSPACE;
+            if (!auto_chosen) return WKV_ERR_UNSUPPORTED;
+            p = wkv_forward_plan{WKV_KERNEL_SEGMENTED, 16, 16, 64};
+        } else {
+            if (need > kLookbackScratchMax) return WKV_ERR_UNSUPPORTED;
+            return from_hip(launch_with_scratch(a, cg, p.segments, p.seg_len, need, stream));
         }
-        if (need > kLookbackScratchMax) return WKV_ERR_UNSUPPORTED;
-        return from_hip(launch_with_scratch(a, cg, p.segments, p.seg_len, need, stream));
     }
     if (B * ((C + p.channels - 1) / p.channels) > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
     return from_hip(wkv::launch_forward_seg(a, p.segments, p.seg_len, p.channels, stream));

@@ -87,15 +87,30 @@ hipError_t launch_state_copy(int64_t lanes, const float *s_in, float *s_out, hip
 hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t st);
 
 // forward with decoupled look-back (wkv_lookback.hip)
-// The scratch starts with a header of kLookbackHeaderBytes: a 32-bit count of
-// look-back waits that gave up (the kernel adds to it; the host reads and
-// clears it), then the slot arrays.
+// The scratch starts with a header of kLookbackHeaderBytes: word 0 a 32-bit
+// count of look-back waits that gave up (the kernel adds to it; the host reads
+// and clears it), word 1 the epoch of the last launch that took its epoch on
+// the device (see below), then the slot arrays.
 constexpr size_t kLookbackHeaderBytes = 256;
+// Epochs tag what a launch publishes, so that no launch mistakes a slot left
+// by an earlier one for its own.  Epochs the host hands out stay below
+// kDeviceEpochFirst; a launch recorded into a graph cannot take a new epoch
+// from the host at each replay, so it takes one on the device instead: a
+// one-workgroup kernel queued before it advances header word 1 through
+// [kDeviceEpochFirst, kDeviceEpochLast] (clearing the slots when the range
+// wraps), and the forward kernel, given epoch 0, reads that word.  The two
+// ranges never meet, so host-epoch and device-epoch launches can share one
+// buffer.
+constexpr uint32_t kDeviceEpochFirst = 0x30000000u;
+constexpr uint32_t kDeviceEpochLast = 0x3fffffffu;  // tags hold 30 bits of epoch
 struct LookbackScratch {
     void *base;           // header then slots; zero-initialised before first use
-    uint32_t epoch;       // distinct for every launch on it, never 0
+    uint32_t epoch;       // distinct for every launch on it; 0: read header word 1
     uint32_t spin_limit;  // look-back rounds without progress before a wait gives up
 };
+// Queues the device-side epoch advance for a buffer of `bytes` (the header
+// included) on st.
+hipError_t launch_lookback_device_epoch(void *base, size_t bytes, hipStream_t st);
 // Default spin limit: 2^16 rounds of a sleep and a device-scope load, tens of
 // milliseconds, far above any wait in a healthy launch.
 constexpr uint32_t kDefaultSpinLimit = 1u << 16;

@@ -39,7 +39,8 @@
 // blocks before its own, so the earliest unfinished workgroup never waits on
 // one that has not started, and the look-back always terminates.  The host
 // gives each launch a fresh epoch (per scratch buffer), so nothing on the
-// device has to be reset between launches.  Every spin is bounded as well:
+// device has to be reset between launches; a launch replayed from a graph
+// takes its epoch from a word that a tiny kernel before it advances.  Every spin is bounded as well:
 // past the bound the wait gives up, the block's outputs become NaN, the
 // inclusive state it publishes carries the NaN to every later block of the
 // sequence and to the final state, and a counter in the scratch header records
@@ -329,6 +330,9 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
     uint32_t spin_limit, uint32_t nsets) {
     constexpr int TB = NS * LS;
     __shared__ LbShared<CG, NS> sh;
+    // epoch 0: the launch's epoch is header word 1, advanced on the device by
+    // the kernel queued before this one (uniform: one read per wave)
+    if (epoch == 0) epoch = __builtin_amdgcn_readfirstlane(giveups[1]);
     LbWave q;
     q.lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -497,6 +501,32 @@ hipError_t launch_lb_gate(const FwdArgs &a, const LookbackScratch &sc, hipStream
     // (a gated call never reaches LS > 16: forward_lookback_supported refuses it)
     if (a.r) return launch_lb<CG, NS, (LS <= 16 ? LS : 16), true, IO>(a, sc, st);
     return launch_lb<CG, NS, LS, false, IO>(a, sc, st);
+}
+
+// One workgroup: every thread reads the last device epoch before thread 0
+// writes the next; when the range is used up the slots are cleared first
+// (vector stores), so that no tag left from the previous pass through the
+// range can match.  Word 1 starts at 0 in a fresh buffer, whose slots hold
+// no device-range tag, so the first epoch needs no clearing.
+__global__ __launch_bounds__(256) void lookback_epoch_kernel(uint32_t *hdr, uint4 *slots,
+                                                             size_t n16) {
+    const uint32_t e = __hip_atomic_load(hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool wrap = e >= kDeviceEpochLast;
+    __syncthreads();
+    if (wrap)
+        for (size_t i = threadIdx.x; i < n16; i += blockDim.x) slots[i] = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(hdr + 1, (e < kDeviceEpochFirst || wrap) ? kDeviceEpochFirst : e + 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_lookback_device_epoch(void *base, size_t bytes, hipStream_t st) {
+    if (bytes < kLookbackHeaderBytes || (bytes - kLookbackHeaderBytes) % 16 != 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lookback_epoch_kernel, dim3(1), dim3(256), 0, st, (uint32_t *)base,
+                       (uint4 *)((char *)base + kLookbackHeaderBytes),
+                       (bytes - kLookbackHeaderBytes) / 16);
+    return hipGetLastError();
 }
 
 hipError_t launch_forward_lookback(const FwdArgs &a, int cg, int ns, int ls,

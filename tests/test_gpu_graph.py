@@ -1,6 +1,9 @@
 """HIP graph capture of the library's calls: every replay of a captured graph
-matches the eager result (the look-back kernel, whose launches are tagged by
-the host, is replaced by a stateless kernel under capture)."""
+matches the eager result.  A look-back forward recorded under capture runs in
+the device's fixed scratch and takes its per-launch tag on the device, so each
+replay is a fresh launch; eager calls between replays (wkv_forward on its own
+scratch, wkv_forward_noalloc on the same fixed array with host tags) must not
+disturb it."""
 import numpy as np
 import pytest
 import torch
@@ -56,20 +59,119 @@ def test_captured_forward_replays_match_eager(shape):
         assert np.all(np.isfinite(sg[:2])), f"replay {rep}: non-finite state"
 
 
-def test_forced_lookback_is_refused_under_capture():
+def _close(got, ref, what):
+    yr, yg = ref.double().cpu().numpy(), got.double().cpu().numpy()
+    assert np.all(np.isfinite(yg)), f"{what}: non-finite"
+    assert np.max(np.abs(yg - yr) / (1e-5 + 1e-4 * np.abs(yr))) <= 1.0, what
+
+
+@pytest.mark.parametrize("shape", [(8, 1024, 2048), (1, 1024, 5120), (3, 300, 130)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_forced_lookback_under_capture_takes_device_epochs(shape):
+    """A forced look-back plan recorded under capture, replayed 6 times with
+    eager wkv_forward_noalloc calls (host-tagged launches on the same fixed
+    array) and a carried-state chain between the replays."""
+    B, T, C = shape
     dev = torch.device("cuda")
-    d = synth.make(synth.TINY, index=3, B=1, T=64, C=64, device=dev)
+    d = synth.make(synth.GPT, index=32, B=B, T=T, C=C, device=dev)
+    e = synth.make(synth.GPT, index=33, B=B, T=T, C=C, device=dev)
+    plan = (wkv.WKV_KERNEL_LOOKBACK, 4, 16)
+    y_ref, s_ref = wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], state_out=True, plan=plan)
+    ye_ref, _ = wkv.wkv_forward(e["w"], e["u"], e["k"], e["v"], state_in=s_ref, state_out=True,
+                                plan=plan)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    y, so = torch.empty_like(d["k"]), torch.empty((3, B, C), device=dev)
+    ye = torch.empty_like(e["k"])
+
+    def chain():
+        wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=y, state_out=so, stream=side, plan=plan)
+        wkv.wkv_forward(e["w"], e["u"], e["k"], e["v"], y=ye, state_in=so, stream=side, plan=plan)
+
+    g = _capture(chain, side)
+    for rep in range(6):
+        y.fill_(float("nan"))
+        ye.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        side.synchronize()
+        _close(y, y_ref, f"replay {rep} first chunk")
+        _close(ye, ye_ref, f"replay {rep} second chunk")
+        # host-tagged launches on the same fixed array between replays
+        yn = torch.empty_like(e["k"])
+        wkv.wkv_forward_noalloc(e["w"], e["u"], e["k"], e["v"], yn)
+        torch.cuda.synchronize()
+    assert wkv.wkv_lookback_status(side) == wkv.WKV_OK
+
+
+def test_captured_lookback_gated_bf16_with_checkpoints():
+    """The training forward (gated, bf16 activations, 128-token checkpoints)
+    on a forced look-back plan, recorded under capture: replays match the
+    eager call within the 16-bit tolerance, checkpoints within the float one."""
+    B, T, C = 4, 1000, 192
+    dev = torch.device("cuda")
+    d = synth.make(synth.STABILITY, index=35, B=B, T=T, C=C, device=dev)
+    r = synth.receptance(synth.STABILITY, 35, (B, T, C), device=dev).to(torch.bfloat16)
+    k, v = d["k"].to(torch.bfloat16), d["v"].to(torch.bfloat16)
+    plan = (wkv.WKV_KERNEL_LOOKBACK, 4, 16)
+    y_ref, s_ref, ck_ref = wkv.wkv_forward_checkpointed(d["w"], d["u"], k, v, r=r,
+                                                        state_out=True, plan=plan)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    y, so = torch.empty_like(k), torch.empty((3, B, C), device=dev)
+    ck = torch.empty_like(ck_ref)
+    g = _capture(lambda: wkv.wkv_forward_checkpointed(d["w"], d["u"], k, v, r=r, y=y,
+                                                       state_out=so, checkpoints=ck,
+                                                       stream=side, plan=plan), side)
+    # both sides rounded to bf16 once from float32 values within the float
+    # tolerance of each other: at most one unit in the last place apart, which
+    # is 2^-7 relative at the bottom of a binade
+    h = 2.0 ** -7
+    for rep in range(4):
+        y.fill_(float("nan"))
+        ck.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        side.synchronize()
+        yr, yg = y_ref.double().cpu().numpy(), y.double().cpu().numpy()
+        assert np.all(np.isfinite(yg)), f"replay {rep}: non-finite y"
+        assert np.max(np.abs(yg - yr) / (1e-5 + (1e-4 + h) * np.abs(yr))) <= 1.0, f"replay {rep}"
+        cr, cg = ck_ref.double().cpu().numpy(), ck.double().cpu().numpy()
+        # the a, b planes at one frame (o) agree up to rounding of the frame
+        m_r, m_g = cr[:, 0] / cr[:, 1], cg[:, 0] / cg[:, 1]
+        assert np.max(np.abs(m_g - m_r) / (1e-5 + 1e-4 * np.abs(m_r))) <= 1.0, f"replay {rep}"
+
+
+def test_oversize_lookback_under_capture():
+    """A shape whose look-back scratch exceeds the fixed array: a forced
+    look-back plan is refused under capture, and the automatic plan records
+    the segmented kernel, whose replays match the eager (look-back) result."""
+    B, T, C = 8, 16384, 2048
+    need = wkv.wkv_forward_scratch_size(B, T, C)
+    assert need > wkv.WKV_NOALLOC_SCRATCH_BYTES
+    dev = torch.device("cuda")
+    d = synth.make(synth.GPT, index=34, B=B, T=T, C=C, device=dev)
+    y_ref, _ = wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"])
+    torch.cuda.synchronize()
     side = torch.cuda.Stream()
     y = torch.empty_like(d["k"])
     with torch.cuda.stream(side):
         wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=y, stream=side,
-                        plan=(wkv.WKV_KERNEL_LOOKBACK, 4, 16))
+                        plan=(wkv.WKV_KERNEL_SEGMENTED, 16, 16))
     side.synchronize()
     g = torch.cuda.CUDAGraph()
     with pytest.raises(wkv.WkvError, match="status 6"):
         with torch.cuda.graph(g, stream=side):
             wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=y, stream=side,
-                            plan=(wkv.WKV_KERNEL_LOOKBACK, 4, 16))
+                            plan=(wkv.WKV_KERNEL_LOOKBACK, 4, 32))
+    g = _capture(lambda: wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], y=y, stream=side),
+                 side)
+    for rep in range(2):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        side.synchronize()
+        _close(y, y_ref, f"replay {rep}")
 
 
 def _capture(fn, side):
@@ -85,8 +187,8 @@ def _capture(fn, side):
 def test_captured_time_mixing_calls_replay_exactly():
     """Token shift, gated step, typed (bf16) forward and the backward with
     carried states, captured together: each replay reproduces the eager bits
-    (none of these uses state shared across launches; the forward under
-    capture is the segmented kernel, bitwise reproducible)."""
+    (none of these uses state shared across launches; the forward is forced
+    to the segmented kernel, which is bitwise reproducible)."""
     dev = torch.device("cuda")
     B, T, C, L = 2, 300, 128, 3
     side = torch.cuda.Stream()
