@@ -31,6 +31,7 @@ workloads with extra measurements, not the headline:
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -112,20 +113,29 @@ def host_description() -> dict:
 
 
 class Timer:
-    """HIP events on the stream the kernels are launched on."""
+    """HIP events on the stream the kernels are launched on.  Python's cyclic
+    garbage collector is paused between start and stop: a full collection in a
+    process holding torch takes about 30 ms of host time, during which no
+    launch is issued and the GPU drains its queue and idles inside the timed
+    region (measured: one such pause tripled a batch of 120 gpt launches)."""
 
     def __init__(self, torch, stream):
         self.torch = torch
         self.stream = stream
         self.a = torch.cuda.Event(enable_timing=True)
         self.b = torch.cuda.Event(enable_timing=True)
+        self.gc_was_enabled = False
 
     def start(self):
+        self.gc_was_enabled = gc.isenabled()
+        gc.disable()
         self.a.record(self.stream)
 
     def stop_ms(self):
         self.b.record(self.stream)
         self.b.synchronize()
+        if self.gc_was_enabled:
+            gc.enable()
         return self.a.elapsed_time(self.b)
 
 
