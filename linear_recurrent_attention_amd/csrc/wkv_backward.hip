@@ -122,6 +122,48 @@ __device__ __forceinline__ void rev_compose(Rev &e, const Rev &l, float W, float
     e.m = late_big ? lm : e.m;
 }
 
+// Summary of LS whole tokens from the empty state in one frame: the largest
+// decayed exponent x_t = K_t - (LS-1-t) W of the segment at its last token,
+// one exponential per token and no rescaling.
+template <int LS>
+__device__ __forceinline__ Lane seg_summary_fixed(const float (&K)[LS], const float (&V)[LS],
+                                                  float W) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < LS; ++t) M = fmaxf(M, fmaf((float)(t - (LS - 1)), W, K[t]));
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int t = 0; t < LS; ++t) {
+        const float e = ex2(fmaf((float)(t - (LS - 1)), W, K[t]) - M);
+        sa = fmaf(e, V[t], sa);
+        sb += e;
+    }
+    return Lane{sa, sb, M, 0.0f};
+}
+
+// Reverse summary of LS whole tokens (outputs t0..t0+LS-1) seen from before
+// the first, from the empty state, in one frame: output j enters R with the
+// weight 2^{x_j}, x_j = -lambda_j - j W, and R', S' with j times it; the frame
+// is the largest x_j, so each token costs one exponential and no rescaling.
+template <int LS>
+__device__ __forceinline__ Rev rev_summary_fixed(const float (&G)[LS], const float (&Y)[LS],
+                                                 const float (&LAM)[LS], float W) {
+    float F = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < LS; ++j) F = fmaxf(F, fmaf(-(float)j, W, -LAM[j]));
+    float R = 0.0f, S = 0.0f, R1 = 0.0f, S1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < LS; ++j) {
+        const float ge = G[j] * ex2(fmaf(-(float)j, W, -LAM[j]) - F);
+        const float gy = ge * Y[j];
+        R += ge;
+        S += gy;
+        R1 = fmaf((float)j, ge, R1);
+        S1 = fmaf((float)j, gy, S1);
+    }
+    return Rev{R, S, R1, S1, F, 0.0f};
+}
+
 template <int NW>
 struct BwdShared {
     float f[2][4][NW][64];
@@ -260,9 +302,13 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 load_seg<LS>(Vn, rows(vseq, t0 + TT), t0 + TT, T);
             }
             Lane S = lane_empty();
+            if constexpr (FULL) {
+                S = seg_summary_fixed<LS>(Kc, Vc, ch.W);
+            } else {
 #pragma unroll
-            for (int j = 0; j < LS; ++j)
-                if (FULL || t0 + j < T) absorb(S, Kc[j], Vc[j], ch);
+                for (int j = 0; j < LS; ++j)
+                    if (t0 + j < T) absorb(S, Kc[j], Vc[j], ch);
+            }
             int buf = 0;
 #pragma unroll
             for (int d = 1; d < NW; d <<= 1) {
@@ -373,9 +419,13 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 }
                 // this segment's summary, scanned over the tile's segments
                 Lane S = lane_empty();
+                if constexpr (FULL) {
+                    S = seg_summary_fixed<LS>(Kc, Vc, ch.W);
+                } else {
 #pragma unroll
-                for (int j = 0; j < LS; ++j)
-                    if (FULL || t0 + j < T) absorb(S, Kc[j], Vc[j], ch);
+                    for (int j = 0; j < LS; ++j)
+                        if (t0 + j < T) absorb(S, Kc[j], Vc[j], ch);
+                }
                 int fb = 0;
 #pragma unroll
                 for (int d = 1; d < NW; d <<= 1) {
@@ -422,10 +472,14 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         const bool seeded = ds_out && tile == ntiles - 1 && t0 <= T - 1 && T - 1 < t0 + LS;
         // local backward summary of this segment
         Rev z = rev_empty();
-        if (seeded) z = seed_of();
+        if (FULL && !seeded) {
+            z = rev_summary_fixed<LS>(Gc, Y, LAM, ch.W);
+        } else {
+            if (seeded) z = seed_of();
 #pragma unroll
-        for (int j = LS - 1; j >= 0; --j)
-            if (FULL || t0 + j < T) rev_absorb(z, Gc[j], Y[j], LAM[j], ch.W);
+            for (int j = LS - 1; j >= 0; --j)
+                if (FULL || t0 + j < T) rev_absorb(z, Gc[j], Y[j], LAM[j], ch.W);
+        }
         // inclusive scan from the last segment backward (Hillis-Steele)
         int buf = 0;
 #pragma unroll
