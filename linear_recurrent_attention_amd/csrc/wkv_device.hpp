@@ -181,15 +181,18 @@ __device__ __forceinline__ void compose(Lane &X, const Lane &Y, float W, float l
 //
 // Valid when no term that is the largest present at its own time sits more
 // than 100 below F (else it could underflow): the present maximum only grows,
-// so it suffices that max(G, x_0) >= F - 100.  seg_frame() returns whether
-// that holds for this lane.
+// so it suffices that max(G, x_0) >= F - 100.  The first token's denominator
+// B + c1 E_0 must also be a normal float (every later one is larger): with an
+// empty or nearly empty state and a small bonus c1 it can fall below float's
+// normal range, where the reciprocal flushes it to zero.  seg_frame() returns
+// whether both hold for this lane.
 struct SegFrame {
     float Ae, An;       // anchor of F: F = Ae - An W
     float alpha, beta;  // R's sums in frame F
 };
 
-__device__ __forceinline__ bool seg_frame(const Lane &R, const Lane &S, float W, float len,
-                                          float K0, SegFrame &f) {
+__device__ __forceinline__ bool seg_frame(const Lane &R, const Lane &S, float W, float c1,
+                                          float len, float K0, SegFrame &f) {
     const float nR = R.n + len;
     const float D = fmaf(-(nR - S.n), W, R.e0 - S.e0);  // G - max x_t
     const bool g = D >= 0.0f;
@@ -199,7 +202,8 @@ __device__ __forceinline__ bool seg_frame(const Lane &R, const Lane &S, float W,
     f.alpha = R.a * sc;
     f.beta = R.b * sc;
     const float d0 = fmaf(f.An - (len - 1.0f), W, K0 - f.Ae);  // x_0 - F
-    return fmaxf(D, d0) >= -100.0f;
+    const float den0 = fmaf(c1, ex2(d0), f.beta);
+    return fmaxf(D, d0) >= -100.0f && den0 >= 0x1p-100f;
 }
 
 // Token t (0-based within the segment of `len` tokens) in the frame of f.

@@ -278,7 +278,7 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
         bool framed = false;
         if constexpr (FULL && !SAFE) {
             SegFrame f;
-            const bool ok = seg_frame(R, lds_lane(sh.s, s, g, lane), ch.W, (float)LS,
+            const bool ok = seg_frame(R, lds_lane(sh.s, s, g, lane), ch.W, ch.c1, (float)LS,
                                       K[0], f);
             if (__all(ok || !q.active)) {
                 framed = true;

@@ -144,6 +144,35 @@ def test_extreme_bonus_takes_the_two_exponential_path(oracle, plan):
     assert_state_close(f64(so), sr)
 
 
+@pytest.mark.parametrize("plan", list(PLANS))
+@pytest.mark.parametrize("with_state", [False, True], ids=["empty", "tiny_state"])
+def test_small_bonus_first_token_below_the_segment_maximum(oracle, plan, with_state):
+    """A bonus near the one-exponential step's lower limit (u down to -59 with
+    w = 0.01) and a key 45 above the first token's a few tokens later, from
+    the empty state or from a state whose denominator is tiny: a frame taken
+    at the segment's largest exponent puts the first token's denominator
+    below float's normal range, so such a segment must take the token-by-token
+    path (the output of a first token from the empty state is its own v)."""
+    B, T, C = 2, 192, 64
+    w = torch.full((C,), 0.01)
+    u = torch.linspace(-30.0, -59.0, C)
+    k = torch.zeros(B, T, C)
+    k[:, 5::64, :] = 45.0
+    v = synth.normal((B, T, C), 1.0, synth.seed_of(synth.TINY, 700, 0))
+    d = dict(w=w, u=u, k=k, v=v)
+    si = None
+    if with_state:
+        si = torch.zeros(3, B, C)
+        si[1] = 1e-30
+        si[2] = -5.0
+    note(f"small bonus, first token low, plan={plan} state={with_state}")
+    y, so = run(d, PLANS[plan], si)
+    yr, sr = oracle.forward_scan(*(f64(d[n]) for n in ("w", "u", "k", "v")),
+                                 None if si is None else f64(si))
+    assert_y_close(f64(y), yr)
+    assert_state_close(f64(so), sr)
+
+
 @pytest.mark.parametrize("plan", ["auto", "lane", "seg16x16", "seg16x16c32", "lb4x16", "lb8x8",
                                   "lb2x16c256"])
 def test_state_updated_in_place(oracle, plan):
