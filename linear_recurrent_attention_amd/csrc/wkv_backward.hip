@@ -286,7 +286,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         // the carried state: every wave folds it into its segments' starting states
         Lane carry = lane_empty();
         if (s_in && active)
-            carry = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
+            carry = lane_in(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
                             o_in(s_in[(2 * B + bb) * C + c]));
         // keys in log2 units, scaled where each prefetched tile is handed over
         float Kc[LS], Vc[LS];
@@ -440,7 +440,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 }
                 fwd_put(sh, fb, s, lane, S);
                 __syncthreads();
-                L = lane_at(a0, b0, o0);
+                L = lane_in(a0, b0, o0);
                 if (s > 0) compose(L, fwd_get(sh, fb, s - 1, lane), ch.W, (float)(s * LS));
             } else {
                 const float *q = ck + ((tile * NW + s) * 4) * 64 + lane;

@@ -68,6 +68,16 @@ struct Lane {
 };
 
 __device__ __forceinline__ Lane lane_at(float a, float b, float o) { return Lane{a, b, o, 0.0f}; }
+
+// A carried state as the ABI hands it in (o2 = o log2 e).  A state is defined
+// up to a common scale, so one whose denominator b lies far from 1 is first
+// rescaled to b = 1 (o2 += log2 b): with b = 1e-30, say, the products the
+// step forms with a small bonus would leave float's normal range.  States the
+// kernels write have b near 1 or above and pass unchanged.
+__device__ __forceinline__ Lane lane_in(float a, float b, float o2) {
+    if (b > 0.0f && (b < 0x1p-20f || b > 0x1p20f)) return Lane{a * rcp(b), 1.0f, o2 + lg2(b), 0.0f};
+    return Lane{a, b, o2, 0.0f};
+}
 __device__ __forceinline__ Lane lane_empty() { return Lane{0.0f, 0.0f, kEmpty2, 0.0f}; }
 // Frame exponent of the sums after the last token.
 __device__ __forceinline__ float lane_o(const Lane &L, float W) { return fmaf(-L.n, W, L.e0); }
@@ -184,15 +194,18 @@ __device__ __forceinline__ void compose(Lane &X, const Lane &Y, float W, float l
 // so it suffices that max(G, x_0) >= F - 100.  The first token's denominator
 // B + c1 E_0 must also be a normal float (every later one is larger): with an
 // empty or nearly empty state and a small bonus c1 it can fall below float's
-// normal range, where the reciprocal flushes it to zero.  seg_frame() returns
-// whether both hold for this lane.
+// normal range, where the reciprocal flushes it to zero.  And with a large
+// bonus (c1 > 1) a token far below F still matters through c1 E_t although
+// E_t alone would flush, so then every x_t (the smallest, xmin) must lie
+// within 100 of F.  seg_frame() returns whether all of this holds for this
+// lane.
 struct SegFrame {
     float Ae, An;       // anchor of F: F = Ae - An W
     float alpha, beta;  // R's sums in frame F
 };
 
 __device__ __forceinline__ bool seg_frame(const Lane &R, const Lane &S, float W, float c1,
-                                          float len, float K0, SegFrame &f) {
+                                          float len, float K0, float xmin, SegFrame &f) {
     const float nR = R.n + len;
     const float D = fmaf(-(nR - S.n), W, R.e0 - S.e0);  // G - max x_t
     const bool g = D >= 0.0f;
@@ -203,7 +216,8 @@ __device__ __forceinline__ bool seg_frame(const Lane &R, const Lane &S, float W,
     f.beta = R.b * sc;
     const float d0 = fmaf(f.An - (len - 1.0f), W, K0 - f.Ae);  // x_0 - F
     const float den0 = fmaf(c1, ex2(d0), f.beta);
-    return fmaxf(D, d0) >= -100.0f && den0 >= 0x1p-100f;
+    const float dmin = fmaf(f.An, W, xmin - f.Ae);  // xmin - F
+    return fmaxf(D, d0) >= -100.0f && den0 >= 0x1p-100f && (c1 <= 1.0f || dmin >= -100.0f);
 }
 
 // Token t (0-based within the segment of `len` tokens) in the frame of f.

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void fwd_lane_kernel(int64_t B, int64_t T, int
 
     Lane L = lane_empty();
     if (s_in)
-        L = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
+        L = lane_in(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
                     o_in(s_in[(2 * B + bb) * C + c]));
     const int64_t base = bb * T * C + c;
     const typename IO::T *rp = GATE ? r + base : nullptr;
@@ -297,7 +297,7 @@ __device__ __forceinline__ void seg_body(int64_t B, int64_t T, int64_t C, int64_
     // carry: the state before the current tile
     Lane carry = lane_empty();
     if (s_in && active)
-        carry = lane_at(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
+        carry = lane_in(s_in[(0 * B + bb) * C + c], s_in[(1 * B + bb) * C + c],
                         o_in(s_in[(2 * B + bb) * C + c]));
 
     float KA[LS], VA[LS], KB[LS], VB[LS], Rc[NR];

@@ -146,10 +146,15 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
     // token costs one exponential and no rescaling (the sums are anchored at
     // that exponent with no decay steps yet).
     Lane S = lane_empty();
+    float xmin = INFINITY;  // smallest x_t (the one-frame re-sweep's bonus check)
     if constexpr (FULL) {
         float M = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < LS; ++t) M = fmaxf(M, fmaf((float)(t - (LS - 1)), ch.W, K[t]));
+        for (int t = 0; t < LS; ++t) {
+            const float x = fmaf((float)(t - (LS - 1)), ch.W, K[t]);
+            M = fmaxf(M, x);
+            xmin = fminf(xmin, x);
+        }
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int t = 0; t < LS; ++t) {
@@ -181,7 +186,7 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
         // update) as soon as that state is visible, and it depends on the values
         // read here
         if (s == 0 && s_in && q.active)
-            P = lane_at(s_in[(0 * B + q.bb) * C + q.c], s_in[(1 * B + q.bb) * C + q.c],
+            P = lane_in(s_in[(0 * B + q.bb) * C + q.c], s_in[(1 * B + q.bb) * C + q.c],
                         o_in(s_in[(2 * B + q.bb) * C + q.c]));
         if (s == 0) lds_put(sh.pv, 0, g, lane, P);
         __syncthreads();
@@ -279,7 +284,7 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
         if constexpr (FULL && !SAFE) {
             SegFrame f;
             const bool ok = seg_frame(R, lds_lane(sh.s, s, g, lane), ch.W, ch.c1, (float)LS,
-                                      K[0], f);
+                                      K[0], xmin, f);
             if (__all(ok || !q.active)) {
                 framed = true;
                 float A = f.alpha, Bs = f.beta;

@@ -20,17 +20,47 @@ namespace wkv {
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 // (a, b, o) is the ABI state of one lane (o in natural-log units).
+//
+// The step runs once per token, so the state it hands on must not drift.
+// Writing o' = o - w at every token would round o each time, in the same
+// direction for similar values: after a few hundred tokens with |o| ~ 60 and
+// a slow decay the log-weight is off by more than 1e-4.  So o is written
+// back unchanged unless this token became the frame (then o' = k, exactly
+// the input), and the decay e^{-w} goes into a and b, whose roundings are
+// relative and do not add up that way.  When b has decayed below 2^-20 the
+// state is rescaled to b = 1, one rounding of o every 20/w tokens or so.
 __device__ __forceinline__ float step_one(float &a, float &b, float &o, float k, float v,
                                           float w, float u) {
     Chan ch;
     ch.W = w * kLog2e;
     ch.U = u * kLog2e;
     ch.c1 = 0.0f;  // unused by the two-exponential step
-    Lane L = lane_at(a, b, o_in(o));
-    const float y = step_safe(L, k * kLog2e, v, ch);
-    a = L.a;
-    b = L.b;
-    o = o_out(lane_o(L, ch.W));
+    const float o2 = o_in(o);
+    Lane L = lane_in(a, b, o2);
+    const bool rescaled = L.e0 != o2;  // a far-off b was brought to 1 on the way in
+    const float K = k * kLog2e;
+    const float y = step_safe(L, K, v, ch);
+    if (L.n == 0.0f) {
+        // this token is the new frame: the sums are relative to 2^K
+        a = L.a;
+        b = L.b;
+        o = k;
+    } else {
+        // one decay step past the frame e0: fold it into the sums
+        const float d = ex2(-ch.W);
+        float an = L.a * d, bn = L.b * d, e0 = L.e0;
+        bool moved = rescaled;
+        if (bn < 0x1p-20f) {
+            const float r = rcp(bn);
+            e0 += lg2(bn);
+            an *= r;
+            bn = 1.0f;
+            moved = true;
+        }
+        a = an;
+        b = bn;
+        if (moved) o = o_out(e0);
+    }
     return y;
 }
 
