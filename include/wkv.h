@@ -154,8 +154,9 @@ WKV_API wkv_status wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, 
  * The state handed on is the same state as wkv_forward's (equal in the
  * canonical a/b and o + ln b) but kept so that it does not drift over many
  * steps: o stays as it was unless the token became the largest term (then
- * o = k exactly), the decay e^{-w} is folded into a and b, and the state is
- * rescaled to b = 1 only when b has decayed below 2^-20.
+ * o = k exactly), the decay e^{-w} is folded into a and b, and when b has
+ * decayed below 2^-20, o moves down by a whole number of units (exactly) and
+ * a, b are rescaled to match.
  */
 WKV_API wkv_status wkv_step(int64_t L, int64_t B, int64_t C, const float *w, const float *u,
                             const float *k, const float *v, float *y, const float *state_in,

@@ -27,8 +27,9 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // a slow decay the log-weight is off by more than 1e-4.  So o is written
 // back unchanged unless this token became the frame (then o' = k, exactly
 // the input), and the decay e^{-w} goes into a and b, whose roundings are
-// relative and do not add up that way.  When b has decayed below 2^-20 the
-// state is rescaled to b = 1, one rounding of o every 20/w tokens or so.
+// relative and do not add up that way.  When b has decayed below 2^-20, o
+// moves down by a whole number m of natural-log units (exact: o is never
+// rounded) and a, b take the factor e^{-m}, which brings b back to [1, e).
 __device__ __forceinline__ float step_one(float &a, float &b, float &o, float k, float v,
                                           float w, float u) {
     Chan ch;
@@ -48,18 +49,18 @@ __device__ __forceinline__ float step_one(float &a, float &b, float &o, float k,
     } else {
         // one decay step past the frame e0: fold it into the sums
         const float d = ex2(-ch.W);
-        float an = L.a * d, bn = L.b * d, e0 = L.e0;
-        bool moved = rescaled;
+        float an = L.a * d, bn = L.b * d;
+        float on = rescaled ? o_out(L.e0) : o;
         if (bn < 0x1p-20f) {
-            const float r = rcp(bn);
-            e0 += lg2(bn);
-            an *= r;
-            bn = 1.0f;
-            moved = true;
+            const float m = floorf(lg2(bn) * kLn2);  // whole natural-log units, <= -14
+            const float sc = ex2(-m * kLog2e);
+            an *= sc;
+            bn *= sc;
+            on += m;
         }
         a = an;
         b = bn;
-        if (moved) o = o_out(e0);
+        o = on;
     }
     return y;
 }

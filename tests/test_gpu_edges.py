@@ -9,8 +9,12 @@ float's range while the inputs are valid (w > 0, finite):
 - rising:  keys rising from -40 to +40, so the first token is far below it;
 - edge:    bonuses at both ends of the one-exponential range and just past
   them (|u - w| around 86 in log2 units), with fast and slow decays;
-- tiny:    a carried state with denominator 1e-30 and a large exponent.
+- tiny:    a carried state with denominator 1e-30 and a large exponent;
+- huge:    keys of +-200 (far past e^k's float range; only differences of
+  exponents are ever formed), decays from 1e-3 to 5.
 Bonuses span -59 to +59 across the channels of every case but "edge".
+The gated forward with bf16 activations runs the same cases on the look-back
+and segmented plans.
 """
 import sys
 
@@ -38,7 +42,7 @@ PLANS = {
     "lb8x8": (wkv.WKV_KERNEL_LOOKBACK, 8, 8),
     "lb2x16c128": (wkv.WKV_KERNEL_LOOKBACK, 2, 16, 128),
 }
-CASES = ["spikes", "falling", "rising", "edge", "tiny"]
+CASES = ["spikes", "falling", "rising", "edge", "tiny", "huge"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -83,6 +87,10 @@ def make(case):
         s_in[1] = 1e-30
         s_in[2] = 40.0
         k[:, 10::64, :] = -30.0
+    elif case == "huge":
+        w = torch.linspace(1e-3, 5.0, C)
+        k[:, 4::41, :] = 200.0
+        k[:, 25::41, :] = -200.0
     return w.float(), u.float(), k, v, dy, s_in
 
 
@@ -102,6 +110,31 @@ def test_forward_edges(oracle, case, plan):
     torch.cuda.synchronize()
     yr, sr = oracle_fwd(oracle, w, u, k, v, s_in)
     assert_y_close(f64(y), yr, f"{case} {plan} y")
+    assert_state_close(f64(so), sr, f"{case} {plan} state")
+
+
+@pytest.mark.parametrize("plan", ["auto", "lb4x16", "lb8x16", "seg16x16"])
+@pytest.mark.parametrize("case", CASES)
+def test_gated_bf16_forward_edges(oracle, case, plan):
+    """sigmoid(r) * wkv with k, v, r and y in bf16; the oracle reads the
+    rounded inputs, and y may differ by one bf16 rounding more."""
+    w, u, k, v, _, s_in = make(case)
+    r = synth.normal((B, T, C), 2.0, synth.seed_of(synth.TINY, 898, 0))
+    k16, v16, r16 = (x.to(torch.bfloat16) for x in (k, v, r))
+    note(f"edges gated bf16 forward {case} {plan}")
+    dev = torch.device("cuda")
+    p = dict(PLANS, lb8x16=(wkv.WKV_KERNEL_LOOKBACK, 8, 16))[plan]
+    y, so = wkv.wkv_forward_typed(w.to(dev), u.to(dev), k16.to(dev), v16.to(dev), r16.to(dev),
+                                  state_in=None if s_in is None else s_in.to(dev),
+                                  state_out=True, plan=p)
+    torch.cuda.synchronize()
+    yr, sr = oracle_fwd(oracle, w, u, k16.float(), v16.float(), s_in)
+    g = oracle.gate(yr, f64(r16))
+    yg = f64(y)
+    assert np.all(np.isfinite(yg))
+    h = 2.0 ** -8
+    e = float(np.max(np.abs(yg - g) / (1e-5 + (1e-4 + h) * np.abs(g))))
+    assert e <= 1.0, f"{case} {plan} gated bf16 y: {e:.3g}x the tolerance"
     assert_state_close(f64(so), sr, f"{case} {plan} state")
 
 
