@@ -29,6 +29,7 @@ from parity import roundoff_floor
 pytestmark = pytest.mark.gpu
 
 B, T, C = 2, 256, 64
+RAGGED = (3, 129, 70)  # partial last block and tile, C not a multiple of 64
 LOG2E = 1.4426950408889634
 
 PLANS = {
@@ -57,8 +58,9 @@ def note(msg):
     sys.stdout.flush()
 
 
-def make(case):
+def make(case, shape=None):
     """(w, u, k, v, dy, state_in or None) on the host, float32."""
+    B, T, C = shape or (globals()["B"], globals()["T"], globals()["C"])
     seed = synth.seed_of(synth.TINY, 800 + CASES.index(case), 0)
     v = synth.normal((B, T, C), 1.0, seed)
     dy = synth.normal((B, T, C), 1.0, seed + 1)
@@ -79,6 +81,8 @@ def make(case):
         # U - W at -88..-84 and 84..88 (log2), decays slow and fast
         w = torch.tensor([1e-3, 1.0] * (C // 2))
         du = torch.linspace(-2.0, 2.0, C // 2).repeat_interleave(2) / LOG2E
+        if C % 2:
+            w, du = torch.cat([w, w[:1]]), torch.cat([du, du[:1]])
         u = torch.where(torch.arange(C) % 4 < 2, -86.0 / LOG2E + w + du, 86.0 / LOG2E + w + du)
         k[:, 7::50, :] = 30.0
     elif case == "tiny":
@@ -98,11 +102,12 @@ def oracle_fwd(oracle, w, u, k, v, s_in):
     return oracle.forward_scan(f64(w), f64(u), f64(k), f64(v), None if s_in is None else f64(s_in))
 
 
+@pytest.mark.parametrize("shape", [None, RAGGED], ids=["2x256x64", "3x129x70"])
 @pytest.mark.parametrize("plan", list(PLANS))
 @pytest.mark.parametrize("case", CASES)
-def test_forward_edges(oracle, case, plan):
-    w, u, k, v, _, s_in = make(case)
-    note(f"edges forward {case} {plan}")
+def test_forward_edges(oracle, case, plan, shape):
+    w, u, k, v, _, s_in = make(case, shape)
+    note(f"edges forward {case} {plan} {shape}")
     dev = torch.device("cuda")
     y, so = wkv.wkv_forward(w.to(dev), u.to(dev), k.to(dev), v.to(dev),
                             state_in=None if s_in is None else s_in.to(dev), state_out=True,
@@ -159,11 +164,13 @@ def test_step_edges(oracle, case):
     assert_state_close(f64(st[0]), sr, f"{case} step state")
 
 
+@pytest.mark.parametrize("shape", [None, RAGGED], ids=["2x256x64", "3x129x70"])
 @pytest.mark.parametrize("path", ["first_pass", "checkpoints", "gated"])
 @pytest.mark.parametrize("case", CASES)
-def test_backward_edges(oracle, case, path):
-    w, u, k, v, dy, s_in = make(case)
-    note(f"edges backward {case} {path}")
+def test_backward_edges(oracle, case, path, shape):
+    w, u, k, v, dy, s_in = make(case, shape)
+    B, T, C = k.shape
+    note(f"edges backward {case} {path} {shape}")
     dev = torch.device("cuda")
     wd, ud, kd, vd, dyd = (x.to(dev) for x in (w, u, k, v, dy))
     sid = None if s_in is None else s_in.to(dev)
