@@ -136,3 +136,41 @@ def test_give_up_path_poisons_whole_blocks_and_is_reported(oracle):
     assert_y_close(np.array([y2g[b, :, c] for b, c in zip(bs, cs)]), yr)
     wkv.wkv_release_stream_scratch(st)
     st.synchronize()
+
+
+def test_concurrent_streams_keep_their_own_scratch(oracle):
+    """Look-back forwards of two shapes issued alternately on two streams, so
+    that they run concurrently, each stream on its own scratch: every output
+    matches the same call made alone on the default stream."""
+    dev = torch.device("cuda")
+    a_host = synth.make(synth.GPT, index=21, B=8, T=1024, C=2048)
+    b_host = synth.make(synth.STREAM, index=22, B=1, T=1024, C=5120)
+    A = {n: t.to(dev) for n, t in a_host.items()}
+    Bd = {n: t.to(dev) for n, t in b_host.items()}
+    for d in (A, Bd):
+        assert wkv.wkv_forward_plan_auto(*d["k"].shape)[0] == wkv.WKV_KERNEL_LOOKBACK
+    ya_ref, sa_ref = wkv.wkv_forward(A["w"], A["u"], A["k"], A["v"], state_out=True)
+    yb_ref, sb_ref = wkv.wkv_forward(Bd["w"], Bd["u"], Bd["k"], Bd["v"], state_out=True)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(6):
+        with torch.cuda.stream(s1):
+            ya, sa = wkv.wkv_forward(A["w"], A["u"], A["k"], A["v"], state_out=True, stream=s1)
+        with torch.cuda.stream(s2):
+            yb, sb = wkv.wkv_forward(Bd["w"], Bd["u"], Bd["k"], Bd["v"], state_out=True,
+                                     stream=s2)
+        outs.append((ya, sa, yb, sb))
+    torch.cuda.synchronize()
+    note("concurrent look-back forwards on two streams")
+    assert wkv.wkv_lookback_status(s1) == wkv.WKV_OK
+    assert wkv.wkv_lookback_status(s2) == wkv.WKV_OK
+    for ya, sa, yb, sb in outs:
+        # same arithmetic, possibly another composition order: the y tolerance
+        assert_y_close(ya.double().cpu().numpy(), ya_ref.double().cpu().numpy(), "stream 1 y")
+        assert_y_close(yb.double().cpu().numpy(), yb_ref.double().cpu().numpy(), "stream 2 y")
+        assert_state_close(sa.double().cpu().numpy(), sa_ref.double().cpu().numpy())
+        assert_state_close(sb.double().cpu().numpy(), sb_ref.double().cpu().numpy())
+    for st in (s1, s2):
+        wkv.wkv_release_stream_scratch(st)
+        st.synchronize()
