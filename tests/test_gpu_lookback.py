@@ -174,3 +174,50 @@ def test_concurrent_streams_keep_their_own_scratch(oracle):
     for st in (s1, s2):
         wkv.wkv_release_stream_scratch(st)
         st.synchronize()
+
+
+def test_host_threads_on_their_own_streams(oracle):
+    """Four host threads, each issuing look-back forwards on a stream of its
+    own (ctypes drops the GIL during the call, so the library's host side
+    runs concurrently: scratch creation, growth and epochs under its lock)."""
+    import threading
+    dev = torch.device("cuda")
+    shapes = [(2, 512, 256), (1, 1024, 512), (4, 256, 128), (2, 768, 320)]
+    inputs = [{n: t.to(dev) for n, t in synth.make(synth.GPT, index=30 + i, B=b, T=t, C=c).items()}
+              for i, (b, t, c) in enumerate(shapes)]
+    for b, t, c in shapes:
+        assert wkv.wkv_forward_plan_auto(b, t, c)[0] == wkv.WKV_KERNEL_LOOKBACK
+    refs = [wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], state_out=True) for d in inputs]
+    torch.cuda.synchronize()
+    results, errors = [None] * 4, []
+
+    def work(i):
+        try:
+            st = torch.cuda.Stream()
+            d = inputs[i]
+            outs = []
+            with torch.cuda.stream(st):
+                for _ in range(25):
+                    outs.append(wkv.wkv_forward(d["w"], d["u"], d["k"], d["v"], state_out=True,
+                                                stream=st))
+            st.synchronize()
+            status = wkv.wkv_lookback_status(st)
+            wkv.wkv_release_stream_scratch(st)
+            st.synchronize()
+            results[i] = (outs, status)
+        except Exception as e:  # reported below, on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    note(f"host threads: errors {errors}")
+    assert not errors and all(r is not None for r in results)
+    for i, (outs, status) in enumerate(results):
+        assert status == wkv.WKV_OK
+        yr, sr = refs[i]
+        for y, so in outs:
+            assert_y_close(y.double().cpu().numpy(), yr.double().cpu().numpy(), f"thread {i} y")
+            assert_state_close(so.double().cpu().numpy(), sr.double().cpu().numpy())
