@@ -601,8 +601,7 @@ def bench_stability(args, torch, wkv, synth, backward: bool, carried: bool = Fal
                 (40 * B * C if carried else 0) + (12 * B * C * nck if ckpt else 0))
         name = "WKV backward tokens·channels/sec, B=8 T=4096 C=2048 fp32"
         # (the whole-tile variant when T is a multiple of its 128-token tile)
-        # (the gated kernel always runs the general variant)
-        full = T % 128 == 0 and not gated
+        full = T % 128 == 0
         kname = (f"bwd_seg_kernel<16, 8, {'true' if full else 'false'}, "
                  f"{'true' if ckpt else 'false'}, {'true' if gated else 'false'}, "
                  f"{IO_NAMES[io]}>")

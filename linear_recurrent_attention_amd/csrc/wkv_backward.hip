@@ -382,23 +382,26 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         return Rev{sh.seed[0][lane], sh.seed[1][lane], 0.0f, 0.0f, sh.seed[2][lane], 0.0f};
     };
     // Kc holds the keys in log2 units (k log2 e): the scaling takes the place
-    // of the register copy that hands each prefetched tile over
+    // of the register copy that hands each prefetched tile over.  k and v of
+    // the next tile are prefetched; dy is loaded at the top of its own tile,
+    // ahead of that prefetch (loads complete in order), and is first needed
+    // after the forward recompute, which covers its latency.  Prefetching it
+    // as well held 8 more registers across the tile and made the kernel spill.
     float Kc[LS], Vc[LS], Gc[LS];
     {
         const int64_t t0 = (ntiles - 1) * TT + (int64_t)s * LS;
         load_seg<LS>(Kc, rows(kseq, t0), t0, T);
         load_seg<LS>(Vc, rows(vseq, t0), t0, T);
-        load_seg<LS>(Gc, rows(gseq, t0), t0, T);
 #pragma unroll
         for (int j = 0; j < LS; ++j) Kc[j] *= kLog2e;
     }
     for (int64_t tile = ntiles - 1; tile >= 0; --tile) {
         const int64_t t0 = tile * TT + (int64_t)s * LS;
-        float Kn[LS], Vn[LS], Gn[LS];
+        load_seg<LS>(Gc, rows(gseq, t0), t0, T);
+        float Kn[LS], Vn[LS];
         if (tile > 0) {
             load_seg<LS>(Kn, rows(kseq, t0 - TT), t0 - TT, T);
             load_seg<LS>(Vn, rows(vseq, t0 - TT), t0 - TT, T);
-            load_seg<LS>(Gn, rows(gseq, t0 - TT), t0 - TT, T);
         }
         // the receptance of this tile (used once the forward is recomputed)
         float Rc[GATE ? LS : 1];
@@ -538,7 +541,6 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         for (int j = 0; j < LS; ++j) {
             Kc[j] = Kn[j] * kLog2e;
             Vc[j] = Vn[j];
-            Gc[j] = Gn[j];
         }
     }
 
@@ -681,19 +683,16 @@ void launch_bwd_seg_k(const BwdArgs &a, int64_t grid, float *ck, double *part, h
                        (T *)a.dr);
 }
 
-// The whole-tile variant where T allows it, except with the gate: its extra
-// row array makes the whole-tile code spill some 40 registers, against none
-// for the general code.
+// The whole-tile variant where T allows it (with the gate as well: its extra
+// row array costs some 20 spilled registers there, and it is still faster than
+// the general code).
 template <bool CK, bool GATE, class IO>
 void launch_bwd_seg_full(const BwdArgs &a, int64_t grid, float *ck, double *part,
                          hipStream_t st) {
-    if constexpr (!GATE) {
-        if (a.T % (kBwdNW * kBwdLS) == 0) {
-            launch_bwd_seg_k<true, CK, GATE, IO>(a, grid, ck, part, st);
-            return;
-        }
-    }
-    launch_bwd_seg_k<false, CK, GATE, IO>(a, grid, ck, part, st);
+    if (a.T % (kBwdNW * kBwdLS) == 0)
+        launch_bwd_seg_k<true, CK, GATE, IO>(a, grid, ck, part, st);
+    else
+        launch_bwd_seg_k<false, CK, GATE, IO>(a, grid, ck, part, st);
 }
 
 template <bool GATE, class IO>
