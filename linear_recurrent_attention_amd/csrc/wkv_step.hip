@@ -7,8 +7,12 @@
 // so the kernel is a pure stream: 36 bytes per lane (k, v, y, 3 state planes in
 // and out) in float32; k, v, r and y may also be 16-bit (fp16 or bf16), the
 // state staying float32.  A thread handles four consecutive channels with 16-byte
-// non-temporal loads and stores; a workgroup covers 1024 channels of one
-// (layer, sequence) row, so every access of a wave is 1 KiB contiguous.
+// non-temporal loads and stores, in IT chunks 1024 channels apart; a workgroup
+// covers IT * 1024 channels of one (layer, sequence) row, so every access of a
+// wave is 1 KiB contiguous.  Each thread issues the loads of all its chunks
+// before it computes or stores anything: with nine streams per lane (five
+// read, four written), more loads in flight per thread is what lifts the
+// kernel toward the bandwidth a plain copy reaches.
 // With a receptance tensor r ([L][B][C], read beside k and v) the output is
 // the time-mixing block's gated sigmoid(r) * wkv (block figure of "RWKV
 // architecture overview"): 4 more bytes per lane.
@@ -18,6 +22,16 @@
 namespace wkv {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Chunks of 1024 channels per thread (4-wide path), plain and gated.
+#ifndef WKV_STEP_IT
+#define WKV_STEP_IT 4
+#endif
+#ifndef WKV_STEP_IT_GATED
+#define WKV_STEP_IT_GATED 2
+#endif
+constexpr int kStepChunks = WKV_STEP_IT;
+constexpr int kStepChunksGated = WKV_STEP_IT_GATED;
 
 // (a, b, o) is the ABI state of one lane (o in natural-log units).
 //
@@ -102,8 +116,9 @@ __device__ __forceinline__ void st4(typename IO::T *p, const f4 &x) {
 }
 
 // VEC = 4: C % 4 == 0 and every pointer aligned to its 4-element access;
-// VEC = 1 otherwise.  IO: element format of k, v, r, y (state, w, u: float32).
-template <int VEC, bool GATE, class IO>
+// VEC = 1 otherwise (then IT = 1).  IT: chunks of 1024 channels per thread.
+// IO: element format of k, v, r, y (state, w, u: float32).
+template <int VEC, int IT, bool GATE, class IO>
 __global__ __launch_bounds__(256) void step_kernel(int64_t L, int64_t B, int64_t C,
                                                    uint32_t blocks_per_row,
                                                    const float *__restrict__ w,
@@ -122,38 +137,53 @@ __global__ __launch_bounds__(256) void step_kernel(int64_t L, int64_t B, int64_t
     const int64_t row = row32;
     const int64_t l = l32;
     const int64_t bb = (int64_t)(row32 - l32 * (uint32_t)B);
-    const int64_t c = ((int64_t)cb * 256 + threadIdx.x) * VEC;
-    if (c >= C) return;
-    const int64_t kv = row * C + c;
-    const int64_t sa = ((l * 3 + 0) * B + bb) * C + c;
+    const int64_t c0 = ((int64_t)cb * 256 * IT + threadIdx.x) * VEC;
+    if (c0 >= C) return;
+    // chunk i of this thread: channels c0 + i * 1024 .. + 3
+    const int64_t kv = row * C + c0;
+    const int64_t sa = ((l * 3 + 0) * B + bb) * C + c0;
     const int64_t sb = sa + B * C;
     const int64_t so = sb + B * C;
-    const int64_t wc = l * C + c;
+    const int64_t wc = l * C + c0;
     if constexpr (VEC == 4) {
-        const f4 kk = ld4<IO>(k + kv);
-        const f4 vv = ld4<IO>(v + kv);
-        f4 aa = __builtin_nontemporal_load((const f4 *)(s_in + sa));
-        f4 bq = __builtin_nontemporal_load((const f4 *)(s_in + sb));
-        f4 oo = __builtin_nontemporal_load((const f4 *)(s_in + so));
-        const f4 ww = *(const f4 *)(w + wc);
-        const f4 uu = *(const f4 *)(u + wc);
-        f4 rr = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (GATE) rr = ld4<IO>(r + kv);
-        f4 yy;
+        constexpr int64_t kStride = 256 * 4;
+        f4 kk[IT], vv[IT], aa[IT], bq[IT], oo[IT], ww[IT], uu[IT], rr[IT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float a = aa[j], b = bq[j], o = oo[j];
-            yy[j] = step_one(a, b, o, kk[j], vv[j], ww[j], uu[j]);
-            if constexpr (GATE) yy[j] *= gate_of(rr[j]);
-            aa[j] = a;
-            bq[j] = b;
-            oo[j] = o;
+        for (int i = 0; i < IT; ++i) {
+            const int64_t d = i * kStride;
+            if (i == 0 || c0 + d < C) {
+                kk[i] = ld4<IO>(k + kv + d);
+                vv[i] = ld4<IO>(v + kv + d);
+                aa[i] = __builtin_nontemporal_load((const f4 *)(s_in + sa + d));
+                bq[i] = __builtin_nontemporal_load((const f4 *)(s_in + sb + d));
+                oo[i] = __builtin_nontemporal_load((const f4 *)(s_in + so + d));
+                ww[i] = *(const f4 *)(w + wc + d);
+                uu[i] = *(const f4 *)(u + wc + d);
+                if constexpr (GATE) rr[i] = ld4<IO>(r + kv + d);
+            }
         }
-        st4<IO>(y + kv, yy);
-        __builtin_nontemporal_store(aa, (f4 *)(s_out + sa));
-        __builtin_nontemporal_store(bq, (f4 *)(s_out + sb));
-        __builtin_nontemporal_store(oo, (f4 *)(s_out + so));
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int64_t d = i * kStride;
+            if (i == 0 || c0 + d < C) {
+                f4 yy;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float a = aa[i][j], b = bq[i][j], o = oo[i][j];
+                    yy[j] = step_one(a, b, o, kk[i][j], vv[i][j], ww[i][j], uu[i][j]);
+                    if constexpr (GATE) yy[j] *= gate_of(rr[i][j]);
+                    aa[i][j] = a;
+                    bq[i][j] = b;
+                    oo[i][j] = o;
+                }
+                st4<IO>(y + kv + d, yy);
+                __builtin_nontemporal_store(aa[i], (f4 *)(s_out + sa + d));
+                __builtin_nontemporal_store(bq[i], (f4 *)(s_out + sb + d));
+                __builtin_nontemporal_store(oo[i], (f4 *)(s_out + so + d));
+            }
+        }
     } else {
+        const int64_t c = c0;
         float a = s_in[sa], b = s_in[sb], o = s_in[so];
         float yy = step_one(a, b, o, IO::to_f(k[kv]), IO::to_f(v[kv]), w[wc], u[wc]);
         if constexpr (GATE) yy *= gate_of(IO::to_f(r[kv]));
@@ -164,10 +194,10 @@ __global__ __launch_bounds__(256) void step_kernel(int64_t L, int64_t B, int64_t
     }
 }
 
-template <int VEC, bool GATE, class IO>
+template <int VEC, int IT, bool GATE, class IO>
 static void launch_step_k(const StepArgs &a, int64_t grid, int64_t bpr, hipStream_t st) {
     using T = typename IO::T;
-    hipLaunchKernelGGL((step_kernel<VEC, GATE, IO>), dim3((unsigned)grid), dim3(256), 0, st, a.L,
+    hipLaunchKernelGGL((step_kernel<VEC, IT, GATE, IO>), dim3((unsigned)grid), dim3(256), 0, st, a.L,
                        a.B, a.C, (uint32_t)bpr, a.w, a.u, (const T *)a.k, (const T *)a.v,
                        (const T *)a.r, (T *)a.y, a.s_in, a.s_out);
 }
@@ -180,18 +210,19 @@ static hipError_t launch_step_io(const StepArgs &a, hipStream_t st) {
                             (uintptr_t)a.s_out;
     const uintptr_t misio = (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.y | (uintptr_t)a.r;
     const bool vec4 = (a.C % 4 == 0) && (mis32 % 16 == 0) && (misio % (4 * IO::kBytes) == 0);
-    const int64_t per_block = 256 * (int64_t)(vec4 ? 4 : 1);
+    const int64_t it = vec4 ? (a.r ? kStepChunksGated : kStepChunks) : 1;
+    const int64_t per_block = 256 * (int64_t)(vec4 ? 4 : 1) * it;
     const int64_t bpr = (a.C + per_block - 1) / per_block;
     const int64_t grid = a.L * a.B * bpr;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (vec4 && a.r)
-        launch_step_k<4, true, IO>(a, grid, bpr, st);
+        launch_step_k<4, kStepChunksGated, true, IO>(a, grid, bpr, st);
     else if (vec4)
-        launch_step_k<4, false, IO>(a, grid, bpr, st);
+        launch_step_k<4, kStepChunks, false, IO>(a, grid, bpr, st);
     else if (a.r)
-        launch_step_k<1, true, IO>(a, grid, bpr, st);
+        launch_step_k<1, 1, true, IO>(a, grid, bpr, st);
     else
-        launch_step_k<1, false, IO>(a, grid, bpr, st);
+        launch_step_k<1, 1, false, IO>(a, grid, bpr, st);
     return hipGetLastError();
 }
 

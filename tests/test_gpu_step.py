@@ -39,7 +39,10 @@ def oracle_states(oracle, L, B, C, seed):
     return torch.from_numpy(np.stack(out).astype(np.float32))
 
 
-@pytest.mark.parametrize("shape", [(3, 4, 40), (2, 3, 37), (1, 1, 1), (4, 2, 1030)],
+# C = 37 and 1030 take the one-channel path; 1032, 2056 and 5128 leave the
+# last 1024-channel chunk of the four-wide path partly filled.
+@pytest.mark.parametrize("shape", [(3, 4, 40), (2, 3, 37), (1, 1, 1), (4, 2, 1030),
+                                   (2, 3, 1032), (1, 2, 5128), (2, 2, 2056)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_steps_match_oracle(oracle, shape):
     L, B, C = shape

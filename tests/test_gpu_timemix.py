@@ -149,7 +149,8 @@ def test_gated_forward_captured_in_a_graph(oracle):
         assert_y_close(f64(y), yr, f"gated y, replay {i}")
 
 
-@pytest.mark.parametrize("shape", [(3, 4, 40), (2, 3, 37), (1, 1, 1), (4, 2, 1030)],
+@pytest.mark.parametrize("shape", [(3, 4, 40), (2, 3, 37), (1, 1, 1), (4, 2, 1030),
+                                   (2, 3, 1032), (1, 2, 5128), (2, 2, 2056)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_gated_steps_match_oracle(oracle, shape):
     """Several gated steps from a reachable state, in place: y and the state
