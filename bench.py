@@ -474,7 +474,8 @@ def bench_decode(args, torch, wkv, synth, gated: bool = False):
     per = ms / nsteps
     lanes = L * B * C
     algo = (40 if gated else 36) * lanes + 8 * L * C
-    kname = f"step_kernel<4, {'true' if gated else 'false'}, wkv::IoF32>"
+    # (four channels per thread, in four 1024-channel chunks; two when gated)
+    kname = f"step_kernel<4, {2 if gated else 4}, {'true' if gated else 'false'}, wkv::IoF32>"
     wl = "decode_gated" if gated else "decode"
     cpu = None
     if not args.no_cpu_baseline:
