@@ -180,7 +180,9 @@ def test_typed_chunked_state_carry(oracle):
 
 @pytest.mark.parametrize("dt", list(DTYPES))
 @pytest.mark.parametrize("gated", [False, True])
-@pytest.mark.parametrize("shape", [(3, 4, 40), (2, 3, 37), (4, 2, 1030)],
+# (1032 and 5128: the last 1024-channel chunk of a thread partly filled)
+@pytest.mark.parametrize("shape", [(3, 4, 40), (2, 3, 37), (4, 2, 1030), (2, 3, 1032),
+                                   (1, 2, 5128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_typed_steps_match_oracle(oracle, dt, gated, shape):
     L, B, C = shape
