@@ -23,15 +23,12 @@ namespace wkv {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-// Chunks of 1024 channels per thread (4-wide path), plain and gated.
-#ifndef WKV_STEP_IT
-#define WKV_STEP_IT 4
-#endif
-#ifndef WKV_STEP_IT_GATED
-#define WKV_STEP_IT_GATED 2
-#endif
-constexpr int kStepChunks = WKV_STEP_IT;
-constexpr int kStepChunksGated = WKV_STEP_IT_GATED;
+// Chunks of 1024 channels per thread (4-wide path), plain and gated.  On
+// MI355X at L=24 B=1024 C=4096: 1, 2 and 4 chunks take 686, 634 and 626 us
+// per plain step; 1 and 2 chunks 763 and 692 us per gated step (four would
+// hold some 170 registers there).
+constexpr int kStepChunks = 4;
+constexpr int kStepChunksGated = 2;
 
 // (a, b, o) is the ABI state of one lane (o in natural-log units).
 //
