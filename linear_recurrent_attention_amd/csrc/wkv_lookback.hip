@@ -28,9 +28,10 @@
 // are single-copy atomic and coherent across the dies, so a reader that sees
 // the expected tag on a word also sees its value; no ordering between words is
 // needed because each word validates itself.  A block's aggregate and its
-// inclusive state go to separate slots, fetched together: a reader that
-// catches the inclusive slot half-way through being written still has the
-// whole aggregate to fold.
+// inclusive state go to separate slots.  A reader fetches the inclusive slot
+// and, only when that is not wholly published (not yet, or caught half-way
+// through being written), the aggregate, which its block wrote before it
+// began its look-back; a reader that finds neither whole tries again.
 //
 // Ordering and progress.  Workgroups are numbered block-major (channel set
 // fastest, then sequence, then block) and the hardware dispatches them in that
@@ -204,15 +205,19 @@ __device__ __forceinline__ void lb_body(int64_t B, int64_t T, int64_t C, const C
                 uint32_t st = 0;
                 Lane X = lane_empty();
                 if (pj >= 0) {
+                    // the inclusive state first; the aggregate only when that
+                    // is not (yet wholly) published
                     Lane Xi, Xa;
                     const bool oi = fetch(incls + slot_of(pj), lane, tag_incl, Xi);
-                    const bool oa = fetch(aggs + slot_of(pj), lane, tag_agg, Xa);
                     if (__all(oi)) {
                         st = kIncl;
                         X = Xi;
-                    } else if (__all(oa)) {
-                        st = kAgg;
-                        X = Xa;
+                    } else {
+                        const bool oa = fetch(aggs + slot_of(pj), lane, tag_agg, Xa);
+                        if (__all(oa)) {
+                            st = kAgg;
+                            X = Xa;
+                        }
                     }
                 }
                 lds_put(sh.pv, s, g, lane, X);
