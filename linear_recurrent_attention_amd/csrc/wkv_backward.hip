@@ -294,6 +294,10 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         load_seg<LS>(Vc, rows(vseq, (int64_t)s * LS), (int64_t)s * LS, T);
 #pragma unroll
         for (int j = 0; j < LS; ++j) Kc[j] *= kLog2e;
+        // the scan's LDS buffers alternate from tile to tile, so that a wave's
+        // first write of a tile never meets another wave's last read of the
+        // previous tile (no barrier lies between them)
+        int buf = 0;
         for (int64_t tile = 0; tile < ntiles; ++tile) {
             const int64_t t0 = tile * TT + (int64_t)s * LS;
             float Kn[LS], Vn[LS];
@@ -309,7 +313,6 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 for (int j = 0; j < LS; ++j)
                     if (t0 + j < T) absorb(S, Kc[j], Vc[j], ch);
             }
-            int buf = 0;
 #pragma unroll
             for (int d = 1; d < NW; d <<= 1) {
                 fwd_put(sh, buf, s, lane, S);
@@ -326,6 +329,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
             Lane R = carry;
             if (s > 0) compose(R, fwd_get(sh, buf, s - 1, lane), ch.W, (float)(s * LS));
             compose(carry, fwd_get(sh, buf, NW - 1, lane), ch.W, (float)TT);
+            buf ^= 1;
             float *q = ck + ((tile * NW + s) * 4) * 64 + lane;
             q[0] = R.a;
             q[64] = R.b;
@@ -395,6 +399,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
 #pragma unroll
         for (int j = 0; j < LS; ++j) Kc[j] *= kLog2e;
     }
+    int rb = 0;  // LDS buffer the next reverse scan starts in (alternating as in phase 1)
     for (int64_t tile = ntiles - 1; tile >= 0; --tile) {
         const int64_t t0 = tile * TT + (int64_t)s * LS;
         load_seg<LS>(Gc, rows(gseq, t0), t0, T);
@@ -484,7 +489,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
                 if (FULL || t0 + j < T) rev_absorb(z, Gc[j], Y[j], LAM[j], ch.W);
         }
         // inclusive scan from the last segment backward (Hillis-Steele)
-        int buf = 0;
+        int buf = rb;
 #pragma unroll
         for (int d = 1; d < NW; d <<= 1) {
             rev_put(sh, buf, s, lane, z);
@@ -497,6 +502,7 @@ __device__ __forceinline__ void bwd_body(int64_t B, int64_t T, int64_t C, int64_
         Rev suf = rev_empty();
         if (s + 1 < NW) suf = rev_get(sh, buf, s + 1, lane);
         const Rev agg = rev_get(sh, buf, 0, lane);
+        rb = buf ^ 1;
         rev_compose(suf, carry, ch.W, (float)((NW - 1 - s) * LS));
         if (seeded) suf = seed_of();  // (later segments and the carry are empty here)
         {

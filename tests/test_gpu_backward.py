@@ -67,31 +67,68 @@ def test_ragged_backward_matches_oracle(oracle, shape, recipe):
     check(g, r, d, oracle)
 
 
+WHOLE_TILES = [(2, 512, 96), (1, 1024, 130), (3, 256, 64)]
+
+
+@pytest.mark.parametrize("shape", WHOLE_TILES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("recipe", [synth.GPT, synth.STABILITY])
+def test_whole_tile_backward_matches_oracle(oracle, shape, recipe):
+    """Sequences of whole 128-token tiles, where each tile's segments are
+    recomputed and swept in one frame: the plain backward, the backward from
+    the GPU forward's checkpoints and the gated backward."""
+    B, T, C = shape
+    d = synth.make(recipe, index=12, B=B, T=T, C=C, with_dy=True)
+    note(f"backward whole tiles B={B} T={T} C={C} recipe={recipe}")
+    a = [f64(d[n]) for n in ("w", "u", "k", "v")]
+    ref = oracle.backward_scan(*a, f64(d["dy"]), nthreads=NTHREADS)
+    check(gpu_grads(d), ref, d, oracle, "plain")
+    dev = torch.device("cuda")
+    w, u, k, v, dy = (d[n].to(dev) for n in ("w", "u", "k", "v", "dy"))
+    _, _, ck = wkv.wkv_forward_checkpointed(w, u, k, v)
+    g = [f64(t) for t in wkv.wkv_backward_checkpointed(w, u, k, v, dy, ck)[:4]]
+    torch.cuda.synchronize()
+    check(g, ref, d, oracle, "from checkpoints")
+    r = synth.receptance(recipe, 12, (B, T, C))
+    dk, dv, dr, dw, du, _ = wkv.wkv_backward_gated(w, u, k, v, r.to(dev), dy, checkpoints=ck)
+    torch.cuda.synchronize()
+    y, _ = oracle.forward_scan(*a)
+    gg, dr_ref = oracle.gate_backward(y, f64(r), f64(d["dy"]))
+    gref = oracle.backward_scan(*a, gg, nthreads=NTHREADS)
+    v64 = f64(d["v"])
+    for name, x, rr in (("dk", dk, gref[0]), ("dv", dv, gref[1]), ("dr", dr, dr_ref)):
+        assert_grad_close(f64(x), rr, f"gated {name}", roundoff_floor(gg, v64))
+    assert_sums_close(oracle, f64(dw), f64(du), gref[2], gref[3], *a, gg, what="gated")
+
+
+@pytest.mark.parametrize("T", [300, 640])
 @pytest.mark.parametrize("hi,lo", [(75.0, -70.0), (88.0, -85.0)], ids=["75", "88"])
-def test_extreme_bonus_backward(oracle, hi, lo):
+def test_extreme_bonus_backward(oracle, hi, lo, T):
     """Channels where the bonus dominates every output (each earlier token's
     weight near e^{-u}, down to float's smallest normal numbers at u = 88) or
     vanishes (own weight near e^{u}): dw and du of those channels are tiny and
     are held, per channel, to the round-off of their own terms."""
-    d = synth.make(synth.TINY, index=3, B=2, T=300, C=64, with_dy=True)
+    d = synth.make(synth.TINY, index=3, B=2, T=T, C=64, with_dy=True)
     d["u"][::3] = hi
     d["u"][1::5] = lo
-    note(f"backward extreme bonus {hi} {lo}")
+    note(f"backward extreme bonus {hi} {lo} T={T}")
     g = gpu_grads(d)
     r = oracle.backward_scan(*(f64(d[n]) for n in ("w", "u", "k", "v", "dy")))
     check(g, r, d, oracle)
 
 
+@pytest.mark.parametrize("T", [600, 640])
 @pytest.mark.parametrize("recipe", [synth.GPT, synth.STABILITY])
-def test_extreme_decay_backward(oracle, recipe):
+def test_extreme_decay_backward(oracle, recipe, T):
     """Per-channel decay rates spread geometrically from 1e-6 (nothing decays
     over the sequence) to 60 (the past vanishes within two tokens): the plain
     backward, the backward from the GPU forward's checkpoints and the gated
-    backward, against the oracle."""
-    B, T, C = 2, 600, 96
+    backward, against the oracle (T = 640: whole tiles, where the groups of
+    moderate rates run in one frame per segment and the others token by
+    token)."""
+    B, C = 2, 96
     d = synth.make(recipe, index=8, B=B, T=T, C=C, with_dy=True)
     d["w"] = torch.from_numpy(np.geomspace(1e-6, 60.0, C).astype(np.float32))
-    note(f"backward extreme decay recipe={recipe}")
+    note(f"backward extreme decay recipe={recipe} T={T}")
     check(gpu_grads(d), oracle.backward_scan(*(f64(d[n]) for n in ("w", "u", "k", "v", "dy"))), d,
           oracle, "plain")
     dev = torch.device("cuda")

@@ -66,7 +66,8 @@ def check(oracle, d, s_in, s_out, g_out, got, what):
             assert_grad_close(f64(got[4])[p], ref[4][p], f"{what} {name}", fs)
 
 
-SHAPES = [(1, 1, 5), (2, 300, 100), (3, 17, 64), (1, 513, 130), (2, 129, 64), (1, 640, 33)]
+SHAPES = [(1, 1, 5), (2, 300, 100), (3, 17, 64), (1, 513, 130), (2, 129, 64), (1, 640, 33),
+          (2, 512, 96)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -204,7 +205,8 @@ HALF_ULP = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
 
 
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
-@pytest.mark.parametrize("shape", [(1, 1, 5), (2, 300, 100), (1, 513, 130), (2, 129, 64)],
+@pytest.mark.parametrize("shape", [(1, 1, 5), (2, 300, 100), (1, 513, 130), (2, 129, 64),
+                                   (2, 512, 96)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("states", [False, True])
 def test_typed_backward_matches_oracle(oracle, dt, shape, states):
