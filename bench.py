@@ -46,21 +46,30 @@ METRIC_GATED = ("WKV fwd with the sigmoid(r) output gate, tokens·channels/sec, 
                 "B=8 T=1024 C=2048 fp32")
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["linear_recurrent_attention_amd/csrc/wkv_forward.hip",
-                  "linear_recurrent_attention_amd/csrc/wkv_lookback.hip",
-                  "linear_recurrent_attention_amd/csrc/wkv_step.hip",
-                  "linear_recurrent_attention_amd/csrc/wkv_backward.hip",
-                  "linear_recurrent_attention_amd/csrc/wkv_shift.hip",
-                  "linear_recurrent_attention_amd/csrc/wkv_device.hpp"]
+# The sources each kernel is compiled from (its own file and the shared
+# headers): a counter run stays valid while these are unchanged.
+_CSRC = "linear_recurrent_attention_amd/csrc/"
+_SHARED = [_CSRC + "wkv_device.hpp", _CSRC + "wkv_internal.hpp"]
+KERNEL_SOURCES = {
+    "fwd_lookback_kernel": [_CSRC + "wkv_lookback.hip"] + _SHARED,
+    "fwd_seg_kernel": [_CSRC + "wkv_forward.hip"] + _SHARED,
+    "fwd_lane_kernel": [_CSRC + "wkv_forward.hip"] + _SHARED,
+    "step_kernel": [_CSRC + "wkv_step.hip"] + _SHARED,
+    "bwd_seg_kernel": [_CSRC + "wkv_backward.hip"] + _SHARED,
+    "shift_kernel": [_CSRC + "wkv_shift.hip"] + _SHARED,
+    "shift_bwd_kernel": [_CSRC + "wkv_shift.hip"] + _SHARED,
+}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def source_hash(kernel: str) -> str:
+    """Hash of the sources the named kernel (its template name; arguments
+    ignored) is built from."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel.split("<")[0]]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -75,7 +84,7 @@ def measured_traffic(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     e = rec.get(workload)
-    if not e or e.get("source_hash") != source_hash() or e.get("kernel") != kernel:
+    if not e or e.get("kernel") != kernel or e.get("source_hash") != source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
