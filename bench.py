@@ -13,6 +13,9 @@ wkv_forward).  Prints one JSON line with the lane-token throughput
 (tokens x channels / s), the roofline of the forward kernel (algorithmic HBM
 bytes per launch over its average launch time, measured with HIP events on the
 stream it runs on), and the float64 CPU oracle timed on this host as a baseline.
+The same line carries, under "other_configs", the stream, decode and stability
+forward and backward figures, each timed as its own --workload run times it
+(fewer steps; --headline-only leaves them out).
 
 Other workloads print their own line in the same format; they are parity
 workloads with extra measurements, not the headline:
@@ -843,6 +846,32 @@ def bench_copy(args, torch, wkv, synth):
                                             "bytes_written": 4 * n}}
 
 
+def other_configs(args, torch, wkv, synth):
+    """The other workloads' figures beside the headline, each timed the way
+    its own --workload run times it (fewer steps, no CPU baseline): the stream
+    chunks, the batched decode step, and the stability forward and backward."""
+    import copy
+    res = {}
+    for name, fn, steps in (("stream", bench_stream, 2), ("decode", bench_decode, 4),
+                            ("stability_fwd", lambda a, t, w, s: bench_stability(a, t, w, s, False), 5),
+                            ("stability_bwd", lambda a, t, w, s: bench_stability(a, t, w, s, True), 5)):
+        a = copy.copy(args)
+        a.steps, a.warmup, a.no_cpu_baseline = steps, 1, True
+        torch.cuda.empty_cache()
+        log(f"other configs: {name}")
+        r = fn(a, torch, wkv, synth)
+        rf = r["roofline"]
+        res[name] = {"metric": r["metric"], "value": r["value"], "unit": r["unit"],
+                     "kernel": r["config"].get("kernel"),
+                     "avg_launch_us": rf["avg_launch_us"], "hbm_gbs": rf["achieved"],
+                     "frac": rf["frac"],
+                     "traffic_x_algorithmic": (rf["traffic"] / rf["algorithmic_bytes_per_launch"]
+                                               if rf.get("traffic") else None),
+                     "timed_steps": r["steps"]}
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -859,6 +888,8 @@ def main():
                     metavar="N", help="force a forward kernel: KERNEL SEGMENTS SEG_LEN [CHANNELS] "
                     "(wkv_forward_ex plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="gpt workload: skip the other workloads' summary (other_configs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -894,6 +925,8 @@ def main():
           }[args.workload]
     torch.cuda.synchronize()
     out = fn(args, torch, wkv, synth)
+    if args.workload == "gpt" and not args.headline_only:
+        out["other_configs"] = other_configs(args, torch, wkv, synth)
     print(json.dumps(out), flush=True)
 
 
