@@ -355,7 +355,8 @@ wkv_status forward_impl(int64_t B, int64_t T, int64_t C, const float *w, const f
         p = auto_plan(B, T, C, device_cus());
         if (gated) p = gated_plan(p);
     }
-    const FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr, io, ck};
+    FwdArgs a{B, T, C, w, u, k, v, y, state_in, state_out, gated ? r : nullptr, io, ck};
+    a.cus = device_cus();
     if (p.kernel == WKV_KERNEL_LANE) {
         if ((lanes + 255) / 256 > 0x7fffffffLL) return WKV_ERR_UNSUPPORTED;
         return from_hip(wkv::launch_forward_lane(a, stream));

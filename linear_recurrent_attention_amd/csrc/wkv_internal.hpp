@@ -29,6 +29,7 @@ struct FwdArgs {
     const void *r;
     int io;
     float *ck = nullptr;
+    int cus = 256;  // compute units of the device (sizes launch choices)
 };
 
 struct StepArgs {
