@@ -350,7 +350,7 @@ __attribute__((amdgpu_waves_per_eu(lb_waves_per_simd(LS, GATE)))) void fwd_lookb
     q.s = wave / CG;
     const uint32_t per_block = nsets * (uint32_t)B;
     // Within each window of xwin consecutive workgroups (xwin a multiple of 8
-    // dividing per_block), the 8 dies each take xwin/8 adjacent items (the
+    // dividing per_block; 0: the plain order), the 8 dies each take xwin/8 adjacent items (the
     // hardware hands consecutive workgroups to the dies in turn).  A window
     // never straddles two blocks, so every item still waits only on
     // workgroups dispatched before its own, and its predecessors run on its
@@ -463,9 +463,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr int lb_key(int cg, int ns, int ls) { return (cg * 64 + ns) * 1024 + ls; }
 
 constexpr uint32_t kXcdWindow = 128;
-#ifndef WKV_LB_XWIN_GATE
-#define WKV_LB_XWIN_GATE 0
-#endif
+constexpr uint32_t kXcdWindowNarrow = 40;
 
 template <int CG, int NS, int LS, bool GATE, class IO>
 hipError_t launch_lb(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st) {
@@ -477,16 +475,24 @@ hipError_t launch_lb(const FwdArgs &a, const LookbackScratch &sc, hipStream_t st
     uint32_t *giveups = (uint32_t *)sc.base;
     Word *aggs = (Word *)((char *)sc.base + kLookbackHeaderBytes);
     Word *incls = (Word *)((char *)aggs + align_up((size_t)nslots * kSlotWords * sizeof(Word)));
-    // Die-contiguous items (xwin above) where the grid runs in more than one
-    // generation of resident workgroups (16-bit activations) or more than two
-    // (float32): measured 5-9% and 2-4% faster there, and 1-2% slower with
-    // fewer generations.
+    // Die-contiguous items (xwin above), chosen from timings on MI355X: windows
+    // of 128 where the grid runs in more than one generation of resident
+    // workgroups (16-bit activations) or more than two (float32), measured
+    // 5-9% and 2-4% faster there and 1-2% slower with fewer generations;
+    // windows of 40 where 128 does not divide the workgroups per block but 40
+    // does (the B=1 C=5120 stream chunk: 3% faster); never for the gated
+    // forward (1.6% slower).
     const int64_t per_block = nsets * a.B;
     const int64_t resident = (int64_t)a.cus * (4 * lb_waves_per_simd(LS, GATE) / (CG * NS));
     const int64_t nwg = per_block * nblocks;
     const bool many = IO::kBytes == 4 ? nwg > 2 * resident : nwg > resident;
-    const uint32_t xwin =
-        (WKV_LB_XWIN_GATE || !GATE) && many && per_block % kXcdWindow == 0 ? kXcdWindow : 0u;
+    uint32_t xwin = 0;
+    if (!GATE) {
+        if (per_block % kXcdWindow == 0)
+            xwin = many ? kXcdWindow : 0u;
+        else if (per_block % kXcdWindowNarrow == 0)
+            xwin = kXcdWindowNarrow;
+    }
     hipLaunchKernelGGL((fwd_lookback_kernel<CG, NS, LS, GATE, IO>),
                        dim3((unsigned)(nsets * a.B * nblocks)), dim3(CG * NS * 64), 0, st, a.B,
                        a.T, a.C, a.w, a.u, (const T *)a.k, (const T *)a.v, (const T *)a.r,

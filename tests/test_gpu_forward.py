@@ -265,3 +265,21 @@ def test_every_kernel_on_the_gpt_workload_sampled(oracle, plan):
                                  f64(lanes(d["v"])))
     assert_y_close(f64(lanes(y)), yr)
     assert_state_close(f64(so[:, bs, cs].unsqueeze(1)), sr)
+
+
+# Grids whose workgroups the look-back forward hands to the dies in windows:
+# 128 workgroups per block over more than two generations (B=4, C=2048,
+# 18 blocks of 128 tokens, the last one ragged), 80 per block (B=1, C=5120)
+# and 40 per block (B=1, C=2560), each from a carried state.
+@pytest.mark.parametrize("shape", [(4, 2200, 2048), (1, 1000, 5120), (1, 777, 2560)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_die_windows_match_oracle(oracle, shape):
+    B, T, C = shape
+    d = synth.make(synth.GPT, index=63, B=B, T=T, C=C)
+    si = reachable_state(oracle, B, C, 4)
+    note(f"die windows B={B} T={T} C={C}")
+    y, so = run(d, None, si)
+    yr, sr = oracle.forward_scan(*(f64(d[n]) for n in ("w", "u", "k", "v")), si.double().numpy(),
+                                 nthreads=NTHREADS)
+    assert_y_close(f64(y), yr)
+    assert_state_close(f64(so), sr)

@@ -208,3 +208,21 @@ def test_typed_steps_match_oracle(oracle, dt, gated, shape):
                 yl = oracle.gate(yl, f64(r[l]))
             assert_y16_close(y[l], yl, dtype, f"step {step} y")
             assert_state_close(f64(st_d[l]), ref[l], f"step {step} state")
+
+
+# Grids whose workgroups the look-back forward hands to the dies in windows
+# (of 128 or of 40 workgroups): several generations of 128 workgroups per
+# block in 16-bit, a block of 80 (B=1, C=5120), and 40 workgroups per block.
+@pytest.mark.parametrize("dt", list(DTYPES))
+@pytest.mark.parametrize("shape", [(2, 1100, 4096), (1, 700, 5120), (1, 333, 2560)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_typed_die_windows_match_oracle(oracle, dt, shape):
+    B, T, C = shape
+    dtype = DTYPES[dt]
+    d = cast(synth.make(synth.GPT, index=62, B=B, T=T, C=C), dtype)
+    si = reachable_state(oracle, B, C, 3)
+    note(f"typed die windows {dt} B={B} T={T} C={C}")
+    y, so = run(d, None, None, si)
+    yr, sr = reference(oracle, d, None, si)
+    assert_y16_close(y, yr, dtype)
+    assert_state_close(f64(so), sr)
