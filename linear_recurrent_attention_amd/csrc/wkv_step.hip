@@ -76,6 +76,8 @@ __device__ __forceinline__ float step_one(float &a, float &b, float &o, float k,
     return y;
 }
 
+constexpr uint32_t kStepWindow = 64;
+
 // Four consecutive elements as floats: one 16-byte access for float32, one
 // 8-byte access for the 16-bit formats.
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -128,8 +130,17 @@ __global__ __launch_bounds__(256) void step_kernel(int64_t L, int64_t B, int64_t
     // rows are (layer, sequence) pairs; s_in may equal s_out (in place), so
     // neither is declared restrict
     // L*B rows < 2^31 (checked at launch), so the row split stays in 32 bits
-    const uint32_t row32 = blockIdx.x / blocks_per_row;
-    const uint32_t cb = blockIdx.x - row32 * blocks_per_row;
+    // The hardware hands consecutive workgroups to the 8 dies in turn; within
+    // each window of 64 workgroups every die takes 8 adjacent ones instead
+    // (contiguous rows of each tensor per die: measured 1-2% faster at the
+    // L=24 B=1024 C=4096 decode shape).
+    uint32_t wid = blockIdx.x;
+    if (gridDim.x % kStepWindow == 0) {
+        const uint32_t in = wid % kStepWindow;
+        wid += (in % 8u) * (kStepWindow / 8u) + in / 8u - in;
+    }
+    const uint32_t row32 = wid / blocks_per_row;
+    const uint32_t cb = wid - row32 * blocks_per_row;
     const uint32_t l32 = row32 / (uint32_t)B;
     const int64_t row = row32;
     const int64_t l = l32;

@@ -40,9 +40,12 @@ def oracle_states(oracle, L, B, C, seed):
 
 
 # C = 37 and 1030 take the one-channel path; 1032, 2056 and 5128 leave the
-# last 1024-channel chunk of the four-wide path partly filled.
+# last 1024-channel chunk of the four-wide path partly filled; grids of 64
+# workgroups (4x16x40, and 2x16x5128 with two per row) are handed to the dies
+# in windows.
 @pytest.mark.parametrize("shape", [(3, 4, 40), (2, 3, 37), (1, 1, 1), (4, 2, 1030),
-                                   (2, 3, 1032), (1, 2, 5128), (2, 2, 2056)],
+                                   (2, 3, 1032), (1, 2, 5128), (2, 2, 2056), (4, 16, 40),
+                                   (2, 16, 5128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_steps_match_oracle(oracle, shape):
     L, B, C = shape
