@@ -119,8 +119,17 @@ __global__ __launch_bounds__(256) void shift_kernel(int64_t B, int64_t T, int64_
                                                     const typename IO::T *x_prev,
                                                     typename IO::T *__restrict__ out,
                                                     typename IO::T *x_prev_out, int write_last) {
-    const uint32_t cb = blockIdx.x % cblocks;
-    const uint32_t rest = blockIdx.x / cblocks;
+    // The hardware hands consecutive workgroups to the 8 dies in turn; within
+    // each window of 64 workgroups every die takes 8 adjacent ones instead
+    // (measured 1.5% faster at B=8 T=1024 C=2048; the same remap made the
+    // backward below 6% slower, so it keeps the plain order)
+    uint32_t wid = blockIdx.x;
+    if (gridDim.x % 64u == 0) {
+        const uint32_t in = wid % 64u;
+        wid += (in % 8u) * 8u + in / 8u - in;
+    }
+    const uint32_t cb = wid % cblocks;
+    const uint32_t rest = wid / cblocks;
     const uint32_t tile = rest % ntiles;
     const int64_t bb = rest / ntiles;
     const int64_t c = ((int64_t)cb * 256 + threadIdx.x) * VEC;

@@ -196,7 +196,8 @@ def check_shift(oracle, mu, x, xp, out, xpo):
         assert np.array_equal(f64(xpo), rp), "carried token is not a bit-exact copy"
 
 
-SHIFT_SHAPES = [(1, 1, 4), (2, 16, 64), (2, 17, 64), (3, 100, 260), (1, 33, 33), (2, 5, 1027)]
+SHIFT_SHAPES = [(1, 1, 4), (2, 16, 64), (2, 17, 64), (3, 100, 260), (1, 33, 33), (2, 5, 1027),
+                (8, 512, 2048)]  # (the last: a grid the forward hands to the dies in windows)
 
 
 @pytest.mark.parametrize("M", [1, 3, 5, 8])
